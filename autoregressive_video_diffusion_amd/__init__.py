@@ -1,0 +1,178 @@
+"""Chunk-causal Causal-RoPE attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over ``libcrattn.so`` (C ABI declared in
+``include/crattn.h``).  Each function has the name of the C entry point it
+wraps and only marshals arguments: torch tensors become device pointers and
+sizes, the current torch stream becomes the HIP stream.  All computation runs
+in the library's HIP kernels; there is no fallback.  If the library has not
+been built, importing the binding's functions raises immediately.
+
+Entry points (see include/crattn.h for the full contracts):
+
+* ``rope_table_bytes`` / ``rope_precompute`` -- cos/sin tables of the 3D
+  rotary code, built once on the device.
+* ``rope_apply_append`` -- rotate Q and K from a global time index, write Q',
+  append K' and V to the KV cache, in one pass.
+* ``chunk_causal_attn_workspace_bytes`` / ``chunk_causal_attn`` -- flash
+  attention of a chunk's queries against the cache, bidirectional inside a
+  chunk and causal across chunks.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
+    "rope_apply_append", "chunk_causal_attn_workspace_bytes", "chunk_causal_attn",
+    "crattn_last_error", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libcrattn.so")
+
+CRATTN_OK, CRATTN_EINVAL, CRATTN_ENOTSUP, CRATTN_EHIP = 0, 1, 2, 3
+CRATTN_F32, CRATTN_BF16 = 0, 1
+
+# Every symbol include/crattn.h declares.
+EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append",
+           "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "crattn_last_error")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+
+
+class CrattnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+def load():
+    """Load libcrattn.so (built by ``python -m autoregressive_video_diffusion_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with "
+                          "`python -m autoregressive_video_diffusion_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    lib.rope_table_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    lib.rope_table_bytes.restype = ctypes.c_size_t
+    lib.rope_precompute.argtypes = [_vp, _i32, _i32, _i32, _i32, ctypes.c_double, _vp]
+    lib.rope_precompute.restype = _i32
+    lib.rope_apply_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32,
+                                      _i32, _i32, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32,
+                                      _vp]
+    lib.rope_apply_append.restype = _i32
+    lib.chunk_causal_attn_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i64, _i64, _i32]
+    lib.chunk_causal_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.chunk_causal_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
+    lib.chunk_causal_attn.restype = _i32
+    lib.crattn_last_error.argtypes = []
+    lib.crattn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def crattn_last_error() -> str:
+    return load().crattn_last_error().decode()
+
+
+def _raise(status: int):
+    if status != CRATTN_OK:
+        raise CrattnError(status, crattn_last_error())
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CRATTN_BF16
+    if t.dtype == torch.float32:
+        return CRATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def rope_table_bytes(head_dim: int, max_t: int, max_h: int, max_w: int) -> int:
+    return int(load().rope_table_bytes(head_dim, max_t, max_h, max_w))
+
+
+def rope_precompute(table: torch.Tensor, head_dim: int, max_t: int, max_h: int, max_w: int,
+                    theta: float = 10000.0, stream=None) -> torch.Tensor:
+    """Fill ``table`` (float32 device tensor of rope_table_bytes/4 elements)."""
+    need = rope_table_bytes(head_dim, max_t, max_h, max_w)
+    if table.dtype != torch.float32 or table.numel() * 4 < need:
+        raise ValueError(f"table must be float32 with at least {need} bytes")
+    _raise(load().rope_precompute(_ptr(table), head_dim, max_t, max_h, max_w, float(theta),
+                                  _stream(stream)))
+    return table
+
+
+def rope_apply_append(q: torch.Tensor | None, q_out: torch.Tensor | None, k: torch.Tensor,
+                      v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      cache_pos: int, table: torch.Tensor, max_t: int, max_h: int, max_w: int,
+                      t0: int, tok_off: int, grid_h: int, grid_w: int, stream=None) -> None:
+    """q, q_out, k, v: [B, n, H, D]; caches [B, H, cap, D]; same dtype (bf16 or fp32)."""
+    B, n, H, D = k.shape
+    cap = k_cache.shape[2]
+    for t in (q, q_out, v):
+        if t is not None and (tuple(t.shape) != (B, n, H, D) or t.dtype != k.dtype):
+            raise ValueError("q, q_out, k, v must share shape [B, n, H, D] and dtype")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != k.dtype:
+            raise ValueError("caches must be [B, H, cap, D] of k's dtype")
+    if table.dtype != torch.float32:
+        raise ValueError("table must be float32")
+    _raise(load().rope_apply_append(_ptr(q), _ptr(q_out), _ptr(k), _ptr(v), _ptr(k_cache),
+                                    _ptr(v_cache), cap, cache_pos, _ptr(table), max_t, max_h,
+                                    max_w, B, H, D, n, t0, tok_off, grid_h, grid_w,
+                                    _dtype_code(k), _stream(stream)))
+
+
+def chunk_causal_attn_workspace_bytes(B: int, H: int, Lq: int, kv_len: int, q_pos0: int,
+                                      chunk_tokens: int, D: int) -> int:
+    return int(load().chunk_causal_attn_workspace_bytes(B, H, Lq, kv_len, q_pos0, chunk_tokens,
+                                                         D))
+
+
+def chunk_causal_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len: int,
+                      q_pos0: int, chunk_tokens: int, out: torch.Tensor,
+                      lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      scale: float = 0.0, stream=None) -> torch.Tensor:
+    """q, out: [B, Lq, H, D] bf16; caches [B, H, cap, D] bf16; lse [B, H, Lq] fp32."""
+    B, Lq, H, D = q.shape
+    cap = k_cache.shape[2]
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if tuple(out.shape) != (B, Lq, H, D):
+        raise ValueError("out must have q's shape")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != torch.bfloat16:
+            raise ValueError("caches must be bf16 [B, H, cap, D]")
+    if lse is not None and (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, H, Lq]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _raise(load().chunk_causal_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, kv_len, q_pos0,
+                                    chunk_tokens, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                    B, H, D, Lq, float(scale), _stream(stream)))
+    return out

@@ -1,0 +1,230 @@
+// C-ABI front end of libcrattn.so: argument validation, launch planning and
+// error reporting.  The entry points and their contracts are declared and
+// documented in include/crattn.h.  Every check runs on the host before any
+// HIP call, so an invalid call launches nothing and writes nothing.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/crattn.h"
+#include "crattn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return CRATTN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(CRATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+constexpr int kMaxExtent = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+size_t rope_table_bytes(int head_dim, int max_t, int max_h, int max_w) {
+  if (head_dim < 2 || head_dim > CRATTN_MAX_HEAD_DIM || (head_dim % 2) != 0) return 0;
+  if (max_t < 0 || max_h < 0 || max_w < 0) return 0;
+  if (max_t > kMaxExtent || max_h > kMaxExtent || max_w > kMaxExtent) return 0;
+  const crattn::RopeSplit sp = crattn::rope_split(head_dim);
+  return 8u * ((size_t)max_t * (sp.dt / 2) + (size_t)max_h * (sp.dh / 2) +
+               (size_t)max_w * (sp.dw / 2));
+}
+
+int rope_precompute(float *table, int head_dim, int max_t, int max_h, int max_w, double theta,
+                    void *stream) {
+  if (table == nullptr) return fail(CRATTN_EINVAL, "rope_precompute: table is NULL");
+  if (!aligned16(table)) return fail(CRATTN_EINVAL, "rope_precompute: table not 16-byte aligned");
+  if (head_dim < 2 || head_dim > CRATTN_MAX_HEAD_DIM || (head_dim % 2) != 0)
+    return fail(CRATTN_EINVAL, "rope_precompute: head_dim %d not even in [2, %d]", head_dim,
+                CRATTN_MAX_HEAD_DIM);
+  if (max_t < 1 || max_h < 1 || max_w < 1 || max_t > kMaxExtent || max_h > kMaxExtent ||
+      max_w > kMaxExtent)
+    return fail(CRATTN_EINVAL, "rope_precompute: extents (%d, %d, %d) outside [1, %d]", max_t,
+                max_h, max_w, kMaxExtent);
+  if (!(theta > 1.0) || !isfinite(theta))
+    return fail(CRATTN_EINVAL, "rope_precompute: theta must be finite and > 1");
+  const crattn::RopeSplit sp = crattn::rope_split(head_dim);
+  crattn::RopeTableArgs a;
+  a.table = reinterpret_cast<float2 *>(table);
+  a.dt = sp.dt;
+  a.dh = sp.dh;
+  a.dw = sp.dw;
+  a.max_t = max_t;
+  a.max_h = max_h;
+  a.max_w = max_w;
+  a.theta = theta;
+  return hip_status(crattn::launch_rope_table(a, static_cast<hipStream_t>(stream)),
+                    "rope_precompute launch");
+}
+
+int rope_apply_append(const void *q, void *q_out, const void *k, const void *v, void *k_cache,
+                      void *v_cache, int64_t cap, int64_t cache_pos, const float *table,
+                      int max_t, int max_h, int max_w, int B, int H, int D, int64_t n, int64_t t0,
+                      int64_t tok_off, int grid_h, int grid_w, int dtype, void *stream) {
+  if (k == nullptr || v == nullptr || k_cache == nullptr || v_cache == nullptr ||
+      table == nullptr)
+    return fail(CRATTN_EINVAL, "rope_apply_append: k, v, k_cache, v_cache and table are required");
+  if ((q == nullptr) != (q_out == nullptr))
+    return fail(CRATTN_EINVAL, "rope_apply_append: q and q_out must both be set or both be NULL");
+  if (!aligned16(q) || !aligned16(q_out) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(table))
+    return fail(CRATTN_EINVAL, "rope_apply_append: pointers must be 16-byte aligned");
+  if (dtype != CRATTN_BF16 && dtype != CRATTN_F32)
+    return fail(CRATTN_EINVAL, "rope_apply_append: unknown dtype %d", dtype);
+  if (D < 8 || D > CRATTN_MAX_HEAD_DIM || (D % 8) != 0)
+    return fail(CRATTN_EINVAL, "rope_apply_append: head_dim %d not a multiple of 8 in [8, %d]", D,
+                CRATTN_MAX_HEAD_DIM);
+  if (B < 1 || H < 1 || n < 1)
+    return fail(CRATTN_EINVAL, "rope_apply_append: B=%d H=%d n=%lld must be >= 1", B, H,
+                (long long)n);
+  if (cap < 1 || cache_pos < 0 || cache_pos > cap || n > cap - cache_pos)
+    return fail(CRATTN_EINVAL, "rope_apply_append: rows [%lld, %lld) outside the cache (cap %lld)",
+                (long long)cache_pos, (long long)(cache_pos + n), (long long)cap);
+  if (t0 < 0 || tok_off < 0 || grid_h < 1 || grid_w < 1)
+    return fail(CRATTN_EINVAL, "rope_apply_append: t0, tok_off >= 0 and grid >= 1 required");
+  if (max_t < 1 || max_h < 1 || max_w < 1 || max_t > kMaxExtent || max_h > kMaxExtent ||
+      max_w > kMaxExtent)
+    return fail(CRATTN_EINVAL, "rope_apply_append: table extents outside [1, %d]", kMaxExtent);
+  if (grid_h > max_h || grid_w > max_w)
+    return fail(CRATTN_EINVAL, "rope_apply_append: grid %dx%d exceeds the table (%dx%d)", grid_h,
+                grid_w, max_h, max_w);
+  const int64_t per_frame = (int64_t)grid_h * grid_w;
+  if (tok_off > kMaxElems || n > kMaxElems)
+    return fail(CRATTN_EINVAL, "rope_apply_append: token range too large");
+  const int64_t last_t = t0 + (tok_off + n - 1) / per_frame;
+  if (last_t >= max_t)
+    return fail(CRATTN_EINVAL,
+                "rope_apply_append: time index %lld outside the table (max_t %d)",
+                (long long)last_t, max_t);
+  if (tok_off + n > (int64_t(1) << 31))
+    return fail(CRATTN_EINVAL, "rope_apply_append: token index exceeds 2^31");
+  const int esize = dtype == CRATTN_BF16 ? 2 : 4;
+  const int64_t vec_per_row = (int64_t)D * esize / 16;
+  const double threads = (double)B * (double)n * (double)H * (double)vec_per_row;
+  if (threads >= 2147483648.0)
+    return fail(CRATTN_EINVAL, "rope_apply_append: B*n*H*D too large for one launch");
+  if ((double)B * H * (double)cap * D > (double)kMaxElems)
+    return fail(CRATTN_EINVAL, "rope_apply_append: cache element count exceeds 2^40");
+  crattn::RopeAppendArgs a;
+  a.q = q;
+  a.q_out = q_out;
+  a.k = k;
+  a.v = v;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cap = cap;
+  a.cache_pos = cache_pos;
+  a.table = reinterpret_cast<const float2 *>(table);
+  a.max_t = max_t;
+  a.max_h = max_h;
+  a.max_w = max_w;
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.n = n;
+  a.t0 = t0;
+  a.tok_off = tok_off;
+  a.grid_h = grid_h;
+  a.grid_w = grid_w;
+  a.dtype = dtype;
+  return hip_status(crattn::launch_rope_append(a, static_cast<hipStream_t>(stream)),
+                    "rope_apply_append launch");
+}
+
+static int attn_shape_check(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
+                            int64_t chunk_tokens, int D, int64_t cap, const char *who) {
+  if (B < 1 || H < 1 || Lq < 1)
+    return fail(CRATTN_EINVAL, "%s: B=%d H=%d Lq=%lld must be >= 1", who, B, H, (long long)Lq);
+  if (chunk_tokens < 1 || q_pos0 < 0)
+    return fail(CRATTN_EINVAL, "%s: chunk_tokens >= 1 and q_pos0 >= 0 required", who);
+  if (kv_len < 1 || (cap >= 0 && kv_len > cap))
+    return fail(CRATTN_EINVAL, "%s: kv_len %lld outside [1, cap=%lld]", who, (long long)kv_len,
+                (long long)cap);
+  if (Lq > kMaxElems || q_pos0 > kMaxElems || kv_len > kMaxElems || chunk_tokens > kMaxElems)
+    return fail(CRATTN_EINVAL, "%s: sizes exceed 2^40", who);
+  const int64_t last_chunk = (q_pos0 + Lq - 1) / chunk_tokens;
+  if (kv_len < (last_chunk + 1) * chunk_tokens)
+    return fail(CRATTN_EINVAL,
+                "%s: kv_len %lld leaves the chunk of the last query incomplete (needs %lld)", who,
+                (long long)kv_len, (long long)((last_chunk + 1) * chunk_tokens));
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "%s: head_dim %d not supported (64 or 128)", who, D);
+  if ((double)B * H * (double)Lq * (D / 4) >= 4294967296.0)
+    return fail(CRATTN_EINVAL, "%s: B*H*Lq*D too large for one launch", who);
+  return CRATTN_OK;
+}
+
+size_t chunk_causal_attn_workspace_bytes(int B, int H, int64_t Lq, int64_t kv_len,
+                                         int64_t q_pos0, int64_t chunk_tokens, int D) {
+  if (attn_shape_check(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, -1, "workspace") != CRATTN_OK)
+    return 0;
+  return crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, true).ws_bytes;
+}
+
+int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
+                      int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens, void *out, float *lse,
+                      void *workspace, size_t ws_bytes, int B, int H, int D, int64_t Lq,
+                      float scale, void *stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr)
+    return fail(CRATTN_EINVAL, "chunk_causal_attn: q, k_cache, v_cache and out are required");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(workspace))
+    return fail(CRATTN_EINVAL, "chunk_causal_attn: pointers must be 16-byte aligned");
+  if (cap < 1) return fail(CRATTN_EINVAL, "chunk_causal_attn: cap must be >= 1");
+  const int st = attn_shape_check(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, cap,
+                                  "chunk_causal_attn");
+  if (st != CRATTN_OK) return st;
+  if (!(scale >= 0.f) || !isfinite(scale))
+    return fail(CRATTN_EINVAL, "chunk_causal_attn: scale must be finite and >= 0");
+  if ((double)B * H * (double)cap * D > (double)kMaxElems)
+    return fail(CRATTN_EINVAL, "chunk_causal_attn: cache element count exceeds 2^40");
+  const bool split_ok = workspace != nullptr;
+  const crattn::AttnPlan plan =
+      crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, split_ok);
+  if (split_ok && ws_bytes < plan.ws_bytes)
+    return fail(CRATTN_EINVAL, "chunk_causal_attn: workspace of %zu bytes, %zu needed", ws_bytes,
+                plan.ws_bytes);
+  crattn::AttnArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.cap = cap;
+  a.kv_len = kv_len;
+  a.q_pos0 = q_pos0;
+  a.chunk_tokens = chunk_tokens;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.ws_bytes = ws_bytes;
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.Lq = Lq;
+  a.scale = scale;
+  return hip_status(crattn::launch_attn(a, plan, static_cast<hipStream_t>(stream)),
+                    "chunk_causal_attn launch");
+}
+
+const char *crattn_last_error(void) { return g_err; }
+
+}  // extern "C"

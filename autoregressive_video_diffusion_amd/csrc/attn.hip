@@ -1,0 +1,502 @@
+// Chunk-causal flash attention for AMD CDNA4 (gfx950), bf16 MFMA.
+//
+// Sources: "Wave Forcing" abstract (chunk-based causal attention over the
+// earlier chunks); "Accelerating Video Generation Inference with
+// Sequential-Parallel 3D Positional Encoding Using a Global Time Index" §1
+// (attention against a KV cache).  Key j is visible to query row i iff
+// j < kv_len and floor(j/L) <= floor((q_pos0+i)/L): bidirectional inside a
+// chunk, causal across chunks.  The design below is this file's own.
+//
+// Work decomposition
+//   * A workgroup (4 wavefronts) owns BM query rows of one (batch, head) and
+//     walks the visible keys in tiles of BN = 64.  Query tiles never straddle
+//     a chunk boundary, so every row of a workgroup has the same visible key
+//     range [0, limit): masking is needed on the last key tile only, and keys
+//     beyond `limit` are never loaded (NaN/Inf in future chunks cannot leak
+//     through 0 * NaN).
+//   * Each wavefront owns QB blocks of 32 query rows.
+//   * Optionally the key range of a tile is split over several workgroups
+//     (split-KV); partial (O, lse) go to a workspace and a combine kernel
+//     merges them with the log-sum-exp identity.
+//
+// Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 64-wide wavefronts)
+//   * S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = 16 dims x 32 queries
+//     held in registers for the whole key loop.  In the accumulator each lane
+//     owns one query column and 16 keys, so the softmax row reductions over
+//     keys are in-lane plus one exchange between the two half-wavefronts.
+//   * K rows are fed to the A operand in a permuted order chosen so that the
+//     accumulator registers of S^T are, unchanged, the B operand (P^T) of the
+//     next product: lane half hf, register r holds key 16*(r/8) + 8*hf + r%8.
+//   * O^T = V^T P^T: A = 32 dims x 16 keys from LDS, where V is stored in
+//     "key octets" (for each group of 8 keys and each dim, the 8 values are
+//     contiguous), written by an in-register 4x8 transpose during staging.
+//   * Softmax in fp32 with base-2 exponent, log2(e) folded into the scale;
+//     P rounded to bf16 for the second product; O kept in fp32.
+#include "crattn_internal.h"
+#include "../../include/crattn.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace crattn {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+struct AttnKArgs {
+  const uint16_t *q;
+  const uint16_t *k;
+  const uint16_t *v;
+  uint16_t *out;
+  float *lse;
+  float *ws_o;    // [splits][B][H][Lq][D]   (split > 1 only)
+  float *ws_lse;  // [splits][B][H][Lq]      base-2 log-sum-exp
+  int B, H;
+  int64_t Lq, cap, kv_len, q_pos0, L;
+  float scale_log2;
+  int64_t seg0_rows, tiles0, tiles_full, n_full, last_rows, n_tiles;
+  int splits;
+};
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+
+// Row of the 32-key block that lane (l32) feeds into the A operand, chosen so
+// that accumulator register r of lane half hf holds key 16*(r/8) + 8*hf + r%8.
+// Accumulator layout of the 32x32 product: lane l, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32.
+__device__ inline int k_row_perm(int m) {
+  const int r = (m >> 3) * 4 + (m & 3);
+  const int hf = (m >> 2) & 1;
+  return (r >> 3) * 16 + hf * 8 + (r & 7);
+}
+
+// Key (within a 32-key block) held by accumulator register r of lane half hf.
+__device__ inline int acc_key(int r, int hf) { return (r >> 3) * 16 + hf * 8 + (r & 7); }
+
+template <int CPR>
+__device__ inline int k_cell(int row, int chunk) {
+  return row * CPR + (chunk ^ (row & (CPR - 1)));
+}
+
+// V octet cell (g, d) -> index of its 16-byte cell in LDS.  The XOR spreads
+// the staging writes of one row group over banks; reads of 32 consecutive d
+// stay within one 512-byte run.
+template <int D>
+__device__ inline int v_cell(int g, int d) {
+  return g * D + (d ^ ((d >> 3) & 7));
+}
+
+template <int D, int QB>
+__global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnKArgs a) {
+  constexpr int DK = D / 16;   // k-steps of the QK product
+  constexpr int DB = D / 32;   // 32-dim blocks of O
+  constexpr int KB = kBN / 32; // 32-key blocks per tile
+  constexpr int CPR = D / 8;   // 16-byte chunks per K row
+  constexpr int BM = kWaves * QB * 32;
+
+  __shared__ uint4 k_lds[kBN * CPR];
+  __shared__ uint4 v_lds[kBN * D / 8];  // key-octet cells, 16 bytes each
+  uint2 *const v_half = reinterpret_cast<uint2 *>(v_lds);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hf = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- which (b, h, query tile, key split) this workgroup computes ----
+  int64_t bid = blockIdx.x;
+  const int split = (int)(bid % a.splits);
+  bid /= a.splits;
+  const int64_t tile = bid % a.n_tiles;
+  bid /= a.n_tiles;
+  const int h = (int)(bid % a.H);
+  const int b = (int)(bid / a.H);
+
+  int64_t seg, t_in, seg_row0, seg_rows;
+  if (tile < a.tiles0) {
+    seg = 0;
+    t_in = tile;
+    seg_row0 = 0;
+    seg_rows = a.seg0_rows;
+  } else {
+    const int64_t u = tile - a.tiles0;
+    if (u < a.n_full * a.tiles_full) {
+      const int64_t s = u / a.tiles_full;
+      t_in = u - s * a.tiles_full;
+      seg = 1 + s;
+      seg_row0 = a.seg0_rows + s * a.L;
+      seg_rows = a.L;
+    } else {
+      t_in = u - a.n_full * a.tiles_full;
+      seg = 1 + a.n_full;
+      seg_row0 = a.seg0_rows + a.n_full * a.L;
+      seg_rows = a.last_rows;
+    }
+  }
+  const int64_t row0 = seg_row0 + t_in * BM;
+  const int64_t nrows = min((int64_t)BM, seg_rows - t_in * BM);
+  const int64_t q_chunk = a.q_pos0 / a.L + seg;
+  const int64_t limit = min(a.kv_len, (q_chunk + 1) * a.L);
+  const int64_t nkt = (limit + kBN - 1) / kBN;
+  const int64_t kt_begin = split * nkt / a.splits;
+  const int64_t kt_end = (split + 1) * nkt / a.splits;
+
+  const int64_t head_off = ((int64_t)b * a.H + h) * a.cap * D;
+  const uint16_t *__restrict__ kh = a.k + head_off;
+  const uint16_t *__restrict__ vh = a.v + head_off;
+
+  // ---- this wavefront's queries, as B operands (16 dims x 32 queries) ----
+  const int64_t wrow0 = row0 + (int64_t)wave * QB * 32;
+  const bool active = (int64_t)wave * QB * 32 < nrows;
+  bf16x8_t qf[QB][DK];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t row = wrow0 + qb * 32 + l32;
+    const bool ok = row < row0 + nrows;
+    const uint16_t *qp = a.q + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (ok) x = *reinterpret_cast<const uint4 *>(qp + ks * 16);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+  }
+
+  f32x16_t o[DB][QB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][qb][r] = 0.f;
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
+
+  const int kperm = k_row_perm(l32);
+
+  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
+    const int64_t key0 = kt * kBN;
+    // ---- stage K: rows as 16-byte chunks, XOR-swizzled per row ----
+#pragma unroll
+    for (int id = tid; id < kBN * CPR; id += kThreads) {
+      const int r = id / CPR, c = id % CPR;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (key0 + r < limit) x = *reinterpret_cast<const uint4 *>(kh + (key0 + r) * D + c * 8);
+      k_lds[k_cell<CPR>(r, c)] = x;
+    }
+    // ---- stage V: 4 keys x 8 dims per thread, transposed to key octets ----
+#pragma unroll
+    for (int id = tid; id < (kBN / 4) * CPR; id += kThreads) {
+      const int c = id % CPR, kq = id / CPR;
+      uint4 rw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rw[r] = make_uint4(0, 0, 0, 0);
+        const int64_t key = key0 + kq * 4 + r;
+        if (key < limit) rw[r] = *reinterpret_cast<const uint4 *>(vh + key * D + c * 8);
+      }
+      const uint32_t w0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
+      const uint32_t w1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
+      const uint32_t w2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
+      const uint32_t w3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
+      const int g = kq >> 1, half = kq & 1;
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+        uint2 cell;
+        cell.x = __builtin_amdgcn_perm(w1[dd >> 1], w0[dd >> 1], sel);
+        cell.y = __builtin_amdgcn_perm(w3[dd >> 1], w2[dd >> 1], sel);
+        v_half[v_cell<D>(g, c * 8 + dd) * 2 + half] = cell;
+      }
+    }
+    __syncthreads();
+
+    if (active) {
+      // ---- S^T = K Q^T for this wavefront's queries ----
+      f32x16_t s[KB][QB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int row = kb * 32 + kperm;
+          const bf16x8_t kf =
+              __builtin_bit_cast(bf16x8_t, k_lds[k_cell<CPR>(row, 2 * ks + hf)]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+        }
+      }
+      // ---- mask keys past the visible limit (last tile only) ----
+      if (key0 + kBN > limit) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool dead = key0 + kb * 32 + acc_key(r, hf) >= limit;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              if (dead) s[kb][qb][r] = -INFINITY;
+          }
+      }
+      // ---- online softmax, per query column ----
+      bf16x8_t pf[QB][KB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 =
+                  __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.scale_log2, -m_new));
+              const float p1 =
+                  __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.scale_log2, -m_new));
+              rs += p0 + p1;
+              pk[e] = pack_bf16(p0, p1);
+            }
+            pf[qb][kb][h2] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+          }
+        }
+        l_run[qb] = l_run[qb] * alpha + rs;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
+      }
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int g = kb * 4 + h2 * 2 + hf;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, v_lds[v_cell<D>(g, db * 32 + l32)]);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][h2], o[db][qb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // ---- epilogue: normalise and store ----
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const int64_t row = wrow0 + qb * 32 + l32;
+    if (row >= row0 + nrows) continue;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const float lse2 = lt > 0.f ? m_run[qb] + __log2f(lt) : -INFINITY;
+    if (a.splits == 1) {
+      uint16_t *op = a.out + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x16_t &acc = o[db][qb];
+          uint2 w;
+          w.x = pack_bf16(acc[i4 * 4 + 0] * inv, acc[i4 * 4 + 1] * inv);
+          w.y = pack_bf16(acc[i4 * 4 + 2] * inv, acc[i4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2 *>(op + db * 32 + i4 * 8) = w;
+        }
+      if (hf == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Lq + row] = lse2 * kLn2;
+    } else {
+      const int64_t prow = (((int64_t)split * a.B + b) * a.H + h) * a.Lq + row;
+      float *op = a.ws_o + prow * D + hf * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x16_t &acc = o[db][qb];
+          *reinterpret_cast<float4 *>(op + db * 32 + i4 * 8) =
+              make_float4(acc[i4 * 4 + 0] * inv, acc[i4 * 4 + 1] * inv, acc[i4 * 4 + 2] * inv,
+                          acc[i4 * 4 + 3] * inv);
+        }
+      if (hf == 0) a.ws_lse[prow] = lse2;
+    }
+  }
+}
+
+struct CombineArgs {
+  const float *ws_o;
+  const float *ws_lse;
+  uint16_t *out;
+  float *lse;
+  int B, H, D, splits;
+  int64_t Lq;
+  uint32_t total;  // B * H * Lq * (D / 4)
+};
+
+// Merge split-KV partials: lse = log2 sum_s 2^lse_s; O = sum_s 2^(lse_s - lse) O_s.
+__global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= a.total) return;
+  const uint32_t nc = (uint32_t)a.D / 4;
+  const uint32_t c4 = t % nc;
+  const uint64_t r = t / nc;  // (b * H + h) * Lq + row
+  const int64_t row = (int64_t)(r % (uint64_t)a.Lq);
+  const uint64_t bh = r / (uint64_t)a.Lq;
+  const int h = (int)(bh % (uint64_t)a.H);
+  const int b = (int)(bh / (uint64_t)a.H);
+  const uint64_t plane = (uint64_t)a.B * a.H * a.Lq;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.ws_lse[s * plane + r]);
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < a.splits; ++s) {
+    const float ls = a.ws_lse[s * plane + r];
+    const float w = ls == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ls - mx);
+    wsum += w;
+    const float4 x = *reinterpret_cast<const float4 *>(a.ws_o + (s * plane + r) * a.D + c4 * 4);
+    acc.x += w * x.x;
+    acc.y += w * x.y;
+    acc.z += w * x.z;
+    acc.w += w * x.w;
+  }
+  const float inv = 1.0f / wsum;
+  uint2 wv;
+  wv.x = pack_bf16(acc.x * inv, acc.y * inv);
+  wv.y = pack_bf16(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2 *>(a.out + (((int64_t)b * a.Lq + row) * a.H + h) * a.D + c4 * 4) = wv;
+  if (c4 == 0 && a.lse != nullptr) a.lse[r] = (mx + __log2f(wsum)) * kLn2;
+}
+
+template <int D, int QB>
+hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, QB>), dim3((unsigned)grid), dim3(kThreads), 0, s, k);
+  return hipGetLastError();
+}
+
+int choose_qb(int D) { return D == 128 ? 2 : 2; }
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
+                   int64_t chunk_tokens, int D, bool allow_split) {
+  AttnPlan p{};
+  p.d = D;
+  p.bm = kWaves * choose_qb(D) * 32;
+  p.bn = kBN;
+  const int64_t L = chunk_tokens;
+  const int64_t c0 = q_pos0 / L;
+  p.seg0_rows = std::min(Lq, (c0 + 1) * L - q_pos0);
+  p.tiles0 = (p.seg0_rows + p.bm - 1) / p.bm;
+  const int64_t rest = Lq - p.seg0_rows;
+  p.n_full = rest / L;
+  p.last_rows = rest - p.n_full * L;
+  p.tiles_full = (L + p.bm - 1) / p.bm;
+  p.n_tiles = p.tiles0 + p.n_full * p.tiles_full + (p.last_rows + p.bm - 1) / p.bm;
+  const int64_t units = (int64_t)B * H * p.n_tiles;
+  // Fewest key tiles any query tile has (the first segment sees the least).
+  const int64_t min_keys = std::min(kv_len, (c0 + 1) * L);
+  const int64_t min_ktiles = (min_keys + kBN - 1) / kBN;
+  constexpr int64_t kSlots = 256;  // one workgroup per compute unit of an MI355X
+  p.splits = 1;
+  // Split the key range only when the query tiles alone leave most of the
+  // chip idle: partials cost (D + 1) * 4 bytes per row and split of traffic.
+  if (allow_split && units * 2 <= kSlots) {
+    double best = (double)units / (double)(((units + kSlots - 1) / kSlots) * kSlots);
+    for (int s = 2; s <= 16; ++s) {
+      if (min_ktiles / s < 8) break;
+      const int64_t u = units * s;
+      const double eff = (double)u / (double)(((u + kSlots - 1) / kSlots) * kSlots);
+      if (eff > best + 0.05) {
+        best = eff;
+        p.splits = s;
+      }
+    }
+  }
+  p.grid = units * p.splits;
+  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0;
+  return p;
+}
+
+hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
+  AttnKArgs k;
+  k.q = static_cast<const uint16_t *>(a.q);
+  k.k = static_cast<const uint16_t *>(a.k);
+  k.v = static_cast<const uint16_t *>(a.v);
+  k.out = static_cast<uint16_t *>(a.out);
+  k.lse = a.lse;
+  k.B = a.B;
+  k.H = a.H;
+  k.Lq = a.Lq;
+  k.cap = a.cap;
+  k.kv_len = a.kv_len;
+  k.q_pos0 = a.q_pos0;
+  k.L = a.chunk_tokens;
+  const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf((float)a.D);
+  k.scale_log2 = scale * 1.44269504088896340736f;
+  k.seg0_rows = p.seg0_rows;
+  k.tiles0 = p.tiles0;
+  k.tiles_full = p.tiles_full;
+  k.n_full = p.n_full;
+  k.last_rows = p.last_rows;
+  k.n_tiles = p.n_tiles;
+  k.splits = p.splits;
+  const size_t o_bytes = (size_t)p.splits * a.B * a.H * a.Lq * (size_t)a.D * 4u;
+  k.ws_o = p.splits > 1 ? static_cast<float *>(a.workspace) : nullptr;
+  k.ws_lse = p.splits > 1 ? reinterpret_cast<float *>(static_cast<char *>(a.workspace) + o_bytes)
+                          : nullptr;
+  hipError_t e;
+  const int qb = choose_qb(a.D);
+  if (a.D == 128)
+    e = qb == 2 ? launch_fwd<128, 2>(k, p.grid, s) : launch_fwd<128, 1>(k, p.grid, s);
+  else
+    e = qb == 2 ? launch_fwd<64, 2>(k, p.grid, s) : launch_fwd<64, 1>(k, p.grid, s);
+  if (e != hipSuccess || p.splits == 1) return e;
+  CombineArgs c;
+  c.ws_o = k.ws_o;
+  c.ws_lse = k.ws_lse;
+  c.out = k.out;
+  c.lse = a.lse;
+  c.B = a.B;
+  c.H = a.H;
+  c.D = a.D;
+  c.splits = p.splits;
+  c.Lq = a.Lq;
+  c.total = (uint32_t)((uint64_t)a.B * a.H * a.Lq * (a.D / 4));
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((c.total + 255u) / 256u), dim3(256), 0, s, c);
+  return hipGetLastError();
+}
+
+}  // namespace crattn

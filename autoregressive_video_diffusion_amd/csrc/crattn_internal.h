@@ -1,0 +1,83 @@
+// Internal declarations shared by the C-ABI front end (api.cpp) and the HIP
+// kernel files.  Not installed; the public interface is include/crattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crattn {
+
+// head_dim split of the 3D rotary code: h and w get 2*floor(D/6) dims each,
+// t the rest, in the order t, h, w.
+struct RopeSplit {
+  int dt, dh, dw;
+};
+inline RopeSplit rope_split(int D) {
+  const int hw = 2 * (D / 6);
+  return RopeSplit{D - 2 * hw, hw, hw};
+}
+
+struct RopeTableArgs {
+  float2 *table;
+  int dt, dh, dw;
+  int max_t, max_h, max_w;
+  double theta;
+};
+
+struct RopeAppendArgs {
+  const void *q;
+  void *q_out;
+  const void *k;
+  const void *v;
+  void *k_cache;
+  void *v_cache;
+  int64_t cap, cache_pos;
+  const float2 *table;
+  int max_t, max_h, max_w;
+  int B, H, D;
+  int64_t n;
+  int64_t t0, tok_off;
+  int grid_h, grid_w;
+  int dtype;  // CRATTN_F32 / CRATTN_BF16
+};
+
+struct AttnArgs {
+  const void *q;
+  const void *k;
+  const void *v;
+  int64_t cap, kv_len, q_pos0, chunk_tokens;
+  void *out;
+  float *lse;
+  void *workspace;
+  size_t ws_bytes;
+  int B, H, D;
+  int64_t Lq;
+  float scale;
+};
+
+// Launch plan of one attention call: how query rows are tiled and how the
+// key range of each tile is split.  A pure function of the shape.
+struct AttnPlan {
+  int d;             // head_dim (64 or 128)
+  int bm;            // query rows per workgroup
+  int bn;            // keys per LDS tile
+  int64_t n_tiles;   // query tiles over all chunk segments (per b, h)
+  int splits;        // key-range splits per query tile (1 = no workspace)
+  int64_t grid;      // workgroups launched by the main kernel
+  size_t ws_bytes;   // workspace the split needs (0 when splits == 1)
+  // segments: query rows grouped by chunk; tiles never straddle a chunk
+  int64_t seg0_rows;  // rows in the first (possibly partial) chunk segment
+  int64_t tiles0;     // tiles of the first segment
+  int64_t tiles_full; // tiles of every full middle segment
+  int64_t n_full;     // number of full middle segments
+  int64_t last_rows;  // rows of the trailing partial segment (0 if none)
+};
+
+AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
+                   int64_t chunk_tokens, int D, bool allow_split);
+
+hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t s);
+hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t s);
+hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
+
+}  // namespace crattn

@@ -1,0 +1,223 @@
+// 3D Causal-RoPE: cos/sin table precompute and the fused rotate + KV-append
+// pass, for AMD CDNA4 (gfx950).
+//
+// Sources: "Accelerating Video Generation Inference with Sequential-Parallel
+// 3D Positional Encoding Using a Global Time Index", technical summary
+// §2.B (global time index t_global = t + s, local rotation from the start
+// offset and local index, no gather) and §2.C (cos/sin precomputed into
+// contiguous device tensors; RoPE fused into one kernel).  The rotary code
+// itself is the standard per-pair 2-D rotation, applied per axis group
+// (t, h, w) of head_dim.
+//
+// The append pass is bound by HBM bandwidth: per token and head it reads
+// Q, K, V rows and writes Q', K', V rows once, 16 bytes per lane per tensor,
+// with every wavefront covering whole 256-byte rows.  The table (tens of KB)
+// stays in L1/L2.
+#include "crattn_internal.h"
+#include "../../include/crattn.h"
+
+namespace crattn {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// One thread per table entry (axis, position, pair).  The angle and its
+// sine/cosine are evaluated in double precision, then rounded to float: at
+// positions of ~80 an fp32 angle alone would carry ~8e-6 absolute error.
+__global__ void __launch_bounds__(256) rope_table_kernel(RopeTableArgs a, int total) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int nt = a.max_t * (a.dt / 2);
+  const int nh = a.max_h * (a.dh / 2);
+  int Da, local;
+  if (e < nt) {
+    Da = a.dt;
+    local = e;
+  } else if (e < nt + nh) {
+    Da = a.dh;
+    local = e - nt;
+  } else {
+    Da = a.dw;
+    local = e - nt - nh;
+  }
+  const int half = Da / 2;
+  const int p = local / half;
+  const int j = local - p * half;
+  const double freq = pow(a.theta, -2.0 * (double)j / (double)Da);
+  const double phi = (double)p * freq;
+  double s, c;
+  sincos(phi, &s, &c);
+  a.table[e] = make_float2((float)c, (float)s);
+}
+
+struct Pos {
+  uint32_t t, h, w;
+};
+
+// Token g of the chunk (raster order) -> (t0 + frame, row, column).
+__device__ inline Pos decode_pos(uint32_t g, uint32_t per_frame, uint32_t gw, uint32_t t0) {
+  const uint32_t f = g / per_frame;
+  const uint32_t in_frame = g - f * per_frame;
+  const uint32_t r = in_frame / gw;
+  return Pos{t0 + f, r, in_frame - r * gw};
+}
+
+struct TabGeom {
+  uint32_t ht, hh;      // pairs in the t group and in the h (= w) group
+  uint32_t base_h;      // first entry of axis h  = max_t * ht
+  uint32_t base_w;      // first entry of axis w  = base_h + max_h * hh
+};
+
+// (cos, sin) of feature pair `pair` of head_dim at position p.
+__device__ inline float2 pair_cs(const float2 *__restrict__ tab, const TabGeom &g,
+                                 uint32_t pair, const Pos &p) {
+  uint32_t idx;
+  if (pair < g.ht)
+    idx = p.t * g.ht + pair;
+  else if (pair < g.ht + g.hh)
+    idx = g.base_h + p.h * g.hh + (pair - g.ht);
+  else
+    idx = g.base_w + p.w * g.hh + (pair - g.ht - g.hh);
+  return tab[idx];
+}
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  f32x2_t x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+
+// Rotate the bf16 pair packed in one dword (element 2j in the low half).
+__device__ inline uint32_t rot_bf16(uint32_t u, float2 cs) {
+  const float x = bf_lo(u), y = bf_hi(u);
+  return pack_bf16(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
+}
+
+struct AppendGeom {
+  uint32_t total;      // B * n * H * V threads
+  uint32_t V;          // 16-byte vectors per row
+  uint32_t n, H;
+  uint32_t per_frame, gw, t0, tok_off;
+};
+
+// One thread per 16-byte vector of one (b, token, head) row.  Thread order is
+// the input order (vector, head, token, batch), so Q/K/V reads are fully
+// contiguous and each cache write covers whole rows of one head.
+__global__ void __launch_bounds__(256) rope_append_bf16_kernel(RopeAppendArgs a, AppendGeom g,
+                                                                TabGeom tg) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= g.total) return;
+  const uint32_t c = t % g.V;
+  const uint32_t row = t / g.V;  // (b * n + i) * H + h
+  const uint32_t h = row % g.H;
+  const uint32_t bi = row / g.H;
+  const uint32_t i = bi % g.n;
+  const uint32_t b = bi / g.n;
+  const Pos p = decode_pos(g.tok_off + i, g.per_frame, g.gw, g.t0);
+
+  const size_t in_off = (size_t)row * (size_t)a.D + (size_t)c * 8;
+  const size_t cache_off =
+      (((size_t)b * g.H + h) * (size_t)a.cap + (size_t)a.cache_pos + i) * (size_t)a.D +
+      (size_t)c * 8;
+
+  const uint4 kv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + in_off);
+  const uint4 vv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + in_off);
+  uint4 qv = make_uint4(0, 0, 0, 0);
+  const bool has_q = a.q != nullptr;
+  if (has_q) qv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + in_off);
+
+  const uint32_t pair0 = c * 4;
+  const float2 cs0 = pair_cs(a.table, tg, pair0 + 0, p);
+  const float2 cs1 = pair_cs(a.table, tg, pair0 + 1, p);
+  const float2 cs2 = pair_cs(a.table, tg, pair0 + 2, p);
+  const float2 cs3 = pair_cs(a.table, tg, pair0 + 3, p);
+
+  const uint4 ko = make_uint4(rot_bf16(kv.x, cs0), rot_bf16(kv.y, cs1), rot_bf16(kv.z, cs2),
+                              rot_bf16(kv.w, cs3));
+  *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.k_cache) + cache_off) = ko;
+  *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.v_cache) + cache_off) = vv;
+  if (has_q) {
+    const uint4 qo = make_uint4(rot_bf16(qv.x, cs0), rot_bf16(qv.y, cs1), rot_bf16(qv.z, cs2),
+                                rot_bf16(qv.w, cs3));
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.q_out) + in_off) = qo;
+  }
+}
+
+__device__ inline float2 rot_f32(float x, float y, float2 cs) {
+  return make_float2(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
+}
+
+// fp32 variant: a 16-byte vector is two pairs.
+__global__ void __launch_bounds__(256) rope_append_f32_kernel(RopeAppendArgs a, AppendGeom g,
+                                                               TabGeom tg) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  if (t >= g.total) return;
+  const uint32_t c = t % g.V;
+  const uint32_t row = t / g.V;
+  const uint32_t h = row % g.H;
+  const uint32_t bi = row / g.H;
+  const uint32_t i = bi % g.n;
+  const uint32_t b = bi / g.n;
+  const Pos p = decode_pos(g.tok_off + i, g.per_frame, g.gw, g.t0);
+
+  const size_t in_off = (size_t)row * (size_t)a.D + (size_t)c * 4;
+  const size_t cache_off =
+      (((size_t)b * g.H + h) * (size_t)a.cap + (size_t)a.cache_pos + i) * (size_t)a.D +
+      (size_t)c * 4;
+
+  const float4 kv = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.k) + in_off);
+  const float4 vv = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.v) + in_off);
+  const bool has_q = a.q != nullptr;
+  float4 qv = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (has_q) qv = *reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + in_off);
+
+  const float2 cs0 = pair_cs(a.table, tg, c * 2 + 0, p);
+  const float2 cs1 = pair_cs(a.table, tg, c * 2 + 1, p);
+  const float2 k0 = rot_f32(kv.x, kv.y, cs0), k1 = rot_f32(kv.z, kv.w, cs1);
+  *reinterpret_cast<float4 *>(static_cast<float *>(a.k_cache) + cache_off) =
+      make_float4(k0.x, k0.y, k1.x, k1.y);
+  *reinterpret_cast<float4 *>(static_cast<float *>(a.v_cache) + cache_off) = vv;
+  if (has_q) {
+    const float2 q0 = rot_f32(qv.x, qv.y, cs0), q1 = rot_f32(qv.z, qv.w, cs1);
+    *reinterpret_cast<float4 *>(static_cast<float *>(a.q_out) + in_off) =
+        make_float4(q0.x, q0.y, q1.x, q1.y);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t s) {
+  const int total = a.max_t * (a.dt / 2) + a.max_h * (a.dh / 2) + a.max_w * (a.dw / 2);
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((total + 255) / 256), dim3(256), 0, s, a, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t s) {
+  const RopeSplit sp = rope_split(a.D);
+  TabGeom tg;
+  tg.ht = (uint32_t)(sp.dt / 2);
+  tg.hh = (uint32_t)(sp.dh / 2);
+  tg.base_h = (uint32_t)a.max_t * tg.ht;
+  tg.base_w = tg.base_h + (uint32_t)a.max_h * tg.hh;
+  AppendGeom g;
+  const int esize = a.dtype == CRATTN_BF16 ? 2 : 4;
+  g.V = (uint32_t)(a.D * esize / 16);
+  g.n = (uint32_t)a.n;
+  g.H = (uint32_t)a.H;
+  g.total = (uint32_t)((uint64_t)a.B * (uint64_t)a.n * (uint64_t)a.H * g.V);
+  g.per_frame = (uint32_t)a.grid_h * (uint32_t)a.grid_w;
+  g.gw = (uint32_t)a.grid_w;
+  g.t0 = (uint32_t)a.t0;
+  g.tok_off = (uint32_t)a.tok_off;
+  const dim3 grid((g.total + 255u) / 256u);
+  if (a.dtype == CRATTN_BF16)
+    hipLaunchKernelGGL(rope_append_bf16_kernel, grid, dim3(256), 0, s, a, g, tg);
+  else
+    hipLaunchKernelGGL(rope_append_f32_kernel, grid, dim3(256), 0, s, a, g, tg);
+  return hipGetLastError();
+}
+
+}  // namespace crattn

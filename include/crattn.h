@@ -1,0 +1,197 @@
+/*
+ * crattn.h -- C ABI of the chunk-causal Causal-RoPE attention library
+ * (libcrattn.so, HIP for AMD CDNA4 / gfx950).
+ *
+ * The library implements the attention step of a chunk-causal autoregressive
+ * video diffusion transformer (Self-Forcing style):
+ *
+ *   1. rope_precompute    -- cos/sin tables of the 3D rotary code, computed
+ *                            once on the device.
+ *   2. rope_apply_append  -- rotate the current chunk's Q and K with the 3D
+ *                            rotary code from a global time index, write the
+ *                            rotated Q, and append the rotated K and the V
+ *                            to the KV cache, in one pass.
+ *   3. chunk_causal_attn  -- flash attention of the chunk's queries against
+ *                            the cache: bidirectional inside a chunk, causal
+ *                            across chunks.
+ *
+ * Sources (web pages, by title and section):
+ *   [CRSP] "Accelerating Video Generation Inference with Sequential-Parallel
+ *          3D Positional Encoding Using a Global Time Index", technical
+ *          summary: §1 (KV cache, rolling windows), §2.A (sequence
+ *          parallelism: each rank holds a slice of the tokens), §2.B
+ *          (Causal-RoPE SP: t_global = t + s; each rank rotates its own
+ *          tokens from the start offset and its local index, no gather),
+ *          §2.C (cos/sin precomputed into contiguous device tensors instead of
+ *          dynamic caching; RoPE fused into one kernel).
+ *   [WF]   "Wave Forcing" abstract: chunk-based causal attention over earlier
+ *          chunks; the cache update is a separate forward pass.
+ *   [SVG2] "Sparse VideoGen2" §2.A: attention output does not depend on the
+ *          order of the key/value pairs (so a ring-buffer window is legal).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are caller-owned device memory (any allocator).  The library
+ *     allocates nothing, frees nothing, keeps no state between calls except a
+ *     thread-local error message, and never synchronises: every call is
+ *     enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).
+ *   - Every argument is validated on the host before anything is launched; a
+ *     call that returns non-zero has written nothing.  Faults inside a kernel
+ *     (for example a pointer to too small a buffer) surface as a HIP error at
+ *     the caller's next synchronisation.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Token order inside a chunk is raster order: frame, then row, then
+ *     column.  A chunk of F frames on a gh x gw grid has F*gh*gw tokens.
+ *   - The rotary code splits head_dim D into three groups of adjacent feature
+ *     pairs, in the order t, h, w: D_h = D_w = 2*floor(D/6), D_t = D - 2*D_h
+ *     (44/42/42 at D = 128, 24/20/20 at D = 64).  Pair j of an axis group with
+ *     D_a dims has frequency theta^(-2j/D_a); at position p it is rotated by
+ *     the angle p * theta^(-2j/D_a):  x' = x cos - y sin,  y' = x sin + y cos.
+ */
+#ifndef CRATTN_H
+#define CRATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define CRATTN_OK 0
+#define CRATTN_EINVAL 1   /* invalid argument; nothing was launched            */
+#define CRATTN_ENOTSUP 2  /* valid but unsupported (head_dim, dtype); nothing launched */
+#define CRATTN_EHIP 3     /* the HIP runtime reported an error at launch        */
+
+/* Element types of rope_apply_append's tensors. */
+#define CRATTN_F32 0
+#define CRATTN_BF16 1
+
+/* Largest head_dim any entry point accepts. */
+#define CRATTN_MAX_HEAD_DIM 256
+
+/*
+ * Size in bytes of the cos/sin table for head_dim D and position extents
+ * (max_t, max_h, max_w): 8 * (max_t*D_t/2 + max_h*D_h/2 + max_w*D_w/2).
+ * Returns 0 for invalid arguments (D not a positive even number, negative
+ * extent).  Pure host function.
+ */
+size_t rope_table_bytes(int head_dim, int max_t, int max_h, int max_w);
+
+/*
+ * Build the cos/sin table on the device [CRSP §2.C].
+ *
+ *   table  device, rope_table_bytes(...) bytes, written.  Layout: float pairs
+ *          (cos, sin); axis t entries first ([max_t][D_t/2]), then axis h
+ *          ([max_h][D_h/2]), then axis w ([max_w][D_w/2]).  Entry (a, p, j)
+ *          holds cos and sin of p * theta^(-2j/D_a), evaluated in double
+ *          precision and rounded to float.
+ *   max_t  temporal positions covered: global time indices 0 .. max_t-1.
+ *          Positions past the model's training length are allowed.
+ *   max_h, max_w  rows / columns covered.
+ *   theta  frequency base (10000 for Wan2.1-class models); must be > 1.
+ *
+ * Errors: EINVAL for a NULL table, a misaligned table, D not even in
+ * [2, CRATTN_MAX_HEAD_DIM], an extent < 1 or > 1<<20, theta <= 1; EHIP.
+ */
+int rope_precompute(float *table, int head_dim, int max_t, int max_h, int max_w,
+                    double theta, void *stream);
+
+/*
+ * Rotate the chunk's Q and K and append K' and V to the KV cache, in one pass
+ * [CRSP §2.B, §2.C; WF].
+ *
+ *   q, k, v   device, [B][n][H][D] of `dtype` (token-major, as a QKV projection
+ *             emits them).  q may be NULL (a cache-update call: only K and V).
+ *   q_out     device, [B][n][H][D] of `dtype`: the rotated Q.  May equal q
+ *             (in place); must be NULL exactly when q is NULL.
+ *   k_cache, v_cache  device, [B][H][cap][D] of `dtype` (head-major).  Rows
+ *             cache_pos .. cache_pos+n-1 of every (b, h) are overwritten with
+ *             the rotated K and the unrotated V; no other byte is touched.
+ *   cap       rows per (b, h) in the cache; cache_pos + n <= cap.
+ *   table     the rope_precompute table for (D, max_t, max_h, max_w).
+ *   n         tokens in this call (>= 1).
+ *   t0        global time index of the first frame of the chunk (the
+ *             chunk's start-frame offset s of [CRSP §2.B]).
+ *   tok_off   chunk-local raster index of the call's first token: 0 for a
+ *             whole chunk, r*n for rank r's slice under sequence parallelism.
+ *             Token i sits at g = tok_off + i; its positions are
+ *             p_t = t0 + g / (grid_h*grid_w), p_h = (g mod grid_h*grid_w) / grid_w,
+ *             p_w = g mod grid_w.  They are decoded from these scalars alone,
+ *             so a slice rotates exactly as the same rows of the whole chunk.
+ *   dtype     CRATTN_BF16 (fp32 arithmetic, round-to-nearest-even stores) or
+ *             CRATTN_F32.  V is copied bit for bit.
+ *
+ * Errors: EINVAL for NULL k/v/caches/table, q and q_out not both NULL or both
+ * set, a misaligned pointer, n < 1, B < 1, H < 1, D not a multiple of 8 in
+ * [8, CRATTN_MAX_HEAD_DIM], cap < 1, cache_pos < 0, cache_pos + n > cap,
+ * t0 < 0, tok_off < 0, grid_h < 1, grid_w < 1, a position outside the table
+ * (t0 + last frame >= max_t, grid_h > max_h, grid_w > max_w), an unknown
+ * dtype, or sizes whose element counts overflow 2^40; EHIP.
+ */
+int rope_apply_append(const void *q, void *q_out, const void *k, const void *v,
+                      void *k_cache, void *v_cache, int64_t cap, int64_t cache_pos,
+                      const float *table, int max_t, int max_h, int max_w,
+                      int B, int H, int D, int64_t n, int64_t t0, int64_t tok_off,
+                      int grid_h, int grid_w, int dtype, void *stream);
+
+/*
+ * Workspace bytes chunk_causal_attn needs to split the key range of a call
+ * of this shape across workgroups (0 when it does not split).  Depends on the
+ * shape only.  Pure host function; returns 0 for invalid shapes.
+ */
+size_t chunk_causal_attn_workspace_bytes(int B, int H, int64_t Lq, int64_t kv_len,
+                                         int64_t q_pos0, int64_t chunk_tokens, int D);
+
+/*
+ * Chunk-causal flash attention [WF; CRSP §1].
+ *
+ *   q        device bf16 [B][Lq][H][D]: the rotated queries of this call.
+ *   k_cache, v_cache  device bf16 [B][H][cap][D]: rotated keys and values.
+ *            Only rows 0 .. kv_len-1 are ever read; rows past the visible
+ *            range of a query may hold anything (NaN included) and do not
+ *            affect it.
+ *   kv_len   keys present (1 <= kv_len <= cap).
+ *   q_pos0   global token index of query row 0 (row i sits at q_pos0 + i).
+ *   chunk_tokens  tokens per chunk, L_c.  Key j is visible to row i iff
+ *            j < kv_len and floor(j / L_c) <= floor((q_pos0 + i) / L_c):
+ *            bidirectional inside the chunk, causal across chunks.  The whole
+ *            chunk of the last query row must be present:
+ *            kv_len >= (floor((q_pos0 + Lq - 1) / L_c) + 1) * L_c.
+ *            A ring window of W chunk slots is addressed by passing
+ *            kv_len = cap = W * L_c and q_pos0 = (W-1) * L_c (+ slice offset):
+ *            every slot is then visible, which is correct because attention
+ *            does not depend on key order [SVG2 §2.A].
+ *   out      device bf16 [B][Lq][H][D]: softmax(scale * q k^T) v over the
+ *            visible keys, rounded to nearest even.  Must not overlap q.
+ *   lse      device float [B][H][Lq] or NULL: natural-log log-sum-exp of the
+ *            scaled scores of each row.
+ *   workspace, ws_bytes  device scratch of at least
+ *            chunk_causal_attn_workspace_bytes(...) bytes, or NULL/0: the
+ *            call then runs without splitting the key range (same result up
+ *            to floating-point summation order, possibly slower).
+ *   scale    score scale; 0 means 1/sqrt(D).
+ *
+ * Arithmetic: q.k products in bf16 with fp32 accumulation, softmax in fp32
+ * (base-2 exponent with log2(e) folded into the scale), probabilities
+ * rounded to bf16 for the P.V product, fp32 accumulation, one final division.
+ *
+ * Errors: EINVAL for NULL q/k_cache/v_cache/out, misaligned pointers, B, H or
+ * Lq < 1, kv_len < 1 or > cap, q_pos0 < 0, chunk_tokens < 1, an incomplete
+ * last chunk (see above), a non-finite or negative scale, a workspace that is
+ * non-NULL but too small; ENOTSUP for D other than 64 or 128; EHIP.
+ */
+int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache,
+                      int64_t cap, int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens,
+                      void *out, float *lse, void *workspace, size_t ws_bytes,
+                      int B, int H, int D, int64_t Lq, float scale, void *stream);
+
+/* Message describing the last non-zero return on this thread ("" if none). */
+const char *crattn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CRATTN_H */

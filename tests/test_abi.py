@@ -1,0 +1,112 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its tables and workspaces, and rejects invalid
+arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import autoregressive_video_diffusion_amd as crattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "crattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(crattn.lib_path),
+                                reason="libcrattn.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert sorted(crattn.EXPORTS) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(crattn.lib_path)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_rope_table_bytes():
+    # 8 bytes per (cos, sin) entry; D=128 splits 44/42/42, D=64 24/20/20
+    assert crattn.rope_table_bytes(128, 21, 30, 52) == 8 * (21 * 22 + 30 * 21 + 52 * 21) == 17472
+    assert crattn.rope_table_bytes(64, 4, 8, 8) == 8 * (4 * 12 + 8 * 10 + 8 * 10) == 1664
+    assert crattn.rope_table_bytes(128, 84, 45, 80) == 35784
+    assert crattn.rope_table_bytes(127, 4, 4, 4) == 0
+    assert crattn.rope_table_bytes(128, -1, 4, 4) == 0
+
+
+def test_workspace_bytes():
+    # 480P chunk: enough query tiles to fill the chip, no split
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32760, 28080, 4680, 128) == 0
+    # one sequence-parallel rank's 585 queries: split-KV partials (O fp32 + lse)
+    ws = crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680, 128)
+    assert ws > 0 and ws % (12 * 585 * 129 * 4) == 0
+    # invalid shapes
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32759, 28080, 4680, 128) == 0
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 0, 32760, 0, 4680, 128) == 0
+
+
+def _lib():
+    return crattn.load()
+
+
+FAKE = 1 << 20          # an aligned, never-dereferenced address
+MIS = FAKE + 8          # misaligned
+
+
+def _append(**kw):
+    a = dict(q=FAKE, q_out=FAKE, k=FAKE, v=FAKE, kc=FAKE, vc=FAKE, cap=100, pos=0, table=FAKE,
+             mt=4, mh=8, mw=8, B=1, H=2, D=64, n=64, t0=3, off=0, gh=8, gw=8, dt=1)
+    a.update(kw)
+    return _lib().rope_apply_append(a["q"], a["q_out"], a["k"], a["v"], a["kc"], a["vc"],
+                                    a["cap"], a["pos"], a["table"], a["mt"], a["mh"], a["mw"],
+                                    a["B"], a["H"], a["D"], a["n"], a["t0"], a["off"], a["gh"],
+                                    a["gw"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(table=None), 1), (dict(q=None), 1), (dict(q_out=None), 1),
+    (dict(k=MIS), 1), (dict(D=60), 1), (dict(D=264), 1), (dict(n=0), 1), (dict(B=0), 1),
+    (dict(pos=40, n=64, cap=100), 1), (dict(pos=-1), 1), (dict(t0=4), 1), (dict(gh=9), 1),
+    (dict(gw=9), 1), (dict(off=1), 1), (dict(dt=7), 1), (dict(t0=-1), 1),
+])
+def test_rope_apply_append_rejects(kw, code):
+    assert _append(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, kv=256, pos0=192, L=64, out=FAKE, lse=None,
+             ws=None, wsb=0, B=1, H=2, D=64, Lq=64, scale=0.0)
+    a.update(kw)
+    return _lib().chunk_causal_attn(a["q"], a["k"], a["v"], a["cap"], a["kv"], a["pos0"], a["L"],
+                                    a["out"], a["lse"], a["ws"], a["wsb"], a["B"], a["H"], a["D"],
+                                    a["Lq"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(v=MIS), 1), (dict(lse=MIS), 1),
+    (dict(kv=257), 1), (dict(kv=255), 1), (dict(kv=0), 1), (dict(Lq=0), 1),
+    (dict(pos0=193), 1), (dict(L=0), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1),
+    (dict(D=96), 2), (dict(D=256), 2), (dict(cap=0), 1),
+    # sp-rank slice with a workspace that is too small
+    (dict(cap=32760, kv=32760, pos0=28080 + 2925, L=4680, Lq=585, H=12, D=128, ws=FAKE, wsb=16), 1),
+])
+def test_chunk_causal_attn_rejects(kw, code):
+    assert _attn(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def test_rope_precompute_rejects():
+    lib = _lib()
+    assert lib.rope_precompute(None, 64, 4, 8, 8, 10000.0, None) == 1
+    assert lib.rope_precompute(FAKE, 63, 4, 8, 8, 10000.0, None) == 1
+    assert lib.rope_precompute(FAKE, 64, 0, 8, 8, 10000.0, None) == 1
+    assert lib.rope_precompute(FAKE, 64, 4, 8, 8, 1.0, None) == 1
+    assert lib.rope_precompute(MIS, 64, 4, 8, 8, 10000.0, None) == 1
