@@ -1,0 +1,314 @@
+"""Benchmark of the chunk-causal Causal-RoPE attention step on one MI355X.
+
+One step = the whole hot path for one denoising call of a 480P Wan-1.3B-shape
+chunk: rope_apply_append (rotate Q and K of the 4680-token chunk at global
+time index 18, write Q', append K' and V to cache slot 6) followed by
+chunk_causal_attn (4680 queries x 32760 keys, 12 heads, head_dim 128, bf16).
+The cos/sin table is built once before timing, as the method prescribes
+(precomputed contiguous tables).
+
+Inputs are synthetic N(0, 1) bf16 (seeded), resident in HBM before timing.
+Several complete buffer sets (inputs, outputs and KV cache, ~1.1 GB in all)
+are used round-robin, so no step finds its data in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
+stream the library launches on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "chunk-causal attn TFLOP/s + ms/chunk (480P, 1.3B shape); % of bf16 MFMA peak"
+COUNTERS = os.path.join(ROOT, "profiles", "attn_step480_hbm_counters.txt")
+ATTN_SRC = os.path.join(ROOT, "autoregressive_video_diffusion_amd", "csrc", "attn.hip")
+
+
+def attn_flops(B, H, Lq, visible_keys, D):
+    """4*B*H*Lq*keys*D: two products (QK^T and PV), 2 flops per multiply-add.
+    Masked pairs are not counted; softmax is not counted."""
+    return 4 * B * H * Lq * visible_keys * D
+
+
+def rope_bytes(B, n, H, D, elt=2, with_q=True):
+    """Algorithmic HBM bytes of one fused RoPE/append call: read Q, K, V and
+    write Q', K', V (6 tensors of B*n*H*D) -- 4 tensors without Q."""
+    return (6 if with_q else 4) * B * n * H * D * elt
+
+
+def source_digest(path=ATTN_SRC) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM traffic per attention launch from the committed counter summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("attn_source_sha256_16") != source_digest():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+class StepBuffers:
+    def __init__(self, w, dev, seed_base):
+        import torch
+
+        from workloads import call_qkv, prior_cache
+
+        q, k, v = call_qkv(w, seed_base)
+        self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
+        kc, vc = prior_cache(w)
+        self.kc, self.vc = kc.to(dev), vc.to(dev)
+        self.q_out = torch.empty_like(self.q)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(w.B, w.H, w.lq, dtype=torch.float32, device=dev)
+
+
+def make_table(w, dev):
+    import torch
+
+    import autoregressive_video_diffusion_amd as crattn
+
+    mt, mh, mw = w.table_extents()
+    t = torch.empty(crattn.rope_table_bytes(w.D, mt, mh, mw) // 4, dtype=torch.float32, device=dev)
+    crattn.rope_precompute(t, w.D, mt, mh, mw, w.theta)
+    return t, (mt, mh, mw)
+
+
+def run_step(crattn, w, b, table, ext, ws):
+    mt, mh, mw = ext
+    crattn.rope_apply_append(b.q, b.q_out, b.k, b.v, b.kc, b.vc, w.cache_pos, table, mt, mh, mw,
+                             w.t0, w.tok_off, w.grid_h, w.grid_w)
+    crattn.chunk_causal_attn(b.q_out, b.kc, b.vc, w.kv_len, w.q_pos0, w.chunk_tokens, b.out,
+                             b.lse, ws)
+
+
+def time_attn_only(crattn, w, dev, reps=5):
+    """Average attention time (ms) of one workload, events on the stream."""
+    import torch
+
+    from workloads import normal, prior_cache
+
+    q = normal((w.B, w.lq, w.H, w.D), 1000 * w.index).to(dev)
+    kc, vc = prior_cache(w)
+    kc, vc = kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    wsb = crattn.chunk_causal_attn_workspace_bytes(w.B, w.H, w.lq, w.kv_len, w.q_pos0,
+                                                   w.chunk_tokens, w.D)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev) if wsb else None
+    for _ in range(2):
+        crattn.chunk_causal_attn(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens, out, None, ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        crattn.chunk_causal_attn(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens, out, None, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def rollout_ms(crattn, dev, reps=2):
+    """Whole 480P rollout: 7 chunks x (4 denoising calls + 1 cache update)."""
+    import torch
+
+    from autoregressive_video_diffusion_amd.rollout import ChunkRollout
+    from workloads import ROLLOUT480 as w
+
+    ro = ChunkRollout(w.B, w.H, w.D, w.frames, w.grid_h, w.grid_w, window=7, max_chunks=7,
+                      device=dev)
+    n = w.chunk_tokens
+    qkv = [tuple(torch.randn(w.B, n, w.H, w.D, device=dev).to(torch.bfloat16) for _ in range(3))
+           for _ in range(5)]
+    q_out = torch.empty_like(qkv[0][0])
+    out = torch.empty_like(q_out)
+
+    def once():
+        for c in range(7):
+            for j in range(4):
+                ro.denoise(c, *qkv[j], q_out, out)
+            ro.update(c, qkv[4][1], qkv[4][2])
+
+    once()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(reps):
+        once()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t) * 1e3 / reps
+
+
+def cpu_baseline(w, stride=1):
+    """The oracle on the host cores: attention of every `stride`-th query row
+    of the 480P chunk (all 12 heads, all 32760 keys), fp64.  The default is
+    the whole chunk, about 10 s on 16 host threads."""
+    import numpy as np
+
+    import oracle
+
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((w.B, w.lq, w.H, w.D))
+    k = rng.standard_normal((w.B, w.H, w.cap, w.D))
+    v = rng.standard_normal((w.B, w.H, w.cap, w.D))
+    rows = np.arange(0, w.lq, stride)
+    threads = oracle.default_threads()
+    t = time.perf_counter()
+    oracle.attn(q, k, v, w.kv_len, w.q_pos0, w.chunk_tokens, rows=rows, threads=threads)
+    dt = time.perf_counter() - t
+    fl = attn_flops(w.B, w.H, len(rows), w.kv_len, w.D)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"attention of {len(rows)} of {w.lq} query rows (stride {stride}) x "
+                       f"{w.H} heads vs {w.kv_len} keys, head_dim {w.D}, fp64, "
+                       f"{dt:.1f} s on {threads} threads")}
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=4, help="buffer sets used round-robin")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path has no multi-GPU leg "
+              f"(asked for --gpus {args.gpus}). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    import autoregressive_video_diffusion_amd as crattn
+    from workloads import SP480, STEP480, WIN720
+
+    crattn.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = STEP480
+    table, ext = make_table(w, dev)
+    sets = [StepBuffers(w, dev, i) for i in range(args.sets)]
+    wsb = crattn.chunk_causal_attn_workspace_bytes(w.B, w.H, w.lq, w.kv_len, w.q_pos0,
+                                                   w.chunk_tokens, w.D)
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev) if wsb else None
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        run_step(crattn, w, sets[i % len(sets)], table, ext, ws)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        b = sets[i % len(sets)]
+        e = ev[i]
+        e[0].record()
+        crattn.rope_apply_append(b.q, b.q_out, b.k, b.v, b.kc, b.vc, w.cache_pos, table, *ext,
+                                 w.t0, w.tok_off, w.grid_h, w.grid_w)
+        e[1].record()
+        crattn.chunk_causal_attn(b.q_out, b.kc, b.vc, w.kv_len, w.q_pos0, w.chunk_tokens, b.out,
+                                 b.lse, ws)
+        e[2].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = wall_ms / args.steps
+    rope_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+
+    fl = attn_flops(w.B, w.H, w.lq, w.kv_len, w.D)
+    rb = rope_bytes(w.B, w.lq, w.H, w.D)
+    attn_tflops = fl / (attn_ms * 1e-3) / 1e12
+    rope_gbs = rb / (rope_ms * 1e-3) / 1e9
+    value = fl / (ms_per_step * 1e-3) / 1e12
+
+    extras = {}
+    if not args.no_extras:
+        extras["sp480_attn_ms"] = round(time_attn_only(crattn, SP480, dev), 4)
+        extras["sp480_attn_tflops"] = round(
+            attn_flops(1, SP480.H, SP480.lq, SP480.kv_len, SP480.D)
+            / (extras["sp480_attn_ms"] * 1e-3) / 1e12, 1)
+        extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)
+        extras["rollout480_ms_per_chunk"] = round(extras["rollout480_ms_total"] / 7, 3)
+        torch.cuda.empty_cache()
+        del sets
+        torch.cuda.empty_cache()
+        extras["win720_attn_ms"] = round(time_attn_only(crattn, WIN720, dev, reps=3), 3)
+        extras["win720_attn_tflops"] = round(
+            attn_flops(1, WIN720.H, WIN720.lq, WIN720.kv_len, WIN720.D)
+            / (extras["win720_attn_ms"] * 1e-3) / 1e12, 1)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic N(0,1) bf16, seeded; inputs resident in HBM",
+        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
+                   "chunk": f"{w.frames}x{w.grid_h}x{w.grid_w}", "queries": w.lq,
+                   "keys": w.kv_len, "t0": w.t0, "buffer_sets": args.sets},
+        "ms_per_chunk": round(ms_per_step, 4),
+        "attn_ms": round(attn_ms, 4),
+        "attn_tflops": round(attn_tflops, 1),
+        "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+        "rope_append_us": round(rope_ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic()},
+        "rope_roofline": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
+                          "bytes_per_launch": rb},
+        "extras": extras,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

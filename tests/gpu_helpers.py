@@ -34,12 +34,22 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.spacing(np.abs(x).astype(np.float32)).astype(np.float64) * 65536.0
 
 
-def assert_within_bf16_ulp(got: np.ndarray, exact: np.ndarray):
+def assert_rope_bf16(got: np.ndarray, exact: np.ndarray, x: np.ndarray):
+    """bf16 RoPE output within one bf16 ulp of the exact rotation, plus the
+    fp32 evaluation error with fp32 cos/sin tables: each table entry carries
+    up to 2^-25 absolute error and the products and sum up to 2^-24 relative
+    each, so |error| <= 2^-22 * (|x| + |y|) for the input pair (x, y).  The
+    second term only matters when the rotated value nearly cancels."""
+    xa = np.abs(x)
+    pair = xa[..., 0::2] + xa[..., 1::2]
+    fp32_err = np.repeat(pair, 2, axis=-1) * 2.0 ** -22
     err = np.abs(got - exact)
-    tol = np.maximum(bf16_ulp(exact), 2.0 ** -126)
+    tol = np.maximum(bf16_ulp(exact), 2.0 ** -126) + fp32_err
     bad = err > tol
-    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} values off by more than one bf16 "
-                           f"ulp; worst {float((err / tol).max()):.2f} ulp")
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} values outside one bf16 ulp + fp32 "
+                           f"error; worst {float((err / tol).max()):.2f}x the bound")
+    within_ulp = (err <= bf16_ulp(exact)).mean()
+    assert within_ulp > 0.9999, within_ulp
 
 
 def attn_errors(got: np.ndarray, ref: np.ndarray) -> tuple[float, float]:

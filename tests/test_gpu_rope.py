@@ -11,7 +11,7 @@ import torch
 
 import autoregressive_video_diffusion_amd as crattn
 import oracle
-from gpu_helpers import ROPE_F32_ABS, assert_within_bf16_ulp, dev, f64, table
+from gpu_helpers import ROPE_F32_ABS, assert_rope_bf16, dev, f64, table
 from workloads import SP480, STEP480, TINY, WIN720, call_qkv
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,7 @@ def _check_cache(w, k, v, kc, vc, cache_pos, n, tok_off, bf16):
     k_ref = oracle.rope(f64(k), w.t0, tok_off, w.grid_h, w.grid_w, w.theta)
     got_k = f64(kc[:, :, cache_pos:cache_pos + n]).transpose(0, 2, 1, 3)
     if bf16:
-        assert_within_bf16_ulp(got_k, k_ref)
+        assert_rope_bf16(got_k, k_ref, f64(k))
     else:
         assert np.abs(got_k - k_ref).max() <= ROPE_F32_ABS
     np.testing.assert_array_equal(f64(vc[:, :, cache_pos:cache_pos + n]).transpose(0, 2, 1, 3),
@@ -99,7 +99,7 @@ def test_step480_bf16_rope_append():
     q, k, v = call_qkv(w, 0)
     q_out, kc, vc = _run(w, q, k, v, w.cap, w.cache_pos)
     q_ref = oracle.rope(f64(q), w.t0, w.tok_off, w.grid_h, w.grid_w, w.theta)
-    assert_within_bf16_ulp(f64(q_out), q_ref)
+    assert_rope_bf16(f64(q_out), q_ref, f64(q))
     exact = (f64(q_out) == oracle.round_bf16(q_ref)).mean()
     print(f"  480P bf16 rope: {exact:.5f} equal to RNE of the exact value", flush=True)
     assert exact > 0.99
@@ -120,7 +120,7 @@ def test_sp_slice_equals_rows_of_whole_chunk_bitwise():
     assert torch.equal(vc_sl[:, :, rows], vc_full[:, :, rows])
     # and against the oracle at the slice's global positions
     q_ref = oracle.rope(f64(q[:, sl]), s.t0, s.tok_off, s.grid_h, s.grid_w, s.theta)
-    assert_within_bf16_ulp(f64(q_sl), q_ref)
+    assert_rope_bf16(f64(q_sl), q_ref, f64(q[:, sl]))
 
 
 def test_cache_update_without_q_and_in_place_q():
@@ -146,7 +146,7 @@ def test_batch2_ragged_grid_fp32_and_bf16():
         if dt == "f32":
             assert np.abs(f64(q_out) - q_ref).max() <= ROPE_F32_ABS
         else:
-            assert_within_bf16_ulp(f64(q_out), q_ref)
+            assert_rope_bf16(f64(q_out), q_ref, f64(q))
         _check_cache(w, k, v, kc, vc, pos, w.lq, w.tok_off, bf16=(dt == "bf16"))
 
 
@@ -155,7 +155,7 @@ def test_win720_beyond_training_length():
     q, k, v = call_qkv(w, 0, n=1200)   # first 1200 tokens of the t0 = 81 chunk
     q_out, kc, vc = _run(w, q, k, v, w.cap, w.cache_pos, n=1200)
     q_ref = oracle.rope(f64(q), w.t0, 0, w.grid_h, w.grid_w, w.theta)
-    assert_within_bf16_ulp(f64(q_out), q_ref)
+    assert_rope_bf16(f64(q_out), q_ref, f64(q))
     _check_cache(w, k, v, kc, vc, w.cache_pos, 1200, 0, bf16=True)
 
 
