@@ -47,10 +47,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBN = 64;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 
 struct AttnKArgs {
   const uint16_t *q;
@@ -98,17 +96,42 @@ __device__ inline int v_cell(int g, int d) {
   return g * D + (d ^ ((d >> 3) & 7));
 }
 
-template <int D, int QB>
-__global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnKArgs a) {
-  constexpr int DK = D / 16;   // k-steps of the QK product
-  constexpr int DB = D / 32;   // 32-dim blocks of O
-  constexpr int KB = kBN / 32; // 32-key blocks per tile
-  constexpr int CPR = D / 8;   // 16-byte chunks per K row
-  constexpr int BM = kWaves * QB * 32;
+// The two lane halves of a wavefront hold the same query column (different
+// keys): fold a value with its partner in the other half.
+__device__ inline float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-  __shared__ uint4 k_lds[kBN * CPR];
-  __shared__ uint4 v_lds[kBN * D / 8];  // key-octet cells, 16 bytes each
-  uint2 *const v_half = reinterpret_cast<uint2 *>(v_lds);
+// Running maximum is only raised when a new score exceeds it by more than
+// 2^kRescaleLog2 (in base-2 units): until then p = 2^(s - m) stays <= 2^8,
+// harmless in bf16 P and fp32 accumulators, and O is not rescaled.  The
+// final division uses the same m for numerator and denominator, so the
+// result is unchanged.
+constexpr float kRescaleLog2 = 8.0f;
+
+template <int D, int NW, int QB, int BN, int MINB>
+__global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
+  constexpr int kBN = BN;
+  constexpr int T = NW * 64;
+  constexpr int DK = D / 16;    // k-steps of the QK product
+  constexpr int DB = D / 32;    // 32-dim blocks of O
+  constexpr int KB = kBN / 32;  // 32-key blocks per tile
+  constexpr int CPR = D / 8;    // 16-byte chunks per K row
+  constexpr int BM = NW * QB * 32;
+  constexpr int K_CELLS = kBN * CPR;        // 16-byte cells of a K tile
+  constexpr int K_PER_T = (K_CELLS + T - 1) / T;
+  constexpr int V_ITEMS = (kBN / 4) * CPR;  // (4 keys x 8 dims) items of a V tile
+  constexpr int V_PER_T = (V_ITEMS + T - 1) / T;
+
+  __shared__ uint4 k_lds[2][K_CELLS];
+  __shared__ uint4 v_lds[2][kBN * D / 8];  // key-octet cells, 16 bytes each
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -117,7 +140,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnKArgs a) {
   const int l32 = lane & 31;
 
   // ---- which (b, h, query tile, key split) this workgroup computes ----
-  int64_t bid = blockIdx.x;
+  // Workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8).
+  // Renumber so that consecutive work items -- the query tiles of one head,
+  // which stream the same K/V -- land on the same XCD and share its L2.
+  int64_t bid;
+  {
+    const int64_t G = gridDim.x;
+    const int64_t xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
+    const int64_t q = G / kXcds, r = G % kXcds;
+    bid = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
   const int split = (int)(bid % a.splits);
   bid /= a.splits;
   const int64_t tile = bid % a.n_tiles;
@@ -188,34 +220,54 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnKArgs a) {
     m_run[qb] = -INFINITY;
     l_run[qb] = 0.f;
   }
-
   const int kperm = k_row_perm(l32);
 
-  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
+  // ---- global -> register prefetch of one K/V tile (rows past limit = 0) ----
+  uint4 kreg[K_PER_T];
+  uint4 vreg[V_PER_T][4];
+  auto gload = [&](int64_t kt) {
     const int64_t key0 = kt * kBN;
-    // ---- stage K: rows as 16-byte chunks, XOR-swizzled per row ----
 #pragma unroll
-    for (int id = tid; id < kBN * CPR; id += kThreads) {
-      const int r = id / CPR, c = id % CPR;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (key0 + r < limit) x = *reinterpret_cast<const uint4 *>(kh + (key0 + r) * D + c * 8);
-      k_lds[k_cell<CPR>(r, c)] = x;
-    }
-    // ---- stage V: 4 keys x 8 dims per thread, transposed to key octets ----
-#pragma unroll
-    for (int id = tid; id < (kBN / 4) * CPR; id += kThreads) {
-      const int c = id % CPR, kq = id / CPR;
-      uint4 rw[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rw[r] = make_uint4(0, 0, 0, 0);
-        const int64_t key = key0 + kq * 4 + r;
-        if (key < limit) rw[r] = *reinterpret_cast<const uint4 *>(vh + key * D + c * 8);
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int id = tid + i * T;
+      kreg[i] = make_uint4(0, 0, 0, 0);
+      if (id < K_CELLS) {
+        const int r = id / CPR, c = id % CPR;
+        if (key0 + r < limit) kreg[i] = *reinterpret_cast<const uint4 *>(kh + (key0 + r) * D + c * 8);
       }
-      const uint32_t w0[4] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w};
-      const uint32_t w1[4] = {rw[1].x, rw[1].y, rw[1].z, rw[1].w};
-      const uint32_t w2[4] = {rw[2].x, rw[2].y, rw[2].z, rw[2].w};
-      const uint32_t w3[4] = {rw[3].x, rw[3].y, rw[3].z, rw[3].w};
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int id = tid + i * T;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vreg[i][r] = make_uint4(0, 0, 0, 0);
+      if (id < V_ITEMS) {
+        const int c = id % CPR, kq = id / CPR;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t key = key0 + kq * 4 + r;
+          if (key < limit) vreg[i][r] = *reinterpret_cast<const uint4 *>(vh + key * D + c * 8);
+        }
+      }
+    }
+  };
+  // ---- registers -> LDS: K as swizzled rows, V transposed to key octets ----
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < K_PER_T; ++i) {
+      const int id = tid + i * T;
+      if (id < K_CELLS) k_lds[buf][k_cell<CPR>(id / CPR, id % CPR)] = kreg[i];
+    }
+    uint2 *const v_half = reinterpret_cast<uint2 *>(v_lds[buf]);
+#pragma unroll
+    for (int i = 0; i < V_PER_T; ++i) {
+      const int id = tid + i * T;
+      if (id >= V_ITEMS) continue;
+      const int c = id % CPR, kq = id / CPR;
+      const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+      const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+      const uint32_t w2[4] = {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w};
+      const uint32_t w3[4] = {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w};
       const int g = kq >> 1, half = kq & 1;
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -226,102 +278,116 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fwd_kernel(AttnKArgs a) {
         v_half[v_cell<D>(g, c * 8 + dd) * 2 + half] = cell;
       }
     }
-    __syncthreads();
+  };
 
-    if (active) {
-      // ---- S^T = K Q^T for this wavefront's queries ----
-      f32x16_t s[KB][QB];
+  if (kt_begin < kt_end) gload(kt_begin);
+  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
+    const int buf = (int)((kt - kt_begin) & 1);
+    const int64_t key0 = kt * kBN;
+    lstore(buf);
+    __syncthreads();
+    // The next tile's loads are in flight while this tile is computed.  One
+    // barrier per tile suffices: a wavefront can only overwrite this buffer
+    // two tiles later, after every wavefront has passed the next barrier.
+    if (kt + 1 < kt_end) gload(kt + 1);
+    if (!active) continue;
+
+    // ---- S^T = K Q^T for this wavefront's queries ----
+    f32x16_t s[KB][QB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int row = kb * 32 + kperm;
+        const bf16x8_t kf =
+            __builtin_bit_cast(bf16x8_t, k_lds[buf][k_cell<CPR>(row, 2 * ks + hf)]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+      }
+    }
+    // ---- mask keys past the visible limit (last tile only) ----
+    if (key0 + kBN > limit) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int row = kb * 32 + kperm;
-          const bf16x8_t kf =
-              __builtin_bit_cast(bf16x8_t, k_lds[k_cell<CPR>(row, 2 * ks + hf)]);
+        for (int r = 0; r < 16; ++r) {
+          const bool dead = key0 + kb * 32 + acc_key(r, hf) >= limit;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+            if (dead) s[kb][qb][r] = -INFINITY;
         }
-      }
-      // ---- mask keys past the visible limit (last tile only) ----
-      if (key0 + kBN > limit) {
+    }
+    // ---- online softmax, per query column, lazy rescale ----
+    bf16x8_t pf[QB][KB][2];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool dead = key0 + kb * 32 + acc_key(r, hf) >= limit;
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              if (dead) s[kb][qb][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax, per query column ----
-      bf16x8_t pf[QB][KB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      const float m_cand = half_swap_max(mx) * a.scale_log2;
+      const bool need = m_cand > m_run[qb] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = need ? m_cand : m_run[qb];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
         m_run[qb] = m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            uint32_t pk[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float p0 =
-                  __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.scale_log2, -m_new));
-              const float p1 =
-                  __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.scale_log2, -m_new));
-              rs += p0 + p1;
-              pk[e] = pack_bf16(p0, p1);
-            }
-            pf[qb][kb][h2] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-          }
-        }
-        l_run[qb] = l_run[qb] * alpha + rs;
+        l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
       }
-      // ---- O^T += V^T P^T ----
+      const float m_use = m_run[qb];
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-          const int g = kb * 4 + h2 * 2 + hf;
+          uint32_t pk[4];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, v_lds[v_cell<D>(g, db * 32 + l32)]);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][h2], o[db][qb], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) {
+            const float p0 =
+                __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.scale_log2, -m_use));
+            const float p1 =
+                __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.scale_log2, -m_use));
+            rs += p0 + p1;
+            pk[e] = pack_bf16(p0, p1);
           }
+          pf[qb][kb][h2] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        }
+      }
+      l_run[qb] += rs;
+    }
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int g = kb * 4 + h2 * 2 + hf;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, v_lds[buf][v_cell<D>(g, db * 32 + l32)]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][h2], o[db][qb], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
   }
 
   if (!active) return;
   // ---- epilogue: normalise and store ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const float lt = half_swap_sum(l_run[qb]);
     const int64_t row = wrow0 + qb * 32 + l32;
     if (row >= row0 + nrows) continue;
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
@@ -400,13 +466,22 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   if (c4 == 0 && a.lse != nullptr) a.lse[r] = (mx + __log2f(wsum)) * kLn2;
 }
 
-template <int D, int QB>
-hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, QB>), dim3((unsigned)grid), dim3(kThreads), 0, s, k);
-  return hipGetLastError();
+// Launch shapes: waves per workgroup, 32-query blocks per wave, minimum
+// resident workgroups per compute unit.
+struct FwdShape {
+  int waves, qb, bn;
+};
+FwdShape fwd_shape(int D) {
+  (void)D;
+  return FwdShape{8, 1, 64};
 }
 
-int choose_qb(int D) { return D == 128 ? 2 : 2; }
+template <int D, int NW, int QB, int BN, int MINB>
+hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, BN, MINB>), dim3((unsigned)grid), dim3(NW * 64),
+                     0, s, k);
+  return hipGetLastError();
+}
 
 }  // namespace
 
@@ -414,8 +489,9 @@ AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
                    int64_t chunk_tokens, int D, bool allow_split) {
   AttnPlan p{};
   p.d = D;
-  p.bm = kWaves * choose_qb(D) * 32;
-  p.bn = kBN;
+  const FwdShape fs = fwd_shape(D);
+  p.bm = fs.waves * fs.qb * 32;
+  p.bn = fs.bn;
   const int64_t L = chunk_tokens;
   const int64_t c0 = q_pos0 / L;
   p.seg0_rows = std::min(Lq, (c0 + 1) * L - q_pos0);
@@ -428,7 +504,7 @@ AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
   const int64_t units = (int64_t)B * H * p.n_tiles;
   // Fewest key tiles any query tile has (the first segment sees the least).
   const int64_t min_keys = std::min(kv_len, (c0 + 1) * L);
-  const int64_t min_ktiles = (min_keys + kBN - 1) / kBN;
+  const int64_t min_ktiles = (min_keys + p.bn - 1) / p.bn;
   constexpr int64_t kSlots = 256;  // one workgroup per compute unit of an MI355X
   p.splits = 1;
   // Split the key range only when the query tiles alone leave most of the
@@ -478,11 +554,10 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.ws_lse = p.splits > 1 ? reinterpret_cast<float *>(static_cast<char *>(a.workspace) + o_bytes)
                           : nullptr;
   hipError_t e;
-  const int qb = choose_qb(a.D);
   if (a.D == 128)
-    e = qb == 2 ? launch_fwd<128, 2>(k, p.grid, s) : launch_fwd<128, 1>(k, p.grid, s);
+    e = launch_fwd<128, 8, 1, 64, 1>(k, p.grid, s);
   else
-    e = qb == 2 ? launch_fwd<64, 2>(k, p.grid, s) : launch_fwd<64, 1>(k, p.grid, s);
+    e = launch_fwd<64, 8, 1, 64, 1>(k, p.grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
   CombineArgs c;
   c.ws_o = k.ws_o;
