@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace crattn {
 namespace {
@@ -83,18 +84,6 @@ __device__ inline int k_row_perm(int m) {
 // Key (within a 32-key block) held by accumulator register r of lane half hf.
 __device__ inline int acc_key(int r, int hf) { return (r >> 3) * 16 + hf * 8 + (r & 7); }
 
-template <int CPR>
-__device__ inline int k_cell(int row, int chunk) {
-  return row * CPR + (chunk ^ (row & (CPR - 1)));
-}
-
-// V octet cell (g, d) -> index of its 16-byte cell in LDS.  The XOR spreads
-// the staging writes of one row group over banks; reads of 32 consecutive d
-// stay within one 512-byte run.
-template <int D>
-__device__ inline int v_cell(int g, int d) {
-  return g * D + (d ^ ((d >> 3) & 7));
-}
 
 // The two lane halves of a wavefront hold the same query column (different
 // keys): fold a value with its partner in the other half.
@@ -116,26 +105,82 @@ __device__ inline float half_swap_sum(float x) {
 // result is unchanged.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int NW, int QB, int BN, int MINB>
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i's bytes land at lds_dst + 16 * i; lds_dst must be wave-uniform.
+// Issued through asm so the compiler does not treat the LDS write as a
+// pending access to every LDS buffer (which makes it wait for the copy
+// before unrelated LDS reads); completion is tracked explicitly with
+// wait_vmcnt and made visible to the workgroup with a barrier.  The asm has
+// no register outputs; its address operand is consumed at issue.
+__device__ inline void lds_dma16(const void *gsrc, void *lds_dst) {
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t *)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most N vector-memory loads of this wavefront are outstanding.
+// An asm with a memory clobber, so the compiler keeps LDS reads after it.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// K tile swizzle: 16-byte chunk c of key row r lives at chunk c ^ k_swz(r).
+// Rows read together by one 16-lane group of the QK A-operand read
+// (k_row_perm order) get distinct low bits, so those reads do not conflict.
+template <int CPR>
+__device__ inline int k_swz(int r) {
+  return ((r & 3) | ((r >> 1) & 4) | ((r << 1) & 8)) & (CPR - 1);
+}
+// V tile swizzle, matched to the transposed reads: one 32-lane read touches
+// 4 consecutive key rows x 4 consecutive chunks; these land on 16 distinct
+// 16-byte bank groups.
+template <int D>
+__device__ inline int v_swz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+template <int D, int NW, int QB, int MINB>
 __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
-  constexpr int kBN = BN;
-  constexpr int T = NW * 64;
+  constexpr int kBN = 64;
   constexpr int DK = D / 16;    // k-steps of the QK product
   constexpr int DB = D / 32;    // 32-dim blocks of O
   constexpr int KB = kBN / 32;  // 32-key blocks per tile
-  constexpr int CPR = D / 8;    // 16-byte chunks per K row
+  constexpr int CPR = D / 8;    // 16-byte chunks per key row
   constexpr int BM = NW * QB * 32;
-  constexpr int K_CELLS = kBN * CPR;        // 16-byte cells of a K tile
-  constexpr int K_PER_T = (K_CELLS + T - 1) / T;
-  constexpr int V_ITEMS = (kBN / 4) * CPR;  // (4 keys x 8 dims) items of a V tile
-  constexpr int V_PER_T = (V_ITEMS + T - 1) / T;
+  constexpr int NS = 3;                          // LDS ring stages
+  constexpr int CELLS = kBN * CPR;               // 16-byte cells of one K (or V) tile
+  constexpr int DPW = CELLS / (64 * NW);         // DMA instructions per wave per tensor
+  static_assert(CELLS % (64 * NW) == 0, "tile must split evenly over the wavefronts");
 
-  __shared__ uint4 k_lds[2][K_CELLS];
-  __shared__ uint4 v_lds[2][kBN * D / 8];  // key-octet cells, 16 bytes each
+  // K and V tiles of the three ring stages, row-major, 16-byte cells.  One
+  // LDS object per stage (and a key loop unrolled by the stage count) lets
+  // the compiler see that a DMA into one stage never aliases reads of
+  // another, so it does not wait for the DMA before those reads.
+  __shared__ uint4 k_st0[CELLS], k_st1[CELLS], k_st2[CELLS];
+  __shared__ uint4 v_st0[CELLS], v_st1[CELLS], v_st2[CELLS];
+  auto k_stage = [&](auto S) -> uint4 * {
+    if constexpr (decltype(S)::value == 0) return k_st0;
+    else if constexpr (decltype(S)::value == 1) return k_st1;
+    else return k_st2;
+  };
+  auto v_stage = [&](auto S) -> uint4 * {
+    if constexpr (decltype(S)::value == 0) return v_st0;
+    else if constexpr (decltype(S)::value == 1) return v_st1;
+    else return v_st2;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5;
   const int l32 = lane & 31;
 
@@ -206,6 +251,10 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
+  // Settle the Q loads here (vmcnt 0; expcnt and lgkmcnt not waited on), in
+  // a form the compiler tracks, so it does not re-wait inside the key loop
+  // where the LDS copies of later tiles are in flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   f32x16_t o[DB][QB];
 #pragma unroll
@@ -222,75 +271,58 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   }
   const int kperm = k_row_perm(l32);
 
-  // ---- global -> register prefetch of one K/V tile (rows past limit = 0) ----
-  uint4 kreg[K_PER_T];
-  uint4 vreg[V_PER_T][4];
-  auto gload = [&](int64_t kt) {
+  // ---- global -> LDS DMA of one K/V tile into a ring stage ----
+  // Lane i of a DMA instruction writes the i-th 16-byte cell after the
+  // wave-uniform LDS base, so each lane fetches the global chunk that the
+  // swizzled layout puts in its cell.  Keys at or past `limit` fetch the
+  // last visible key instead: their scores are masked to -inf (p = 0) and
+  // the copied values are finite whenever the visible ones are, so nothing
+  // past the visible range is ever read.
+  auto dma = [&](int64_t kt, auto S) {
+    uint4 *const kdst = k_stage(S);
+    uint4 *const vdst = v_stage(S);
     const int64_t key0 = kt * kBN;
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int id = tid + i * T;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (id < K_CELLS) {
-        const int r = id / CPR, c = id % CPR;
-        if (key0 + r < limit) kreg[i] = *reinterpret_cast<const uint4 *>(kh + (key0 + r) * D + c * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int id = tid + i * T;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[i][r] = make_uint4(0, 0, 0, 0);
-      if (id < V_ITEMS) {
-        const int c = id % CPR, kq = id / CPR;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t key = key0 + kq * 4 + r;
-          if (key < limit) vreg[i][r] = *reinterpret_cast<const uint4 *>(vh + key * D + c * 8);
-        }
-      }
-    }
-  };
-  // ---- registers -> LDS: K as swizzled rows, V transposed to key octets ----
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int id = tid + i * T;
-      if (id < K_CELLS) k_lds[buf][k_cell<CPR>(id / CPR, id % CPR)] = kreg[i];
-    }
-    uint2 *const v_half = reinterpret_cast<uint2 *>(v_lds[buf]);
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int id = tid + i * T;
-      if (id >= V_ITEMS) continue;
-      const int c = id % CPR, kq = id / CPR;
-      const uint32_t w0[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
-      const uint32_t w1[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
-      const uint32_t w2[4] = {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w};
-      const uint32_t w3[4] = {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w};
-      const int g = kq >> 1, half = kq & 1;
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        uint2 cell;
-        cell.x = __builtin_amdgcn_perm(w1[dd >> 1], w0[dd >> 1], sel);
-        cell.y = __builtin_amdgcn_perm(w3[dd >> 1], w2[dd >> 1], sel);
-        v_half[v_cell<D>(g, c * 8 + dd) * 2 + half] = cell;
-      }
+    for (int n = 0; n < DPW; ++n) {
+      const int base = (wave * DPW + n) * 64;
+      const int cell = base + lane;
+      const int r = cell / CPR, pc = cell % CPR;
+      const int64_t key = min(key0 + r, limit - 1);
+      lds_dma16(kh + key * D + (pc ^ k_swz<CPR>(r)) * 8, kdst + base);
+      lds_dma16(vh + key * D + (pc ^ v_swz<D>(r)) * 8, vdst + base);
     }
   };
 
-  if (kt_begin < kt_end) gload(kt_begin);
-  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
-    const int buf = (int)((kt - kt_begin) & 1);
+  // V^T A-operand lane geometry for the transposed reads: a 16-lane block
+  // reads 4 key rows x 16 dims; lane j of the block points at 4 dims of row
+  // j/4, and receives 4 keys of dim (block's first dim) + j.
+  const int vblk = l32 >> 4;         // which 16-dim half of the 32-dim block
+  const int vj = lane & 15;
+  const int v_row_in = vj >> 2;      // key row within the 4-row group
+  const int v_dim = vblk * 16 + 4 * (vj & 3);
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  if (kt_begin < kt_end) dma(kt_begin, S0{});
+  if (kt_begin + 1 < kt_end) dma(kt_begin + 1, S1{});
+  // One key tile in ring stage S; the DMA two tiles ahead goes to stage S+2.
+  auto step = [&](int64_t kt, auto S) {
+    using SN = std::integral_constant<int, (decltype(S)::value + 2) % NS>;
     const int64_t key0 = kt * kBN;
-    lstore(buf);
+    // This tile's DMA is complete once at most the next tile's is pending.
+    if (kt + 1 < kt_end)
+      wait_vmcnt<2 * DPW>();
+    else
+      wait_vmcnt<0>();
+    // After the barrier every wavefront sees this tile, and every wavefront
+    // has finished the previous tile, whose stage the DMA below refills.
     __syncthreads();
-    // The next tile's loads are in flight while this tile is computed.  One
-    // barrier per tile suffices: a wavefront can only overwrite this buffer
-    // two tiles later, after every wavefront has passed the next barrier.
-    if (kt + 1 < kt_end) gload(kt + 1);
-    if (!active) continue;
+    if (kt + 2 < kt_end) dma(kt + 2, SN{});
+    if (!active) return;
+
+    const uint4 *__restrict__ kt_lds = k_stage(S);
+    const char *__restrict__ vt_lds = reinterpret_cast<const char *>(v_stage(S));
 
     // ---- S^T = K Q^T for this wavefront's queries ----
     f32x16_t s[KB][QB];
@@ -306,7 +338,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       for (int kb = 0; kb < KB; ++kb) {
         const int row = kb * 32 + kperm;
         const bf16x8_t kf =
-            __builtin_bit_cast(bf16x8_t, k_lds[buf][k_cell<CPR>(row, 2 * ks + hf)]);
+            __builtin_bit_cast(bf16x8_t, kt_lds[row * CPR + ((2 * ks + hf) ^ k_swz<CPR>(row))]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
@@ -371,16 +403,32 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int g = kb * 4 + h2 * 2 + hf;
+        // keys kb*32 + h2*16 + 8*hf + (0..7): two transposed 4-key reads
+        const int vr0 = kb * 32 + h2 * 16 + 8 * hf + v_row_in;
+        const int vr1 = vr0 + 4;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, v_lds[buf][v_cell<D>(g, db * 32 + l32)]);
+          const int d = db * 32 + v_dim;
+          const int c = d >> 3, half = (d >> 2) & 1;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t *)(vt_lds + vr0 * (D * 2) + ((c ^ v_swz<D>(vr0)) << 4) + (half << 3)));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4_t *)(vt_lds + vr1 * (D * 2) + ((c ^ v_swz<D>(vr1)) << 4) + (half << 3)));
+          const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][h2], o[db][qb], 0, 0, 0);
         }
       }
     }
+  };
+  for (int64_t kt = kt_begin; kt < kt_end;) {
+    step(kt++, S0{});
+    if (kt >= kt_end) break;
+    step(kt++, S1{});
+    if (kt >= kt_end) break;
+    step(kt++, S2{});
   }
 
   if (!active) return;
@@ -476,10 +524,10 @@ FwdShape fwd_shape(int D) {
   return FwdShape{8, 1, 64};
 }
 
-template <int D, int NW, int QB, int BN, int MINB>
+template <int D, int NW, int QB, int MINB>
 hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, BN, MINB>), dim3((unsigned)grid), dim3(NW * 64),
-                     0, s, k);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                     s, k);
   return hipGetLastError();
 }
 
@@ -555,9 +603,9 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
                           : nullptr;
   hipError_t e;
   if (a.D == 128)
-    e = launch_fwd<128, 8, 1, 64, 1>(k, p.grid, s);
+    e = launch_fwd<128, 8, 1, 1>(k, p.grid, s);
   else
-    e = launch_fwd<64, 8, 1, 64, 1>(k, p.grid, s);
+    e = launch_fwd<64, 8, 1, 1>(k, p.grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
   CombineArgs c;
   c.ws_o = k.ws_o;
