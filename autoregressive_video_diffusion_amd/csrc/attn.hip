@@ -109,22 +109,6 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-// Global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
-// lane i's bytes land at lds_dst + 16 * i; lds_dst must be wave-uniform.
-// Issued through asm so the compiler does not treat the LDS write as a
-// pending access to every LDS buffer (which makes it wait for the copy
-// before unrelated LDS reads); completion is tracked explicitly with
-// wait_vmcnt and made visible to the workgroup with a barrier.  The asm has
-// no register outputs; its address operand is consumed at issue.
-__device__ inline void lds_dma16(const void *gsrc, void *lds_dst) {
-  typedef __attribute__((address_space(3))) char lds_char_t;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t *)lds_dst);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(gsrc)
-               : "memory", "m0");
-}
-
 // Wait until at most N vector-memory loads of this wavefront are outstanding.
 // An asm with a memory clobber, so the compiler keeps LDS reads after it.
 template <int N>
@@ -133,20 +117,42 @@ __device__ inline void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// K tile swizzle: 16-byte chunk c of key row r lives at chunk c ^ k_swz(r).
-// Rows read together by one 16-lane group of the QK A-operand read
-// (k_row_perm order) get distinct low bits, so those reads do not conflict.
-template <int CPR>
-__device__ inline int k_swz(int r) {
-  return ((r & 3) | ((r >> 1) & 4) | ((r << 1) & 8)) & (CPR - 1);
+// LDS row pitches, in 16-byte cells.  Rows are padded instead of swizzled
+// so that every fragment read is a per-lane base plus an immediate offset.
+//  * K: CPR + 1 cells.  The QK A-operand read has 16 lanes fetch the same
+//    chunk of 16 different rows; a 16-byte shift per row puts them on 16
+//    distinct bank groups.
+//  * V: CPR + 4 cells.  A transposed V read has 32 lanes fetch 4 consecutive
+//    rows x 64 bytes; a row pitch of 64 mod 256 bytes keeps them disjoint.
+// Global -> LDS copy with a wave-uniform global base and a per-lane 32-bit
+// byte offset (the scalar-base form of global_load_lds_dwordx4); see
+// Lane i's 16 bytes land at lds_dst + 16 * i; lds_dst must be wave-uniform.
+// Issued through asm so the compiler does not treat the LDS write as a
+// pending access to every LDS buffer (which makes it wait for the copy
+// before unrelated LDS reads); completion is tracked explicitly with
+// wait_vmcnt and made visible to the workgroup with a barrier.  The asm has
+// no register outputs; its operands are consumed at issue.  M0 (the LDS
+// base) is set inside the asm;
+// nothing else in these kernels uses M0, so listing it as clobbered only
+// tells the compiler not to assume its value afterwards.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_dma16_sv(const void *gbase, uint32_t voff, void *lds_dst) {
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t *)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(gbase)
+               : "memory", "m0");
 }
-// V tile swizzle, matched to the transposed reads: one 32-lane read touches
-// 4 consecutive key rows x 4 consecutive chunks; these land on 16 distinct
-// 16-byte bank groups.
+#pragma clang diagnostic pop
+
 template <int D>
-__device__ inline int v_swz(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
+struct Pitch {
+  static constexpr int CPR = D / 8;
+  static constexpr int K = CPR + 1;
+  static constexpr int V = CPR + 4;
+};
 
 template <int D, int NW, int QB, int MINB>
 __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
@@ -156,27 +162,22 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   constexpr int KB = kBN / 32;  // 32-key blocks per tile
   constexpr int CPR = D / 8;    // 16-byte chunks per key row
   constexpr int BM = NW * QB * 32;
-  constexpr int NS = 3;                          // LDS ring stages
-  constexpr int CELLS = kBN * CPR;               // 16-byte cells of one K (or V) tile
-  constexpr int DPW = CELLS / (64 * NW);         // DMA instructions per wave per tensor
-  static_assert(CELLS % (64 * NW) == 0, "tile must split evenly over the wavefronts");
+  constexpr int NS = 4;                          // LDS ring stages
+  constexpr int KP = Pitch<D>::K, VP = Pitch<D>::V;
+  constexpr int K_CELLS = kBN * KP;              // 16-byte cells of one K tile (padded)
+  constexpr int V_CELLS = kBN * VP;
+  constexpr int K_INSTR = K_CELLS / 64;          // DMA instructions per K tile (= KP)
+  constexpr int V_INSTR = V_CELLS / 64;
+  constexpr int K_SLOTS = (K_INSTR + NW - 1) / NW;  // per wavefront
+  constexpr int V_SLOTS = (V_INSTR + NW - 1) / NW;
 
-  // K and V tiles of the three ring stages, row-major, 16-byte cells.  One
-  // LDS object per stage (and a key loop unrolled by the stage count) lets
-  // the compiler see that a DMA into one stage never aliases reads of
-  // another, so it does not wait for the DMA before those reads.
-  __shared__ uint4 k_st0[CELLS], k_st1[CELLS], k_st2[CELLS];
-  __shared__ uint4 v_st0[CELLS], v_st1[CELLS], v_st2[CELLS];
-  auto k_stage = [&](auto S) -> uint4 * {
-    if constexpr (decltype(S)::value == 0) return k_st0;
-    else if constexpr (decltype(S)::value == 1) return k_st1;
-    else return k_st2;
-  };
-  auto v_stage = [&](auto S) -> uint4 * {
-    if constexpr (decltype(S)::value == 0) return v_st0;
-    else if constexpr (decltype(S)::value == 1) return v_st1;
-    else return v_st2;
-  };
+  // K and V tiles of the four ring stages, row-major with padded rows,
+  // 16-byte cells.  Tile t lives in stage t % 4: its K is read while tile
+  // t-1 is finished, its V one tile later, and its copy is issued three
+  // tiles ahead.  The copies are asm the compiler does not track, so the
+  // ordering against LDS reads is explicit: wait_vmcnt + barrier.
+  constexpr int STAGE_CELLS = K_CELLS + V_CELLS;
+  __shared__ uint4 lds_ring[NS * STAGE_CELLS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -226,10 +227,11 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   const int64_t row0 = seg_row0 + t_in * BM;
   const int64_t nrows = min((int64_t)BM, seg_rows - t_in * BM);
   const int64_t q_chunk = a.q_pos0 / a.L + seg;
-  const int64_t limit = min(a.kv_len, (q_chunk + 1) * a.L);
-  const int64_t nkt = (limit + kBN - 1) / kBN;
-  const int64_t kt_begin = split * nkt / a.splits;
-  const int64_t kt_end = (split + 1) * nkt / a.splits;
+  // keys of one head fit 32-bit indices (the front end bounds cap * D)
+  const int limit = (int)min(a.kv_len, (q_chunk + 1) * a.L);
+  const int nkt = (limit + kBN - 1) / kBN;
+  const int kt_begin = split * nkt / a.splits;
+  const int kt_end = (split + 1) * nkt / a.splits;
 
   const int64_t head_off = ((int64_t)b * a.H + h) * a.cap * D;
   const uint16_t *__restrict__ kh = a.k + head_off;
@@ -272,26 +274,58 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   const int kperm = k_row_perm(l32);
 
   // ---- global -> LDS DMA of one K/V tile into a ring stage ----
-  // Lane i of a DMA instruction writes the i-th 16-byte cell after the
-  // wave-uniform LDS base, so each lane fetches the global chunk that the
-  // swizzled layout puts in its cell.  Keys at or past `limit` fetch the
-  // last visible key instead: their scores are masked to -inf (p = 0) and
-  // the copied values are finite whenever the visible ones are, so nothing
-  // past the visible range is ever read.
-  auto dma = [&](int64_t kt, auto S) {
-    uint4 *const kdst = k_stage(S);
-    uint4 *const vdst = v_stage(S);
-    const int64_t key0 = kt * kBN;
+  // DMA instruction j of a tile fills padded cells [64j, 64j + 64); lane i
+  // writes cell 64j + i, so each lane fetches the global 16-byte chunk of its
+  // cell's (row, column).  Pad cells are skipped.  Instruction j is issued
+  // by wavefront j % NW.  The per-lane byte offsets within a tile are fixed;
+  // only the scalar tile base moves.  In the tile holding `limit`, keys at
+  // or past it fetch the last visible key instead: their scores are masked
+  // to -inf (p = 0) and the copied values are finite whenever the visible
+  // ones are, so nothing past the visible range is ever read.
+  // Byte offset of a padded cell's global chunk within a tile, or ~0 for a
+  // pad cell (skipped).
+  auto cell_off = [&](int cell, int pitch) -> uint32_t {
+    const int row = cell / pitch;
+    const int c = cell - row * pitch;
+    return c < CPR ? (uint32_t)(row * D + c * 8) * 2u : ~0u;
+  };
+  constexpr uint32_t kRowBytes = D * 2;
+  uint32_t dma_k_off[K_SLOTS], dma_v_off[V_SLOTS];
 #pragma unroll
-    for (int n = 0; n < DPW; ++n) {
-      const int base = (wave * DPW + n) * 64;
-      const int cell = base + lane;
-      const int r = cell / CPR, pc = cell % CPR;
-      const int64_t key = min(key0 + r, limit - 1);
-      lds_dma16(kh + key * D + (pc ^ k_swz<CPR>(r)) * 8, kdst + base);
-      lds_dma16(vh + key * D + (pc ^ v_swz<D>(r)) * 8, vdst + base);
+  for (int n = 0; n < K_SLOTS; ++n) dma_k_off[n] = cell_off((wave + n * NW) * 64 + lane, KP);
+#pragma unroll
+  for (int n = 0; n < V_SLOTS; ++n) dma_v_off[n] = cell_off((wave + n * NW) * 64 + lane, VP);
+  // In the edge tile, rows past the last visible key re-read that key.
+  auto clamp_off = [&](uint32_t off, int last) -> uint32_t {
+    const int r = (int)(off / kRowBytes);
+    return off - (uint32_t)(r - min(r, last)) * kRowBytes;
+  };
+  auto dma = [&](int kt, int stage) {
+    uint4 *const kdst = lds_ring + stage * STAGE_CELLS;
+    uint4 *const vdst = kdst + K_CELLS;
+    const int key0 = kt * kBN;
+    const uint16_t *kb = kh + key0 * D;
+    const uint16_t *vb = vh + key0 * D;
+    const bool edge = key0 + kBN > limit;
+    const int last = limit - 1 - key0;
+#pragma unroll
+    for (int n = 0; n < K_SLOTS; ++n) {
+      const int j = wave + n * NW;
+      if (j < K_INSTR && dma_k_off[n] != ~0u)
+        lds_dma16_sv(kb, edge ? clamp_off(dma_k_off[n], last) : dma_k_off[n], kdst + j * 64);
+    }
+#pragma unroll
+    for (int n = 0; n < V_SLOTS; ++n) {
+      const int j = wave + n * NW;
+      if (j < V_INSTR && dma_v_off[n] != ~0u)
+        lds_dma16_sv(vb, edge ? clamp_off(dma_v_off[n], last) : dma_v_off[n], vdst + j * 64);
     }
   };
+  // Fewest LDS-DMA instructions any wavefront issues per tile.  Loads retire
+  // in order, so "at most kDmaMin outstanding" after a later tile was issued
+  // implies every earlier tile's copies are complete.
+  constexpr int kDmaMin = K_INSTR / NW + V_INSTR / NW;
+  static_assert(kDmaMin >= 1 && 2 * kDmaMin < 16, "vmcnt wait range");
 
   // V^T A-operand lane geometry for the transposed reads: a 16-lane block
   // reads 4 key rows x 16 dims; lane j of the block points at 4 dims of row
@@ -301,50 +335,29 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   const int v_row_in = vj >> 2;      // key row within the 4-row group
   const int v_dim = vblk * 16 + 4 * (vj & 3);
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  if (kt_begin < kt_end) dma(kt_begin, S0{});
-  if (kt_begin + 1 < kt_end) dma(kt_begin + 1, S1{});
-  // One key tile in ring stage S; the DMA two tiles ahead goes to stage S+2.
-  auto step = [&](int64_t kt, auto S) {
-    using SN = std::integral_constant<int, (decltype(S)::value + 2) % NS>;
-    const int64_t key0 = kt * kBN;
-    // This tile's DMA is complete once at most the next tile's is pending.
-    if (kt + 1 < kt_end)
-      wait_vmcnt<2 * DPW>();
-    else
-      wait_vmcnt<0>();
-    // After the barrier every wavefront sees this tile, and every wavefront
-    // has finished the previous tile, whose stage the DMA below refills.
-    __syncthreads();
-    if (kt + 2 < kt_end) dma(kt + 2, SN{});
-    if (!active) return;
-
-    const uint4 *__restrict__ kt_lds = k_stage(S);
-    const char *__restrict__ vt_lds = reinterpret_cast<const char *>(v_stage(S));
-
-    // ---- S^T = K Q^T for this wavefront's queries ----
-    f32x16_t s[KB][QB];
+  // ---- S^T = K Q^T of one tile from ring stage S ----
+  auto qk = [&](int stage, f32x16_t (&sc)[KB][QB]) {
+    const uint4 *__restrict__ kt_lds = lds_ring + stage * STAGE_CELLS;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][qb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int row = kb * 32 + kperm;
         const bf16x8_t kf =
-            __builtin_bit_cast(bf16x8_t, kt_lds[row * CPR + ((2 * ks + hf) ^ k_swz<CPR>(row))]);
+            __builtin_bit_cast(bf16x8_t, kt_lds[(kb * 32 + kperm) * KP + 2 * ks + hf]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[kb][qb], 0, 0, 0);
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sc[kb][qb], 0, 0, 0);
       }
     }
-    // ---- mask keys past the visible limit (last tile only) ----
+  };
+  // ---- softmax, part 1 (branchy): edge mask, running max, lazy rescale ----
+  auto softmax_prep = [&](f32x16_t (&sc)[KB][QB], int key0) {
     if (key0 + kBN > limit) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -353,18 +366,16 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
           const bool dead = key0 + kb * 32 + acc_key(r, hf) >= limit;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            if (dead) s[kb][qb][r] = -INFINITY;
+            if (dead) sc[kb][qb][r] = -INFINITY;
         }
     }
-    // ---- online softmax, per query column, lazy rescale ----
-    bf16x8_t pf[QB][KB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][qb][r]);
       const float m_cand = half_swap_max(mx) * a.scale_log2;
       const bool need = m_cand > m_run[qb] + kRescaleLog2;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -377,6 +388,12 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
       }
+    }
+  };
+  // ---- softmax, part 2 (branch-free): p = 2^(s*c - m), row sums, bf16 P ----
+  auto softmax_exp = [&](const f32x16_t (&sc)[KB][QB], bf16x8_t (&pf)[QB][KB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float m_use = m_run[qb];
       float rs = 0.f;
 #pragma unroll
@@ -387,9 +404,9 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float p0 =
-                __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.scale_log2, -m_use));
+                __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][h2 * 8 + 2 * e], a.scale_log2, -m_use));
             const float p1 =
-                __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.scale_log2, -m_use));
+                __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][h2 * 8 + 2 * e + 1], a.scale_log2, -m_use));
             rs += p0 + p1;
             pk[e] = pack_bf16(p0, p1);
           }
@@ -398,7 +415,11 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       }
       l_run[qb] += rs;
     }
-    // ---- O^T += V^T P^T ----
+  };
+  // ---- O^T += V^T P^T of one tile from ring stage S ----
+  auto pv = [&](int stage, const bf16x8_t (&pf)[QB][KB][2]) {
+    const char *__restrict__ vt_lds =
+        reinterpret_cast<const char *>(lds_ring + stage * STAGE_CELLS + K_CELLS);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
@@ -408,12 +429,11 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
         const int vr1 = vr0 + 4;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = db * 32 + v_dim;
-          const int c = d >> 3, half = (d >> 2) & 1;
+          const int dbyte = (db * 32 + v_dim) * 2;  // byte offset of 4 dims within a row
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(vt_lds + vr0 * (D * 2) + ((c ^ v_swz<D>(vr0)) << 4) + (half << 3)));
+              (lds_i16x4_t *)(vt_lds + vr0 * (VP * 16) + dbyte));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(vt_lds + vr1 * (D * 2) + ((c ^ v_swz<D>(vr1)) << 4) + (half << 3)));
+              (lds_i16x4_t *)(vt_lds + vr1 * (VP * 16) + dbyte));
           const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
           const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
 #pragma unroll
@@ -423,12 +443,65 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       }
     }
   };
-  for (int64_t kt = kt_begin; kt < kt_end;) {
-    step(kt++, S0{});
+
+  // ---- the key loop, software-pipelined across tiles ----
+  // Step for tile kt: wait for tile kt+1's copy, barrier, issue the copy of
+  // tile kt+3, then compute S(kt+1) = K(kt+1) Q^T on the matrix cores while
+  // the vector ALUs turn S(kt) into probabilities, and finish with
+  // O += P(kt) V(kt).  The two S buffers alternate (loop unrolled by 2).
+  f32x16_t sbuf[2][KB][QB];
+  if (kt_begin < kt_end) dma(kt_begin, 0);
+  if (kt_begin + 1 < kt_end) dma(kt_begin + 1, 1);
+  if (kt_begin + 2 < kt_end) dma(kt_begin + 2, 2);
+  if (kt_begin + 2 < kt_end)
+    wait_vmcnt<2 * kDmaMin>();
+  else if (kt_begin + 1 < kt_end)
+    wait_vmcnt<kDmaMin>();
+  else
+    wait_vmcnt<0>();
+  __syncthreads();
+  if (active && kt_begin < kt_end) qk(0, sbuf[0]);
+
+  auto step = [&](int kt, auto P) {
+    constexpr int par = decltype(P)::value;
+    const int stage = (kt - kt_begin) & (NS - 1);
+    const bool more = kt + 1 < kt_end;
+    if (more) {
+      // tile kt+1 has landed once at most tile kt+2's copies are pending
+      if (kt + 2 < kt_end)
+        wait_vmcnt<kDmaMin>();
+      else
+        wait_vmcnt<0>();
+      // every wavefront now sees tile kt+1 and has finished tile kt-1, whose
+      // stage the copy of tile kt+3 refills
+      __syncthreads();
+      if (kt + 3 < kt_end) dma(kt + 3, (stage + 3) & (NS - 1));
+    }
+    if (!active) return;
+    f32x16_t (&cur)[KB][QB] = sbuf[par];
+    f32x16_t (&nxt)[KB][QB] = sbuf[par ^ 1];
+    softmax_prep(cur, kt * kBN);
+    bf16x8_t pf[QB][KB][2];
+    // S of the next tile, unconditionally so that it shares a basic block
+    // with the softmax it overlaps.  On the last tile it reads a stage no
+    // copy is writing (stale, in bounds) and the result is never used.
+    qk((stage + 1) & (NS - 1), nxt);
+    softmax_exp(cur, pf);
+    // interleave: each S MFMA with a share of the softmax
+#pragma unroll
+    for (int i = 0; i < KB * DK * QB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    pv(stage, pf);
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  for (int kt = kt_begin; kt < kt_end;) {
+    step(kt++, P0{});
     if (kt >= kt_end) break;
-    step(kt++, S1{});
-    if (kt >= kt_end) break;
-    step(kt++, S2{});
+    step(kt++, P1{});
   }
 
   if (!active) return;
