@@ -11,8 +11,8 @@
 //
 // The append pass is bound by HBM bandwidth: per token and head it reads
 // Q, K, V rows and writes Q', K', V rows once, 16 bytes per lane per tensor,
-// with every wavefront covering whole 256-byte rows.  The table (tens of KB)
-// stays in L1/L2.
+// with every wavefront covering whole 256-byte rows, and streaming stores.
+// The table (tens of KB) stays in L1/L2.
 #include "crattn_internal.h"
 #include "../../include/crattn.h"
 
@@ -51,6 +51,15 @@ __global__ void __launch_bounds__(256) rope_table_kernel(RopeTableArgs a, int to
   a.table[e] = make_float2((float)c, (float)s);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// Streaming (non-temporal) 16-byte store.  Every output of the append pass
+// is written once and not re-read by this kernel; streaming stores avoid
+// allocating them in the caches on the way out (measured: 19.1 -> 13.9 us on
+// the 480P chunk, 4.5 -> 6.2 TB/s).  Non-temporal loads did not help.
+__device__ inline void ntstore(const uint4 &x, void *p) {
+  const u32x4_t v = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
+}
 struct Pos {
   uint32_t t, h, w;
 };
@@ -136,12 +145,13 @@ __global__ void __launch_bounds__(256) rope_append_bf16_kernel(RopeAppendArgs a,
 
   const uint4 ko = make_uint4(rot_bf16(kv.x, cs0), rot_bf16(kv.y, cs1), rot_bf16(kv.z, cs2),
                               rot_bf16(kv.w, cs3));
-  *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.k_cache) + cache_off) = ko;
-  *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.v_cache) + cache_off) = vv;
+  ntstore(ko, static_cast<uint16_t *>(a.k_cache) + cache_off);
+  ntstore(vv, static_cast<uint16_t *>(a.v_cache) + cache_off);
   if (has_q) {
     const uint4 qo = make_uint4(rot_bf16(qv.x, cs0), rot_bf16(qv.y, cs1), rot_bf16(qv.z, cs2),
                                 rot_bf16(qv.w, cs3));
-    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.q_out) + in_off) = qo;
+    ntstore(qo, static_cast<uint16_t *>(a.q_out) + in_off);
+
   }
 }
 
@@ -176,13 +186,17 @@ __global__ void __launch_bounds__(256) rope_append_f32_kernel(RopeAppendArgs a, 
   const float2 cs0 = pair_cs(a.table, tg, c * 2 + 0, p);
   const float2 cs1 = pair_cs(a.table, tg, c * 2 + 1, p);
   const float2 k0 = rot_f32(kv.x, kv.y, cs0), k1 = rot_f32(kv.z, kv.w, cs1);
-  *reinterpret_cast<float4 *>(static_cast<float *>(a.k_cache) + cache_off) =
-      make_float4(k0.x, k0.y, k1.x, k1.y);
-  *reinterpret_cast<float4 *>(static_cast<float *>(a.v_cache) + cache_off) = vv;
+  ntstore(make_uint4(__float_as_uint(k0.x), __float_as_uint(k0.y), __float_as_uint(k1.x),
+                     __float_as_uint(k1.y)),
+          static_cast<float *>(a.k_cache) + cache_off);
+  ntstore(make_uint4(__float_as_uint(vv.x), __float_as_uint(vv.y), __float_as_uint(vv.z),
+                     __float_as_uint(vv.w)),
+          static_cast<float *>(a.v_cache) + cache_off);
   if (has_q) {
     const float2 q0 = rot_f32(qv.x, qv.y, cs0), q1 = rot_f32(qv.z, qv.w, cs1);
-    *reinterpret_cast<float4 *>(static_cast<float *>(a.q_out) + in_off) =
-        make_float4(q0.x, q0.y, q1.x, q1.y);
+    ntstore(make_uint4(__float_as_uint(q0.x), __float_as_uint(q0.y), __float_as_uint(q1.x),
+                       __float_as_uint(q1.y)),
+            static_cast<float *>(a.q_out) + in_off);
   }
 }
 
