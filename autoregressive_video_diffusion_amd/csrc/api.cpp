@@ -198,6 +198,10 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, i
     return fail(CRATTN_EINVAL, "chunk_causal_attn: scale must be finite and >= 0");
   if ((double)B * H * (double)cap * D > (double)kMaxElems)
     return fail(CRATTN_EINVAL, "chunk_causal_attn: cache element count exceeds 2^40");
+  // the kernel indexes the keys of one head (cap rows of D elements) in 32 bits
+  if ((double)cap * D >= 2147483648.0)
+    return fail(CRATTN_EINVAL, "chunk_causal_attn: cap * head_dim = %.0f must be below 2^31",
+                (double)cap * D);
   const bool split_ok = workspace != nullptr;
   const crattn::AttnPlan plan =
       crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, split_ok);

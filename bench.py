@@ -46,13 +46,17 @@ def rope_bytes(B, n, H, D, elt=2, with_q=True):
     return (6 if with_q else 4) * B * n * H * D * elt
 
 
+ROPE_SRC = os.path.join(ROOT, "autoregressive_video_diffusion_amd", "csrc", "rope.hip")
+
+
 def source_digest(path=ATTN_SRC) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM traffic per attention launch from the committed counter summary,
-    if it was taken on the current kernel source; else None."""
+def read_traffic(kernel="attn"):
+    """HBM bytes per launch of the attention ("attn") or RoPE/append ("rope")
+    kernel from the committed counter summary, if it was taken on the current
+    kernel source; else None."""
     if not os.path.exists(COUNTERS):
         return None
     kv = {}
@@ -60,10 +64,12 @@ def read_traffic():
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("attn_source_sha256_16") != source_digest():
+    src, key = ((ATTN_SRC, "traffic_bytes_per_launch") if kernel == "attn" else
+                (ROPE_SRC, "rope_traffic_bytes_per_launch"))
+    if kv.get(f"{kernel}_source_sha256_16") != source_digest(src):
         return None
     try:
-        return int(float(kv["traffic_bytes_per_launch"]))
+        return int(float(kv[key]))
     except (KeyError, ValueError):
         return None
 
@@ -199,8 +205,10 @@ def copy_calibration():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # the attention launches keep speeding up over the first ~30 ms of work
+    # (clock ramp); 40 warmup steps (~40 ms) reach the steady state
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--sets", type=int, default=4, help="buffer sets used round-robin")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -317,7 +325,8 @@ def main():
                      "traffic": read_traffic()},
         "rope_roofline": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
-                          "bytes_per_launch": rb, "launches_timed": burst},
+                          "bytes_per_launch": rb, "launches_timed": burst,
+                          "traffic": read_traffic("rope")},
         "extras": extras,
     }
     if not args.no_cpu_baseline:

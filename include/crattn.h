@@ -179,7 +179,8 @@ size_t chunk_causal_attn_workspace_bytes(int B, int H, int64_t Lq, int64_t kv_le
  *
  * Errors: EINVAL for NULL q/k_cache/v_cache/out, misaligned pointers, B, H or
  * Lq < 1, kv_len < 1 or > cap, q_pos0 < 0, chunk_tokens < 1, an incomplete
- * last chunk (see above), a non-finite or negative scale, a workspace that is
+ * last chunk (see above), a non-finite or negative scale, cap * D >= 2^31
+ * (the keys of one head are indexed in 32 bits), a workspace that is
  * non-NULL but too small; ENOTSUP for D other than 64 or 128; EHIP.
  */
 int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache,

@@ -95,6 +95,8 @@ def _attn(**kw):
     (dict(kv=257), 1), (dict(kv=255), 1), (dict(kv=0), 1), (dict(Lq=0), 1),
     (dict(pos0=193), 1), (dict(L=0), 1), (dict(scale=-1.0), 1), (dict(scale=float("nan")), 1),
     (dict(D=96), 2), (dict(D=256), 2), (dict(cap=0), 1),
+    # one head's keys must be indexable in 32 bits: cap * D < 2^31
+    (dict(cap=1 << 25), 1),
     # sp-rank slice with a workspace that is too small
     (dict(cap=32760, kv=32760, pos0=28080 + 2925, L=4680, Lq=585, H=12, D=128, ws=FAKE, wsb=16), 1),
 ])
