@@ -125,24 +125,22 @@ __device__ inline void wait_vmcnt() {
 //  * V: CPR + 4 cells.  A transposed V read has 32 lanes fetch 4 consecutive
 //    rows x 64 bytes; a row pitch of 64 mod 256 bytes keeps them disjoint.
 // Global -> LDS copy with a wave-uniform global base and a per-lane 32-bit
-// byte offset (the scalar-base form of global_load_lds_dwordx4); see
-// Lane i's 16 bytes land at lds_dst + 16 * i; lds_dst must be wave-uniform.
+// byte offset (the scalar-base form of global_load_lds_dwordx4): lane i's 16
+// bytes land at LDS byte address lds_addr + 16 * i; lds_addr is wave-uniform.
 // Issued through asm so the compiler does not treat the LDS write as a
 // pending access to every LDS buffer (which makes it wait for the copy
 // before unrelated LDS reads); completion is tracked explicitly with
 // wait_vmcnt and made visible to the workgroup with a barrier.  The asm has
 // no register outputs; its operands are consumed at issue.  M0 (the LDS
-// base) is set inside the asm;
-// nothing else in these kernels uses M0, so listing it as clobbered only
-// tells the compiler not to assume its value afterwards.
+// base) is set inside the asm; nothing else in these kernels uses M0, so
+// listing it as clobbered only tells the compiler not to assume its value
+// afterwards.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void lds_dma16_sv(const void *gbase, uint32_t voff, void *lds_dst) {
-  typedef __attribute__((address_space(3))) char lds_char_t;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t *)lds_dst);
+__device__ inline void lds_dma16_sv(const void *gbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(m0), "v"(voff), "s"(gbase)
+               : "s"(lds_addr), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -276,18 +274,18 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   // ---- global -> LDS DMA of one K/V tile into a ring stage ----
   // DMA instruction j of a tile fills padded cells [64j, 64j + 64); lane i
   // writes cell 64j + i, so each lane fetches the global 16-byte chunk of its
-  // cell's (row, column).  Pad cells are skipped.  Instruction j is issued
-  // by wavefront j % NW.  The per-lane byte offsets within a tile are fixed;
-  // only the scalar tile base moves.  In the tile holding `limit`, keys at
-  // or past it fetch the last visible key instead: their scores are masked
-  // to -inf (p = 0) and the copied values are finite whenever the visible
-  // ones are, so nothing past the visible range is ever read.
-  // Byte offset of a padded cell's global chunk within a tile, or ~0 for a
-  // pad cell (skipped).
+  // cell's (row, column); a lane on a pad cell fetches its row's first chunk
+  // (a line the same instruction reads anyway) into that never-read cell, so
+  // no lane is masked off.  Instruction j is issued by wavefront j % NW.  The
+  // per-lane byte offsets within a tile are fixed; only the scalar tile base
+  // and the LDS address move.  In the tile holding `limit`, keys at or past
+  // it fetch the last visible key instead: their scores are masked to -inf
+  // (p = 0) and the copied values are finite whenever the visible ones are,
+  // so nothing past the visible range is ever read.
   auto cell_off = [&](int cell, int pitch) -> uint32_t {
     const int row = cell / pitch;
     const int c = cell - row * pitch;
-    return c < CPR ? (uint32_t)(row * D + c * 8) * 2u : ~0u;
+    return (uint32_t)(row * D + (c < CPR ? c * 8 : 0)) * 2u;
   };
   constexpr uint32_t kRowBytes = D * 2;
   uint32_t dma_k_off[K_SLOTS], dma_v_off[V_SLOTS];
@@ -300,25 +298,41 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     const int r = (int)(off / kRowBytes);
     return off - (uint32_t)(r - min(r, last)) * kRowBytes;
   };
+  // LDS byte address of the ring (one generic-to-LDS conversion)
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(lds_ring));
+  // (slots n with (n + 1) * NW <= instructions exist for every wavefront:
+  // the test is decided at compile time)
   auto dma = [&](int kt, int stage) {
-    uint4 *const kdst = lds_ring + stage * STAGE_CELLS;
-    uint4 *const vdst = kdst + K_CELLS;
+    const uint32_t kdst = ring_lds + (uint32_t)stage * (STAGE_CELLS * 16);
+    const uint32_t vdst = kdst + K_CELLS * 16;
     const int key0 = kt * kBN;
     const uint16_t *kb = kh + key0 * D;
     const uint16_t *vb = vh + key0 * D;
-    const bool edge = key0 + kBN > limit;
-    const int last = limit - 1 - key0;
+    if (key0 + kBN <= limit) {
 #pragma unroll
-    for (int n = 0; n < K_SLOTS; ++n) {
-      const int j = wave + n * NW;
-      if (j < K_INSTR && dma_k_off[n] != ~0u)
-        lds_dma16_sv(kb, edge ? clamp_off(dma_k_off[n], last) : dma_k_off[n], kdst + j * 64);
-    }
+      for (int n = 0; n < K_SLOTS; ++n) {
+        const int j = wave + n * NW;
+        if ((n + 1) * NW <= K_INSTR || j < K_INSTR) lds_dma16_sv(kb, dma_k_off[n], kdst + j * 1024);
+      }
 #pragma unroll
-    for (int n = 0; n < V_SLOTS; ++n) {
-      const int j = wave + n * NW;
-      if (j < V_INSTR && dma_v_off[n] != ~0u)
-        lds_dma16_sv(vb, edge ? clamp_off(dma_v_off[n], last) : dma_v_off[n], vdst + j * 64);
+      for (int n = 0; n < V_SLOTS; ++n) {
+        const int j = wave + n * NW;
+        if ((n + 1) * NW <= V_INSTR || j < V_INSTR) lds_dma16_sv(vb, dma_v_off[n], vdst + j * 1024);
+      }
+    } else {
+      const int last = limit - 1 - key0;
+#pragma unroll
+      for (int n = 0; n < K_SLOTS; ++n) {
+        const int j = wave + n * NW;
+        if ((n + 1) * NW <= K_INSTR || j < K_INSTR) lds_dma16_sv(kb, clamp_off(dma_k_off[n], last), kdst + j * 1024);
+      }
+#pragma unroll
+      for (int n = 0; n < V_SLOTS; ++n) {
+        const int j = wave + n * NW;
+        if ((n + 1) * NW <= V_INSTR || j < V_INSTR) lds_dma16_sv(vb, clamp_off(dma_v_off[n], last), vdst + j * 1024);
+      }
     }
   };
   // Fewest LDS-DMA instructions any wavefront issues per tile.  Loads retire

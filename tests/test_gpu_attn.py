@@ -131,6 +131,43 @@ def test_ragged_segments_and_tails(D):
     np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_split_key_range_all_rows(D):
+    # Three chunk segments (500, 1000, 1000 rows), 40 query tiles whose 32..63
+    # key tiles are split between workgroups: every row is compared with the
+    # oracle.  The workspace starts as garbage (NaN bytes) and is then reused
+    # as is by a second split call of another shape.
+    B, H, L, Lq, q_pos0, kv_len, cap = 2, 2, 1000, 2500, 1500, 4000, 4096
+    q = rand_bf16((B, Lq, H, D), 51)
+    kc = rand_bf16((B, H, cap, D), 52)
+    vc = rand_bf16((B, H, cap, D), 53)
+    wsb = crattn.chunk_causal_attn_workspace_bytes(B, H, Lq, kv_len, q_pos0, L, D)
+    assert wsb > 0
+    ws = torch.full((wsb // 4 + 4,), float("nan"), dtype=torch.float32, device=dev())
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, Lq, dtype=torch.float32, device=dev())
+    crattn.chunk_causal_attn(q, kc, vc, kv_len, q_pos0, L, out, lse, ws)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_rows(q, kc, vc, kv_len, q_pos0, L)
+    assert_attn_close(f64(out), o_ref, f"split D{D}")
+    np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
+    plain, plain_lse = run_attn(q, kc, vc, kv_len, q_pos0, L, use_ws=False)
+    assert (out.float() - plain.float()).abs().max().item() <= 2e-3
+    # splits round p to bf16 relative to their own running maxima
+    assert (lse - plain_lse).abs().max().item() <= 1e-3
+    # second call, 3 heads x 2 tiles of 63 key tiles, same workspace untouched
+    B2, H2, Lq2, q_pos2 = 1, 3, 300, 3700
+    assert 0 < crattn.chunk_causal_attn_workspace_bytes(B2, H2, Lq2, kv_len, q_pos2, L, D) <= wsb
+    q2 = rand_bf16((B2, Lq2, H2, D), 54)
+    kc2 = kc[:1, :1].expand(B2, H2, cap, D).contiguous()
+    vc2 = vc[1:, 1:].expand(B2, H2, cap, D).contiguous()
+    out2 = torch.empty_like(q2)
+    crattn.chunk_causal_attn(q2, kc2, vc2, kv_len, q_pos2, L, out2, None, ws)
+    torch.cuda.synchronize()
+    o_ref2, _ = oracle_rows(q2, kc2, vc2, kv_len, q_pos2, L)
+    assert_attn_close(f64(out2), o_ref2, f"split reuse D{D}")
+
+
 @pytest.mark.parametrize("kind", ["peaked_q_x8", "key_ramp_1_to_4", "identical_keys",
                                   "tiny_scale"])
 def test_stress_distributions(kind):
@@ -226,7 +263,10 @@ def test_sp_slice_equals_rows_of_whole_chunk():
     # exactly like the same rows of the whole-chunk call.
     full, w = STEP480, SP480
     (q, k, v, _, _), (q_out, kcd, vcd) = _step(full)
-    outf, lsef = run_attn(q_out, kcd, vcd, full.kv_len, full.q_pos0, full.chunk_tokens)
+    # one workgroup per query tile (no workspace): rows are computed
+    # independently, in the same order, whatever the call's extent
+    outf, lsef = run_attn(q_out, kcd, vcd, full.kv_len, full.q_pos0, full.chunk_tokens,
+                          use_ws=False)
     sl = slice(w.tok_off, w.tok_off + w.lq)
     mt, mh, mw = w.table_extents()
     tab = table(w.D, mt, mh, mw)
@@ -242,6 +282,13 @@ def test_sp_slice_equals_rows_of_whole_chunk():
     d = (out.float() - outf[:, sl].float()).abs().max().item()
     print(f"  split-KV slice vs whole-chunk rows: max-abs {d:.2e}", flush=True)
     assert d <= 2e-3
+    # the whole chunk with the workspace (split if the planner splits it)
+    outs, lses = run_attn(q_out, kcd, vcd, full.kv_len, full.q_pos0, full.chunk_tokens)
+    d = (outs.float() - outf.float()).abs().max().item()
+    dl = (lses - lsef).abs().max().item()
+    print(f"  whole chunk with workspace vs without: max-abs {d:.2e}, lse {dl:.2e}",
+          flush=True)
+    assert d <= 2e-3 and dl <= 1e-3
 
 
 def test_win720_ring_window_sampled():
