@@ -175,8 +175,7 @@ size_t chunk_causal_attn_workspace_bytes(int B, int H, int64_t Lq, int64_t kv_le
  *
  * Arithmetic: q.k products in bf16 with fp32 accumulation, softmax in fp32
  * (base-2 exponent with log2(e) folded into the scale), probabilities
- * rounded to bf16 for the P.V product and for the row sums (the same weights
- * in numerator and denominator), fp32 accumulation, one final division.
+ * rounded to bf16 for the P.V product, fp32 accumulation, one final division.
  *
  * Errors: EINVAL for NULL q/k_cache/v_cache/out, misaligned pointers, B, H or
  * Lq < 1, kv_len < 1 or > cap, q_pos0 < 0, chunk_tokens < 1, an incomplete
