@@ -349,29 +349,64 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   const int v_row_in = vj >> 2;      // key row within the 4-row group
   const int v_dim = vblk * 16 + 4 * (vj & 3);
 
-  // ---- S^T = K Q^T of one tile from ring stage S ----
-  auto qk = [&](int stage, f32x16_t (&sc)[KB][QB]) {
+  // ---- operand fragments from a ring stage ----
+  // K (A operand of S^T = K Q^T) for QK MFMA i of a tile: k-step i / KB,
+  // 32-key block i % KB (consecutive MFMAs alternate accumulators).
+  auto k_frag = [&](int stage, int i) -> bf16x8_t {
     const uint4 *__restrict__ kt_lds = lds_ring + stage * STAGE_CELLS;
+    const int ks = i / KB, kb = i % KB;
+    return __builtin_bit_cast(bf16x8_t, kt_lds[(kb * 32 + kperm) * KP + 2 * ks + hf]);
+  };
+  // V^T (A operand of O^T += V^T P^T) for PV MFMA i of 32-key block kb:
+  // key half h2 = i / DB, dims db = i % DB; keys kb*32 + h2*16 + 8*hf + 0..7
+  // arrive as two transposed 4-key reads.
+  auto v_frag = [&](int stage, int kb, int i) -> bf16x8_t {
+    const char *__restrict__ vt_lds =
+        reinterpret_cast<const char *>(lds_ring + stage * STAGE_CELLS + K_CELLS);
+    const int h2 = i / DB, db = i % DB;
+    const int vr0 = kb * 32 + h2 * 16 + 8 * hf + v_row_in;
+    const int dbyte = (db * 32 + v_dim) * 2;  // byte offset of 4 dims within a row
+    const i16x4_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vt_lds + vr0 * (VP * 16) + dbyte));
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t *)(vt_lds + (vr0 + 4) * (VP * 16) + dbyte));
+    const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+  };
+  // ---- S^T = K Q^T of one whole tile (prologue) ----
+  auto qk = [&](int stage, f32x16_t (&sc)[KB][QB]) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int i = 0; i < KB * DK; ++i) {
+      const bf16x8_t kf = k_frag(stage, i);
+      const int ks = i / KB, kb = i % KB;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
+      for (int qb = 0; qb < QB; ++qb) {
+        if (ks == 0) {
+          f32x16_t z;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8_t kf =
-            __builtin_bit_cast(bf16x8_t, kt_lds[(kb * 32 + kperm) * KP + 2 * ks + hf]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], z, 0, 0, 0);
+        } else {
           sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sc[kb][qb], 0, 0, 0);
+        }
       }
     }
   };
-  // ---- softmax, part 1 (branchy): edge mask, running max, lazy rescale ----
-  auto softmax_prep = [&](f32x16_t (&sc)[KB][QB], int key0) {
+  // ---- softmax, part 1: row maximum of a tile (no mask) ----
+  auto row_max = [&](const f32x16_t (&sc)[KB][QB], float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[kb][qb][r]);
+      mx[qb] = half_swap_max(m);
+    }
+  };
+  // ---- softmax, part 2 (branchy, after the tile's products): edge mask,
+  // running max, lazy rescale of the row sums and of O ----
+  auto softmax_fix = [&](f32x16_t (&sc)[KB][QB], int key0, float (&mx)[QB]) {
     if (key0 + kBN > limit) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -382,15 +417,11 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
           for (int qb = 0; qb < QB; ++qb)
             if (dead) sc[kb][qb][r] = -INFINITY;
         }
+      row_max(sc, mx);
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][qb][r]);
-      const float m_cand = half_swap_max(mx) * a.scale_log2;
+      const float m_cand = mx[qb] * a.scale_log2;
       const bool need = m_cand > m_run[qb] + kRescaleLog2;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float m_new = need ? m_cand : m_run[qb];
@@ -404,65 +435,39 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       }
     }
   };
-  // ---- softmax, part 2 (branch-free): p = 2^(s*c - m), row sums, bf16 P ----
-  auto softmax_exp = [&](const f32x16_t (&sc)[KB][QB], bf16x8_t (&pf)[QB][KB][2]) {
+  // ---- softmax, part 3: p = 2^(s*c - m) for the two keys of packed pair j
+  // (0..15) of a tile, rounded to bf16 for the P.V product; the row sums add
+  // the fp32 p in two chains.
+  auto exp_pair = [&](const f32x16_t (&sc)[KB][QB], uint32_t (&pk)[QB][16],
+                      float (&rs)[QB][2], int j) {
+    const int kb = j >> 3, r = ((j >> 2) & 1) * 8 + 2 * (j & 3);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float m_use = m_run[qb];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          uint32_t pk[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p0 =
-                __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][h2 * 8 + 2 * e], a.scale_log2, -m_use));
-            const float p1 =
-                __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][h2 * 8 + 2 * e + 1], a.scale_log2, -m_use));
-            rs += p0 + p1;
-            pk[e] = pack_bf16(p0, p1);
-          }
-          pf[qb][kb][h2] = __builtin_bit_cast(bf16x8_t, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-        }
-      }
-      l_run[qb] += rs;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][r], a.scale_log2, -m_run[qb]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kb][qb][r + 1], a.scale_log2, -m_run[qb]));
+      pk[qb][j] = pack_bf16(p0, p1);
+      rs[qb][j & 1] += p0 + p1;
     }
   };
-  // ---- O^T += V^T P^T of one tile from ring stage S ----
-  auto pv = [&](int stage, const bf16x8_t (&pf)[QB][KB][2]) {
-    const char *__restrict__ vt_lds =
-        reinterpret_cast<const char *>(lds_ring + stage * STAGE_CELLS + K_CELLS);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        // keys kb*32 + h2*16 + 8*hf + (0..7): two transposed 4-key reads
-        const int vr0 = kb * 32 + h2 * 16 + 8 * hf + v_row_in;
-        const int vr1 = vr0 + 4;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dbyte = (db * 32 + v_dim) * 2;  // byte offset of 4 dims within a row
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(vt_lds + vr0 * (VP * 16) + dbyte));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4_t *)(vt_lds + vr1 * (VP * 16) + dbyte));
-          const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][h2], o[db][qb], 0, 0, 0);
-        }
-      }
-    }
+  // P^T B operand of 16 keys (chunk c = 2 * kb + h2) from the packed pairs
+  auto p_frag = [&](const uint32_t (&pk)[QB][16], int qb, int c) -> bf16x8_t {
+    return __builtin_bit_cast(bf16x8_t,
+                              make_uint4(pk[qb][4 * c], pk[qb][4 * c + 1], pk[qb][4 * c + 2],
+                                         pk[qb][4 * c + 3]));
   };
 
   // ---- the key loop, software-pipelined across tiles ----
   // Step for tile kt: wait for tile kt+1's copy, barrier, issue the copy of
-  // tile kt+3, then compute S(kt+1) = K(kt+1) Q^T on the matrix cores while
-  // the vector ALUs turn S(kt) into probabilities, and finish with
-  // O += P(kt) V(kt).  The two S buffers alternate (loop unrolled by 2).
+  // tile kt+3, then three MFMA streams, each interleaved one MFMA at a time
+  // with a share of the vector work:
+  //   S(kt+1) = K Q^T        (16 MFMAs) with p of S(kt), pairs 0..11
+  //   O += P V, keys 0..31   ( 8 MFMAs) with p of S(kt), pairs 12..15
+  //   O += P V, keys 32..63  ( 8 MFMAs) with the row maximum of S(kt+1)
+  // and finally, outside the MFMA streams, the edge mask and the (rare)
+  // rescale for tile kt+1.  Operand fragments are read from LDS two MFMAs
+  // ahead.  A scheduling barrier after each slot keeps MFMAs and vector
+  // instructions in this order while letting LDS reads and scalar work move.
+  constexpr int kSlotMask = 0x0100 | 0x0004;  // DS reads, SALU may cross
   f32x16_t sbuf[2][KB][QB];
   if (kt_begin < kt_end) dma(kt_begin, 0);
   if (kt_begin + 1 < kt_end) dma(kt_begin + 1, 1);
@@ -474,11 +479,21 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   else
     wait_vmcnt<0>();
   __syncthreads();
-  if (active && kt_begin < kt_end) qk(0, sbuf[0]);
+  if (active && kt_begin < kt_end) {
+    qk(0, sbuf[0]);
+    float mx[QB];
+    row_max(sbuf[0], mx);
+    softmax_fix(sbuf[0], kt_begin * kBN, mx);
+  }
 
   auto step = [&](int kt, auto P) {
     constexpr int par = decltype(P)::value;
+    constexpr int NQK = KB * DK;  // 16 (D = 128) or 8 (D = 64)
+    constexpr int NPV = 2 * DB;   // per 32-key block: 8 or 4
+    constexpr int NPAIR = 16;     // packed p pairs per tile
+    constexpr int NA = NPAIR * 3 / 4;  // pairs done during S(kt+1)
     const int stage = (kt - kt_begin) & (NS - 1);
+    const int st1 = (stage + 1) & (NS - 1);
     const bool more = kt + 1 < kt_end;
     if (more) {
       // tile kt+1 has landed once at most tile kt+2's copies are pending
@@ -494,21 +509,79 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     if (!active) return;
     f32x16_t (&cur)[KB][QB] = sbuf[par];
     f32x16_t (&nxt)[KB][QB] = sbuf[par ^ 1];
-    softmax_prep(cur, kt * kBN);
-    bf16x8_t pf[QB][KB][2];
-    // S of the next tile, unconditionally so that it shares a basic block
-    // with the softmax it overlaps.  On the last tile it reads a stage no
-    // copy is writing (stale, in bounds) and the result is never used.
-    qk((stage + 1) & (NS - 1), nxt);
-    softmax_exp(cur, pf);
-    // interleave: each S MFMA with a share of the softmax
+    uint32_t pk[QB][16];
+    float rs[QB][2];
 #pragma unroll
-    for (int i = 0; i < KB * DK * QB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+    for (int qb = 0; qb < QB; ++qb) rs[qb][0] = rs[qb][1] = 0.f;
+
+    // S(kt+1), unconditionally so that the stream keeps its shape; on the
+    // last tile it reads a stage no copy is writing (stale, in bounds) and
+    // the result is never used.
+    bf16x8_t kf[NQK];
+    kf[0] = k_frag(st1, 0);
+    kf[1] = k_frag(st1, 1);
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      if (i + 2 < NQK) kf[i + 2] = k_frag(st1, i + 2);
+      const int ks = i / KB, kb = i % KB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        if (ks == 0) {
+          f32x16_t z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          nxt[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[qb][ks], z, 0, 0, 0);
+        } else {
+          nxt[kb][qb] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[qb][ks], nxt[kb][qb], 0, 0, 0);
+        }
+      }
+      // NA pairs spread over NQK slots
+      if (i * NA / NQK != (i + 1) * NA / NQK) exp_pair(cur, pk, rs, i * NA / NQK);
+      if ((i + 1) * NA / NQK - i * NA / NQK == 2) exp_pair(cur, pk, rs, i * NA / NQK + 1);
+      __builtin_amdgcn_sched_barrier(kSlotMask);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    pv(stage, pf);
+
+    // O += P V for keys 0..31 with the last quarter of p, then for keys
+    // 32..63 with the row maximum of S(kt+1)
+    float mp[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mp[qb] = -INFINITY;
+    bf16x8_t vf[2 * NPV];
+    vf[0] = v_frag(stage, 0, 0);
+    vf[1] = v_frag(stage, 0, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * NPV; ++i) {
+      if (i + 2 < 2 * NPV) vf[i + 2] = v_frag(stage, (i + 2) / NPV, (i + 2) % NPV);
+      const int kb = i / NPV, h2 = (i % NPV) / DB, db = i % DB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], p_frag(pk, qb, 2 * kb + h2),
+                                                            o[db][qb], 0, 0, 0);
+      if (kb == 0) {
+        // pairs NA..15 over the first block's slots
+        const int j0 = NA + i * (NPAIR - NA) / NPV, j1 = NA + (i + 1) * (NPAIR - NA) / NPV;
+#pragma unroll
+        for (int j = j0; j < j1; ++j) exp_pair(cur, pk, rs, j);
+      } else {
+        // a share of the scores of S(kt+1) into the running row maximum
+        constexpr int per = KB * 16 / NPV;
+#pragma unroll
+        for (int v = 0; v < per; ++v) {
+          const int idx = (i - NPV) * per + v;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) mp[qb] = fmaxf(mp[qb], nxt[idx / 16][qb][idx % 16]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(kSlotMask);
+    }
+    float mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      mx[qb] = half_swap_max(mp[qb]);
+      l_run[qb] += rs[qb][0] + rs[qb][1];
+    }
+    if (more) softmax_fix(nxt, (kt + 1) * kBN, mx);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
