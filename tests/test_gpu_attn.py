@@ -133,11 +133,11 @@ def test_ragged_segments_and_tails(D):
 
 @pytest.mark.parametrize("D", [64, 128])
 def test_split_key_range_all_rows(D):
-    # Three chunk segments (500, 1000, 1000 rows), 40 query tiles whose 32..63
-    # key tiles are split between workgroups: every row is compared with the
-    # oracle.  The workspace starts as garbage (NaN bytes) and is then reused
-    # as is by a second split call of another shape.
-    B, H, L, Lq, q_pos0, kv_len, cap = 2, 2, 1000, 2500, 1500, 4000, 4096
+    # Two chunk segments (2000 and 500 rows), 40 query tiles of 188 or 250 key
+    # tiles whose key ranges are split between workgroups: every row is
+    # compared with the oracle.  The workspace starts as garbage (NaN bytes)
+    # and is then reused as is by a second call of another shape.
+    B, H, L, Lq, q_pos0, kv_len, cap = 2, 2, 4000, 2500, 10000, 16000, 16384
     q = rand_bf16((B, Lq, H, D), 51)
     kc = rand_bf16((B, H, cap, D), 52)
     vc = rand_bf16((B, H, cap, D), 53)
@@ -153,14 +153,13 @@ def test_split_key_range_all_rows(D):
     np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
     plain, plain_lse = run_attn(q, kc, vc, kv_len, q_pos0, L, use_ws=False)
     assert (out.float() - plain.float()).abs().max().item() <= 2e-3
-    # splits round p to bf16 relative to their own running maxima
     assert (lse - plain_lse).abs().max().item() <= 1e-3
-    # second call, 3 heads x 2 tiles of 63 key tiles, same workspace untouched
-    B2, H2, Lq2, q_pos2 = 1, 3, 300, 3700
+    # second call: 2 x 8 heads x 2 tiles of 250 key tiles, same workspace
+    B2, H2, Lq2, q_pos2 = 2, 8, 300, 15700
     assert 0 < crattn.chunk_causal_attn_workspace_bytes(B2, H2, Lq2, kv_len, q_pos2, L, D) <= wsb
     q2 = rand_bf16((B2, Lq2, H2, D), 54)
-    kc2 = kc[:1, :1].expand(B2, H2, cap, D).contiguous()
-    vc2 = vc[1:, 1:].expand(B2, H2, cap, D).contiguous()
+    kc2 = kc[:, :1].expand(B2, H2, cap, D).contiguous()
+    vc2 = vc[:, 1:].expand(B2, H2, cap, D).contiguous()
     out2 = torch.empty_like(q2)
     crattn.chunk_causal_attn(q2, kc2, vc2, kv_len, q_pos2, L, out2, None, ws)
     torch.cuda.synchronize()
