@@ -20,6 +20,12 @@ What is computed, and where it comes from (pages cited by title/section):
 * chunk-causal attention: bidirectional inside a chunk, causal across
   chunks -- "Wave Forcing" abstract (chunk-based causal attention over
   earlier chunks).
+* the QKV projection with Causal-RoPE fused into it -- same page as the
+  rotary code, §2.C (RoPE fused into the QKV projection).  The projection is
+  the plain linear map y = x W^T (W stored [3*H*D, C], the usual linear-layer
+  layout), columns ordered Q, K, V with heads contiguous; no bias.  The
+  matrix product is numpy's (a library primitive); the rotation is the C
+  oracle's.
 * the log-sum-exp merge of two key subsets -- the exact identity
   attn(A u B) = merge(attn(A), attn(B)); it has no page of its own and is
   pinned by the tests against the oracle's own whole-set attention.
@@ -218,6 +224,33 @@ def append(cache, x, cache_pos):
 
 def attn(q, k, v, kv_len, q_pos0, chunk_tokens, scale=None, rows=None, threads=None):
     return _get().attn(q, k, v, kv_len, q_pos0, chunk_tokens, scale, rows, threads)
+
+
+def qkv_project(x, w, H, D):
+    """y = x W^T split into Q, K, V of shape [B, n, H, D] (fp64).
+
+    x: [B, n, C]; w: [3*H*D, C].  Columns [0, HD) are Q, [HD, 2HD) K and
+    [2HD, 3HD) V; inside each, head h owns columns [h*D, (h+1)*D)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, n, C = x.shape
+    assert w.shape == (3 * H * D, C)
+    y = np.matmul(x.reshape(B * n, C), w.T).reshape(B, n, 3, H, D)
+    return y[:, :, 0], y[:, :, 1], y[:, :, 2]
+
+
+def qkv_rope(x, w, H, D, t0, tok_off, grid_h, grid_w, theta=10000.0):
+    """The fused projection's outputs: rotated Q', rotated K' and V, each
+    [B, n, H, D] fp64 (the caller rounds to the storage dtype and appends
+    K', V to the cache)."""
+    q, k, v = qkv_project(x, w, H, D)
+    return (rope(np.ascontiguousarray(q), t0, tok_off, grid_h, grid_w, theta),
+            rope(np.ascontiguousarray(k), t0, tok_off, grid_h, grid_w, theta), v)
+
+
+def qkv_abs(x, w, H, D):
+    """sum_c |x_c| |w_c| for every output of the projection (error bounds)."""
+    return qkv_project(np.abs(x), np.abs(w), H, D)
 
 
 def lse_merge(o_a, lse_a, o_b, lse_b):
