@@ -13,6 +13,8 @@ Entry points (see include/crattn.h for the full contracts):
   rotary code, built once on the device.
 * ``rope_apply_append`` -- rotate Q and K from a global time index, write Q',
   append K' and V to the KV cache, in one pass.
+* ``qkv_rope_append`` -- the QKV projection of the chunk's hidden states with
+  the same rotation and append fused into its epilogue.
 * ``chunk_causal_attn_workspace_bytes`` / ``chunk_causal_attn`` -- flash
   attention of a chunk's queries against the cache, bidirectional inside a
   chunk and causal across chunks.
@@ -26,8 +28,8 @@ import torch
 
 __all__ = [
     "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
-    "rope_apply_append", "chunk_causal_attn_workspace_bytes", "chunk_causal_attn",
-    "crattn_last_error", "EXPORTS",
+    "rope_apply_append", "qkv_rope_append", "chunk_causal_attn_workspace_bytes",
+    "chunk_causal_attn", "crattn_last_error", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +39,7 @@ CRATTN_OK, CRATTN_EINVAL, CRATTN_ENOTSUP, CRATTN_EHIP = 0, 1, 2, 3
 CRATTN_F32, CRATTN_BF16 = 0, 1
 
 # Every symbol include/crattn.h declares.
-EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append",
+EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append", "qkv_rope_append",
            "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "crattn_last_error")
 
 _lib = None
@@ -69,6 +71,9 @@ def load():
                                       _i32, _i32, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _i32,
                                       _vp]
     lib.rope_apply_append.restype = _i32
+    lib.qkv_rope_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32,
+                                    _i32, _i32, _i32, _i32, _i64, _i64, _i64, _i32, _i32, _vp]
+    lib.qkv_rope_append.restype = _i32
     lib.chunk_causal_attn_workspace_bytes.argtypes = [_i32, _i32, _i64, _i64, _i64, _i64, _i32]
     lib.chunk_causal_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.chunk_causal_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
@@ -147,6 +152,30 @@ def rope_apply_append(q: torch.Tensor | None, q_out: torch.Tensor | None, k: tor
                                     _ptr(v_cache), cap, cache_pos, _ptr(table), max_t, max_h,
                                     max_w, B, H, D, n, t0, tok_off, grid_h, grid_w,
                                     _dtype_code(k), _stream(stream)))
+
+
+def qkv_rope_append(x: torch.Tensor, w: torch.Tensor, q_out: torch.Tensor | None,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, cache_pos: int,
+                    table: torch.Tensor, max_t: int, max_h: int, max_w: int, t0: int,
+                    tok_off: int, grid_h: int, grid_w: int, stream=None) -> None:
+    """x: [B, n, C] bf16; w: [3*H*D, C] bf16; q_out: [B, n, H, D] bf16 or None;
+    caches [B, H, cap, D] bf16."""
+    B, n, C = x.shape
+    _, H, cap, D = k_cache.shape
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("x and w must be bfloat16")
+    if tuple(w.shape) != (3 * H * D, C):
+        raise ValueError("w must be [3*H*D, C] for the caches' H and D")
+    if q_out is not None and (tuple(q_out.shape) != (B, n, H, D) or q_out.dtype != x.dtype):
+        raise ValueError("q_out must be [B, n, H, D] bfloat16")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != x.dtype:
+            raise ValueError("caches must be [B, H, cap, D] bfloat16")
+    if table.dtype != torch.float32:
+        raise ValueError("table must be float32")
+    _raise(load().qkv_rope_append(_ptr(x), _ptr(w), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+                                  cap, cache_pos, _ptr(table), max_t, max_h, max_w, B, H, D, C,
+                                  n, t0, tok_off, grid_h, grid_w, _stream(stream)))
 
 
 def chunk_causal_attn_workspace_bytes(B: int, H: int, Lq: int, kv_len: int, q_pos0: int,

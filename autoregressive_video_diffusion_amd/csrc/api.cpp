@@ -151,6 +151,71 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v, 
                     "rope_apply_append launch");
 }
 
+int qkv_rope_append(const void *x, const void *w, void *q_out, void *k_cache, void *v_cache,
+                    int64_t cap, int64_t cache_pos, const float *table, int max_t, int max_h,
+                    int max_w, int B, int H, int D, int C, int64_t n, int64_t t0, int64_t tok_off,
+                    int grid_h, int grid_w, void *stream) {
+  if (x == nullptr || w == nullptr || k_cache == nullptr || v_cache == nullptr ||
+      table == nullptr)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: x, w, k_cache, v_cache and table are required");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q_out) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(table))
+    return fail(CRATTN_EINVAL, "qkv_rope_append: pointers must be 16-byte aligned");
+  if (B < 1 || H < 1 || n < 1 || C < 1)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: B=%d H=%d n=%lld C=%d must be >= 1", B, H,
+                (long long)n, C);
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "qkv_rope_append: head_dim %d not supported (64 or 128)", D);
+  if (C % 32 != 0 || C > 65536)
+    return fail(CRATTN_ENOTSUP, "qkv_rope_append: C=%d must be a multiple of 32, at most 65536",
+                C);
+  if (cap < 1 || cache_pos < 0 || cache_pos > cap || n > cap - cache_pos)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: rows [%lld, %lld) outside the cache (cap %lld)",
+                (long long)cache_pos, (long long)(cache_pos + n), (long long)cap);
+  if (t0 < 0 || tok_off < 0 || grid_h < 1 || grid_w < 1)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: t0, tok_off >= 0 and grid >= 1 required");
+  if (max_t < 1 || max_h < 1 || max_w < 1 || max_t > kMaxExtent || max_h > kMaxExtent ||
+      max_w > kMaxExtent)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: table extents outside [1, %d]", kMaxExtent);
+  if (grid_h > max_h || grid_w > max_w)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: grid %dx%d exceeds the table (%dx%d)", grid_h,
+                grid_w, max_h, max_w);
+  if (tok_off > kMaxElems || n > kMaxElems)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: token range too large");
+  const int64_t last_t = t0 + (tok_off + n - 1) / ((int64_t)grid_h * grid_w);
+  if (last_t >= max_t)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: time index %lld outside the table (max_t %d)",
+                (long long)last_t, max_t);
+  if (tok_off + n > (int64_t(1) << 31) || (double)B * (double)n >= 2147483648.0 ||
+      3.0 * H * D >= 2147483648.0)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: B*n, tok_off + n or 3*H*D exceeds 2^31");
+  if ((double)B * H * (double)cap * D > (double)kMaxElems)
+    return fail(CRATTN_EINVAL, "qkv_rope_append: cache element count exceeds 2^40");
+  crattn::QkvArgs a;
+  a.x = x;
+  a.w = w;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cap = cap;
+  a.cache_pos = cache_pos;
+  a.table = table;
+  a.max_t = max_t;
+  a.max_h = max_h;
+  a.max_w = max_w;
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.C = C;
+  a.n = n;
+  a.t0 = t0;
+  a.tok_off = tok_off;
+  a.grid_h = grid_h;
+  a.grid_w = grid_w;
+  return hip_status(crattn::launch_qkv_rope(a, static_cast<hipStream_t>(stream)),
+                    "qkv_rope_append launch");
+}
+
 static int attn_shape_check(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
                             int64_t chunk_tokens, int D, int64_t cap, const char *who) {
   if (B < 1 || H < 1 || Lq < 1)

@@ -41,6 +41,21 @@ struct RopeAppendArgs {
   int dtype;  // CRATTN_F32 / CRATTN_BF16
 };
 
+struct QkvArgs {
+  const void *x;      // [B][n][C] bf16
+  const void *w;      // [3*H*D][C] bf16
+  void *q_out;        // [B][n][H][D] bf16 or null
+  void *k_cache;      // [B][H][cap][D] bf16
+  void *v_cache;
+  int64_t cap, cache_pos;
+  const float *table;
+  int max_t, max_h, max_w;
+  int B, H, D, C;
+  int64_t n;
+  int64_t t0, tok_off;
+  int grid_h, grid_w;
+};
+
 struct AttnArgs {
   const void *q;
   const void *k;
@@ -79,5 +94,6 @@ AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
 hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t s);
 hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
+hipError_t launch_qkv_rope(const QkvArgs &a, hipStream_t s);
 
 }  // namespace crattn

@@ -14,6 +14,7 @@
 // with every wavefront covering whole 256-byte rows, and streaming stores.
 // The table (tens of KB) stays in L1/L2.
 #include "crattn_internal.h"
+#include "rope_common.h"
 #include "../../include/crattn.h"
 
 namespace crattn {
@@ -60,37 +61,6 @@ __device__ inline void ntstore(const uint4 &x, void *p) {
   const u32x4_t v = {x.x, x.y, x.z, x.w};
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t *>(p));
 }
-struct Pos {
-  uint32_t t, h, w;
-};
-
-// Token g of the chunk (raster order) -> (t0 + frame, row, column).
-__device__ inline Pos decode_pos(uint32_t g, uint32_t per_frame, uint32_t gw, uint32_t t0) {
-  const uint32_t f = g / per_frame;
-  const uint32_t in_frame = g - f * per_frame;
-  const uint32_t r = in_frame / gw;
-  return Pos{t0 + f, r, in_frame - r * gw};
-}
-
-struct TabGeom {
-  uint32_t ht, hh;      // pairs in the t group and in the h (= w) group
-  uint32_t base_h;      // first entry of axis h  = max_t * ht
-  uint32_t base_w;      // first entry of axis w  = base_h + max_h * hh
-};
-
-// (cos, sin) of feature pair `pair` of head_dim at position p.
-__device__ inline float2 pair_cs(const float2 *__restrict__ tab, const TabGeom &g,
-                                 uint32_t pair, const Pos &p) {
-  uint32_t idx;
-  if (pair < g.ht)
-    idx = p.t * g.ht + pair;
-  else if (pair < g.ht + g.hh)
-    idx = g.base_h + p.h * g.hh + (pair - g.ht);
-  else
-    idx = g.base_w + p.w * g.hh + (pair - g.ht - g.hh);
-  return tab[idx];
-}
-
 __device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ inline uint32_t pack_bf16(float lo, float hi) {

@@ -137,6 +137,36 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v,
                       int grid_h, int grid_w, int dtype, void *stream);
 
 /*
+ * The QKV projection of the chunk with the rotary code and the cache append
+ * fused into its epilogue [CRSP §2.C; §2.B; §1]: y = x W^T, then Q' = rot(Q),
+ * K' = rot(K) appended with V to the cache, exactly as rope_apply_append does
+ * with the projected Q, K, V (rotated in fp32 from the fp32 accumulators,
+ * before any bf16 rounding).
+ *
+ *   x         device bf16 [B][n][C]: the chunk's hidden states.
+ *   w         device bf16 [3*H*D][C] (linear-layer layout, out x in): rows
+ *             [0, HD) project Q, [HD, 2HD) K, [2HD, 3HD) V, head h owning
+ *             rows [h*D, (h+1)*D) of each part.  No bias.
+ *   q_out     device bf16 [B][n][H][D] or NULL (a cache-update call: the Q
+ *             rows of w are not computed).
+ *   k_cache, v_cache, cap, cache_pos, table, max_t, max_h, max_w, n, t0,
+ *   tok_off, grid_h, grid_w   as for rope_apply_append.
+ *   C         hidden size: a multiple of 32, at most 65536.
+ *
+ * Arithmetic: bf16 products with fp32 accumulation (matrix cores), rotation in
+ * fp32 with the table's fp32 cos/sin, round-to-nearest-even bf16 stores.
+ *
+ * Errors: EINVAL for NULL x/w/caches/table, a misaligned pointer, B, H, n or
+ * C < 1, the cache-range and position errors of rope_apply_append, B*n or
+ * 3*H*D >= 2^31, or a cache over 2^40 elements; ENOTSUP for D other than 64
+ * or 128, or C not a multiple of 32 or above 65536; EHIP.
+ */
+int qkv_rope_append(const void *x, const void *w, void *q_out, void *k_cache, void *v_cache,
+                    int64_t cap, int64_t cache_pos, const float *table, int max_t, int max_h,
+                    int max_w, int B, int H, int D, int C, int64_t n, int64_t t0,
+                    int64_t tok_off, int grid_h, int grid_w, void *stream);
+
+/*
  * Workspace bytes chunk_causal_attn needs to split the key range of a call
  * of this shape across workgroups (0 when it does not split).  Depends on the
  * shape only.  Pure host function; returns 0 for invalid shapes.

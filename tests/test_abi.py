@@ -81,6 +81,27 @@ def test_rope_apply_append_rejects(kw, code):
     assert crattn.crattn_last_error() != ""
 
 
+def _qkv(**kw):
+    a = dict(x=FAKE, w=FAKE, q_out=FAKE, kc=FAKE, vc=FAKE, cap=100, pos=0, table=FAKE, mt=4,
+             mh=8, mw=8, B=1, H=2, D=64, C=128, n=64, t0=3, off=0, gh=8, gw=8)
+    a.update(kw)
+    return _lib().qkv_rope_append(a["x"], a["w"], a["q_out"], a["kc"], a["vc"], a["cap"],
+                                  a["pos"], a["table"], a["mt"], a["mh"], a["mw"], a["B"],
+                                  a["H"], a["D"], a["C"], a["n"], a["t0"], a["off"], a["gh"],
+                                  a["gw"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(kc=None), 1), (dict(table=None), 1),
+    (dict(w=MIS), 1), (dict(q_out=MIS), 1), (dict(D=96), 2), (dict(C=100), 2), (dict(C=0), 1),
+    (dict(C=65568), 2), (dict(n=0), 1), (dict(B=0), 1), (dict(pos=40, n=64, cap=100), 1),
+    (dict(t0=4), 1), (dict(gh=9), 1), (dict(off=1), 1), (dict(t0=-1), 1),
+])
+def test_qkv_rope_append_rejects(kw, code):
+    assert _qkv(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, kv=256, pos0=192, L=64, out=FAKE, lse=None,
              ws=None, wsb=0, B=1, H=2, D=64, Lq=64, scale=0.0)
