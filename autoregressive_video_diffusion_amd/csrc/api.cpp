@@ -166,8 +166,8 @@ int qkv_rope_append(const void *x, const void *w, void *q_out, void *k_cache, vo
                 (long long)n, C);
   if (D != 64 && D != 128)
     return fail(CRATTN_ENOTSUP, "qkv_rope_append: head_dim %d not supported (64 or 128)", D);
-  if (C % 32 != 0 || C > 65536)
-    return fail(CRATTN_ENOTSUP, "qkv_rope_append: C=%d must be a multiple of 32, at most 65536",
+  if (C % 64 != 0 || C > 65536)
+    return fail(CRATTN_ENOTSUP, "qkv_rope_append: C=%d must be a multiple of 64, at most 65536",
                 C);
   if (cap < 1 || cache_pos < 0 || cache_pos > cap || n > cap - cache_pos)
     return fail(CRATTN_EINVAL, "qkv_rope_append: rows [%lld, %lld) outside the cache (cap %lld)",

@@ -151,7 +151,7 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v,
  *             rows of w are not computed).
  *   k_cache, v_cache, cap, cache_pos, table, max_t, max_h, max_w, n, t0,
  *   tok_off, grid_h, grid_w   as for rope_apply_append.
- *   C         hidden size: a multiple of 32, at most 65536.
+ *   C         hidden size: a multiple of 64, at most 65536.
  *
  * Arithmetic: bf16 products with fp32 accumulation (matrix cores), rotation in
  * fp32 with the table's fp32 cos/sin, round-to-nearest-even bf16 stores.
@@ -159,7 +159,7 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v,
  * Errors: EINVAL for NULL x/w/caches/table, a misaligned pointer, B, H, n or
  * C < 1, the cache-range and position errors of rope_apply_append, B*n or
  * 3*H*D >= 2^31, or a cache over 2^40 elements; ENOTSUP for D other than 64
- * or 128, or C not a multiple of 32 or above 65536; EHIP.
+ * or 128, or C not a multiple of 64 or above 65536; EHIP.
  */
 int qkv_rope_append(const void *x, const void *w, void *q_out, void *k_cache, void *v_cache,
                     int64_t cap, int64_t cache_pos, const float *table, int max_t, int max_h,

@@ -93,7 +93,7 @@ def _qkv(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(x=None), 1), (dict(w=None), 1), (dict(kc=None), 1), (dict(table=None), 1),
-    (dict(w=MIS), 1), (dict(q_out=MIS), 1), (dict(D=96), 2), (dict(C=100), 2), (dict(C=0), 1),
+    (dict(w=MIS), 1), (dict(q_out=MIS), 1), (dict(D=96), 2), (dict(C=100), 2), (dict(C=96), 2), (dict(C=0), 1),
     (dict(C=65568), 2), (dict(n=0), 1), (dict(B=0), 1), (dict(pos=40, n=64, cap=100), 1),
     (dict(t0=4), 1), (dict(gh=9), 1), (dict(off=1), 1), (dict(t0=-1), 1),
 ])

@@ -68,8 +68,8 @@ def _expected(x, w, H, D, t0, tok_off, gh, gw):
 
 @pytest.mark.parametrize("B,n,C,H,D,gh,gw,t0,cap,pos", [
     (1, 64, 128, 2, 64, 8, 8, 3, 256, 192),     # one 8x8 frame, one token tile
-    (2, 200, 96, 2, 64, 10, 20, 5, 260, 40),    # ragged tokens, 3 C steps, 384 features
-    (1, 330, 160, 3, 128, 11, 15, 2, 400, 64),  # 1152 features (4.5 tiles), 2 frames
+    (2, 200, 192, 2, 64, 10, 20, 5, 260, 40),   # ragged tokens, 3 C stages, 384 features
+    (1, 330, 320, 3, 128, 11, 15, 2, 400, 64),  # 1152 features (4.5 tiles), 2 frames
 ])
 def test_small_shapes_every_element(B, n, C, H, D, gh, gw, t0, cap, pos):
     x, w = _inputs(B, n, C, H, D, 300 + n)
@@ -117,4 +117,21 @@ def test_480p_chunk_projection():
     _check(f64(q), qe, aq, q0, C, True, "480P Q'")
     _check(f64(kc[:, :, pos:]).transpose(0, 2, 1, 3), ke, ak, k0, C, True, "480P K'")
     _check(f64(vc[:, :, pos:]).transpose(0, 2, 1, 3), ve, av, ve, C, False, "480P V")
+    assert bool((kc[:, :, :pos] == 7.0).all()) and bool((vc[:, :, :pos] == -7.0).all())
+
+
+@pytest.mark.parametrize("B,n,C", [
+    (2, 3584, 256),   # 7168 tokens: 504 tiles of 256 x 256 fill two rounds of 256 CUs
+    (1, 1000, 64),    # ragged token tail, one C stage
+])
+def test_large_token_counts_every_element(B, n, C):
+    # shapes whose tile choice differs from the 480P chunk's; every element
+    H, D, gh, gw, t0 = 12, 128, 28, 32, 1
+    cap, pos = n + 64, 64
+    x, w = _inputs(B, n, C, H, D, 5000 + n)
+    q, kc, vc = _run(x, w, H, D, cap, pos, t0, 0, gh, gw)
+    (qe, ke, ve), (q0, k0), (aq, ak, av) = _expected(x, w, H, D, t0, 0, gh, gw)
+    _check(f64(q), qe, aq, q0, C, True, "Q'")
+    _check(f64(kc[:, :, pos:]).transpose(0, 2, 1, 3), ke, ak, k0, C, True, "K'")
+    _check(f64(vc[:, :, pos:]).transpose(0, 2, 1, 3), ve, av, ve, C, False, "V")
     assert bool((kc[:, :, :pos] == 7.0).all()) and bool((vc[:, :, :pos] == -7.0).all())
