@@ -47,6 +47,18 @@ def rope_bytes(B, n, H, D, elt=2, with_q=True):
 
 
 ROPE_SRC = os.path.join(ROOT, "autoregressive_video_diffusion_amd", "csrc", "rope.hip")
+QKV_SRC = os.path.join(ROOT, "autoregressive_video_diffusion_amd", "csrc", "qkv.hip")
+
+
+def qkv_flops(B, n, C, H, D):
+    """2*B*n*C*3HD: the projection's multiply-adds (the rotation is not counted)."""
+    return 2 * B * n * C * 3 * H * D
+
+
+def qkv_bytes(B, n, C, H, D, elt=2):
+    """Algorithmic HBM bytes of one fused projection call: read x and W, write
+    Q', K', V (the cos/sin table, a few hundred KB, is not counted)."""
+    return (B * n * C + 3 * H * D * C + 3 * B * n * H * D) * elt
 
 
 def source_digest(path=ATTN_SRC) -> str:
@@ -54,9 +66,9 @@ def source_digest(path=ATTN_SRC) -> str:
 
 
 def read_traffic(kernel="attn"):
-    """HBM bytes per launch of the attention ("attn") or RoPE/append ("rope")
-    kernel from the committed counter summary, if it was taken on the current
-    kernel source; else None."""
+    """HBM bytes per launch of the attention ("attn"), RoPE/append ("rope") or
+    fused projection ("qkv") kernel from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
     if not os.path.exists(COUNTERS):
         return None
     kv = {}
@@ -64,8 +76,9 @@ def read_traffic(kernel="attn"):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    src, key = ((ATTN_SRC, "traffic_bytes_per_launch") if kernel == "attn" else
-                (ROPE_SRC, "rope_traffic_bytes_per_launch"))
+    src, key = {"attn": (ATTN_SRC, "traffic_bytes_per_launch"),
+                "rope": (ROPE_SRC, "rope_traffic_bytes_per_launch"),
+                "qkv": (QKV_SRC, "qkv_traffic_bytes_per_launch")}[kernel]
     if kv.get(f"{kernel}_source_sha256_16") != source_digest(src):
         return None
     try:
@@ -132,6 +145,37 @@ def time_attn_only(crattn, w, dev, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
+def time_qkv(crattn, w, dev, table, ext, burst=40):
+    """Fused QKV projection + RoPE + append of the chunk (hidden size H*D):
+    average per-launch time (ms) of a burst of back-to-back launches over
+    four hidden-state sets, between two events on the stream."""
+    import torch
+
+    from workloads import projection_inputs
+
+    sets = [projection_inputs(w, i) for i in range(4)]
+    xs = [x.to(dev) for x, _ in sets]
+    wt = sets[0][1].to(dev)
+    q_out = torch.empty(w.B, w.lq, w.H, w.D, dtype=torch.bfloat16, device=dev)
+    kc = torch.empty(w.B, w.H, w.cap, w.D, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+
+    def call(i):
+        crattn.qkv_rope_append(xs[i % 4], wt, q_out, kc, vc, w.cache_pos, table, *ext, w.t0,
+                               w.tok_off, w.grid_h, w.grid_w)
+
+    for i in range(burst):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(burst):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / burst
+
+
 def rollout_ms(crattn, dev, reps=2):
     """Whole 480P rollout: 7 chunks x (4 denoising calls + 1 cache update)."""
     import torch
@@ -180,11 +224,18 @@ def cpu_baseline(w, stride=1):
     oracle.attn(q, k, v, w.kv_len, w.q_pos0, w.chunk_tokens, rows=rows, threads=threads)
     dt = time.perf_counter() - t
     fl = attn_flops(w.B, w.H, len(rows), w.kv_len, w.D)
+    # one RoPE pass of the chunk's Q and K (fp64), for the append row
+    x = rng.standard_normal((w.B, w.lq, w.H, w.D))
+    t = time.perf_counter()
+    oracle.rope(x, w.t0, w.tok_off, w.grid_h, w.grid_w)
+    oracle.rope(x, w.t0, w.tok_off, w.grid_h, w.grid_w)
+    dt_rope = time.perf_counter() - t
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"attention of {len(rows)} of {w.lq} query rows (stride {stride}) x "
                        f"{w.H} heads vs {w.kv_len} keys, head_dim {w.D}, fp64, "
-                       f"{dt:.1f} s on {threads} threads")}
+                       f"{dt:.1f} s on {threads} threads; RoPE of the chunk's Q and K "
+                       f"{dt_rope * 1e3:.0f} ms")}
 
 
 def copy_calibration():
@@ -259,7 +310,9 @@ def main():
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = wall_ms / args.steps
     rope_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    attn_each = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    attn_ms = sum(attn_each) / args.steps
+    pct = lambda f: attn_each[min(len(attn_each) - 1, int(f * len(attn_each)))]
 
     # RoPE/append alone: a burst of back-to-back launches over the rotated
     # buffer sets between two events, so event overhead does not inflate the
@@ -274,6 +327,11 @@ def main():
     r1.record()
     torch.cuda.synchronize()
     rope_burst_ms = r0.elapsed_time(r1) / burst
+
+    # fused QKV projection (the next row of the path), timed on its own
+    qkv_ms = time_qkv(crattn, w, dev, table, ext)
+    C = w.H * w.D
+    qkv_tflops = qkv_flops(w.B, w.lq, C, w.H, w.D) / (qkv_ms * 1e-3) / 1e12
 
     fl = attn_flops(w.B, w.H, w.lq, w.kv_len, w.D)
     rb = rope_bytes(w.B, w.lq, w.H, w.D)
@@ -315,6 +373,7 @@ def main():
                    "keys": w.kv_len, "t0": w.t0, "buffer_sets": args.sets},
         "ms_per_chunk": round(ms_per_step, 4),
         "attn_ms": round(attn_ms, 4),
+        "attn_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
         "attn_tflops": round(attn_tflops, 1),
         "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "rope_append_us": round(rope_burst_ms * 1e3, 2),
@@ -327,6 +386,13 @@ def main():
                           "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                           "bytes_per_launch": rb, "launches_timed": burst,
                           "traffic": read_traffic("rope")},
+        "qkv_rope_append": {"us": round(qkv_ms * 1e3, 2), "hidden": C,
+                            "roofline": {"bound": "mfma", "achieved": round(qkv_tflops, 1),
+                                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(qkv_tflops / PEAK_BF16_TFLOPS, 4),
+                                         "flops_per_launch": qkv_flops(w.B, w.lq, C, w.H, w.D),
+                                         "bytes_per_launch": qkv_bytes(w.B, w.lq, C, w.H, w.D),
+                                         "traffic": read_traffic("qkv")}},
         "extras": extras,
     }
     if not args.no_cpu_baseline:

@@ -119,3 +119,15 @@ def prior_cache(w: Workload, dtype=None):
         x = torch.randn(w.B, w.H, w.cap, w.D, generator=g, dtype=torch.float32)
         out.append(x if dt == torch.float32 else x.to(dt))
     return tuple(out)
+
+
+def projection_inputs(w: Workload, call_index: int, hidden: int | None = None):
+    """Hidden states x [B, lq, C] (N(0, 1)) and a QKV weight [3*H*D, C]
+    (N(0, 1) / sqrt(C)), bf16, C = H*D unless given (the Wan-class models
+    have hidden size = heads x head_dim)."""
+    C = w.H * w.D if hidden is None else hidden
+    g = torch.Generator().manual_seed(1000 * w.index + 500 + call_index)
+    x = torch.randn(w.B, w.lq, C, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    wt = (torch.randn(3 * w.H * w.D, C, generator=g, dtype=torch.float32) / C ** 0.5)
+    return x, wt.to(torch.bfloat16)
+
