@@ -18,6 +18,8 @@ Entry points (see include/crattn.h for the full contracts):
 * ``chunk_causal_attn_workspace_bytes`` / ``chunk_causal_attn`` -- flash
   attention of a chunk's queries against the cache, bidirectional inside a
   chunk and causal across chunks.
+* ``chunk_causal_attn_rope`` -- the same attention on un-rotated queries,
+  rotated on load.
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ import torch
 __all__ = [
     "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
     "rope_apply_append", "qkv_rope_append", "chunk_causal_attn_workspace_bytes",
-    "chunk_causal_attn", "crattn_last_error", "EXPORTS",
+    "chunk_causal_attn", "chunk_causal_attn_rope", "crattn_last_error", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +42,8 @@ CRATTN_F32, CRATTN_BF16 = 0, 1
 
 # Every symbol include/crattn.h declares.
 EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append", "qkv_rope_append",
-           "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "crattn_last_error")
+           "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "chunk_causal_attn_rope",
+           "crattn_last_error")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -79,6 +82,10 @@ def load():
     lib.chunk_causal_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                       ctypes.c_size_t, _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
     lib.chunk_causal_attn.restype = _i32
+    lib.chunk_causal_attn_rope.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _vp, _vp,
+                                           _i64, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_size_t,
+                                           _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
+    lib.chunk_causal_attn_rope.restype = _i32
     lib.crattn_last_error.argtypes = []
     lib.crattn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -204,4 +211,35 @@ def chunk_causal_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _raise(load().chunk_causal_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, kv_len, q_pos0,
                                     chunk_tokens, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                     B, H, D, Lq, float(scale), _stream(stream)))
+    return out
+
+
+def chunk_causal_attn_rope(q: torch.Tensor, table: torch.Tensor, max_t: int, max_h: int,
+                           max_w: int, t0: int, grid_h: int, grid_w: int, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, kv_len: int, q_pos0: int, chunk_tokens: int,
+                           out: torch.Tensor, lse: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, scale: float = 0.0,
+                           stream=None) -> torch.Tensor:
+    """As chunk_causal_attn, with q not yet rotated: the Causal-RoPE of each
+    query row (token (q_pos0 mod chunk_tokens) + i of the chunk starting at
+    time index t0) is applied on load."""
+    B, Lq, H, D = q.shape
+    cap = k_cache.shape[2]
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if tuple(out.shape) != (B, Lq, H, D):
+        raise ValueError("out must have q's shape")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != torch.bfloat16:
+            raise ValueError("caches must be bf16 [B, H, cap, D]")
+    if lse is not None and (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, H, Lq]")
+    if table.dtype != torch.float32:
+        raise ValueError("table must be float32")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _raise(load().chunk_causal_attn_rope(_ptr(q), _ptr(table), max_t, max_h, max_w, t0, grid_h,
+                                         grid_w, _ptr(k_cache), _ptr(v_cache), cap, kv_len,
+                                         q_pos0, chunk_tokens, _ptr(out), _ptr(lse),
+                                         _ptr(workspace), ws_bytes, B, H, D, Lq, float(scale),
+                                         _stream(stream)))
     return out

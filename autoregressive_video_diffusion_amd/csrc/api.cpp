@@ -246,34 +246,79 @@ size_t chunk_causal_attn_workspace_bytes(int B, int H, int64_t Lq, int64_t kv_le
   return crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, true).ws_bytes;
 }
 
-int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
-                      int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens, void *out, float *lse,
-                      void *workspace, size_t ws_bytes, int B, int H, int D, int64_t Lq,
-                      float scale, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Table and chunk geometry for rotating the queries on load.
+struct QRope {
+  const float *table;
+  int max_t, max_h, max_w;
+  int64_t t0;
+  int grid_h, grid_w;
+};
+
+int attn_call(const char *who, const QRope *rq, const void *q, const void *k_cache,
+              const void *v_cache, int64_t cap, int64_t kv_len, int64_t q_pos0,
+              int64_t chunk_tokens, void *out, float *lse, void *workspace, size_t ws_bytes, int B,
+              int H, int D, int64_t Lq, float scale, void *stream) {
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr)
-    return fail(CRATTN_EINVAL, "chunk_causal_attn: q, k_cache, v_cache and out are required");
+    return fail(CRATTN_EINVAL, "%s: q, k_cache, v_cache and out are required", who);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
       !aligned16(lse) || !aligned16(workspace))
-    return fail(CRATTN_EINVAL, "chunk_causal_attn: pointers must be 16-byte aligned");
-  if (cap < 1) return fail(CRATTN_EINVAL, "chunk_causal_attn: cap must be >= 1");
-  const int st = attn_shape_check(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, cap,
-                                  "chunk_causal_attn");
+    return fail(CRATTN_EINVAL, "%s: pointers must be 16-byte aligned", who);
+  if (cap < 1) return fail(CRATTN_EINVAL, "%s: cap must be >= 1", who);
+  const int st = attn_shape_check(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, cap, who);
   if (st != CRATTN_OK) return st;
   if (!(scale >= 0.f) || !isfinite(scale))
-    return fail(CRATTN_EINVAL, "chunk_causal_attn: scale must be finite and >= 0");
+    return fail(CRATTN_EINVAL, "%s: scale must be finite and >= 0", who);
   if ((double)B * H * (double)cap * D > (double)kMaxElems)
-    return fail(CRATTN_EINVAL, "chunk_causal_attn: cache element count exceeds 2^40");
+    return fail(CRATTN_EINVAL, "%s: cache element count exceeds 2^40", who);
   // the kernel indexes the keys of one head (cap rows of D elements) in 32 bits
   if ((double)cap * D >= 2147483648.0)
-    return fail(CRATTN_EINVAL, "chunk_causal_attn: cap * head_dim = %.0f must be below 2^31",
+    return fail(CRATTN_EINVAL, "%s: cap * head_dim = %.0f must be below 2^31", who,
                 (double)cap * D);
+  crattn::AttnArgs a{};
+  a.rope = rq != nullptr;
+  if (rq != nullptr) {
+    if (rq->table == nullptr || !aligned16(rq->table))
+      return fail(CRATTN_EINVAL, "%s: table is required, 16-byte aligned", who);
+    if (rq->max_t < 1 || rq->max_h < 1 || rq->max_w < 1 || rq->max_t > kMaxExtent ||
+        rq->max_h > kMaxExtent || rq->max_w > kMaxExtent)
+      return fail(CRATTN_EINVAL, "%s: table extents outside [1, %d]", who, kMaxExtent);
+    if (rq->t0 < 0 || rq->grid_h < 1 || rq->grid_w < 1)
+      return fail(CRATTN_EINVAL, "%s: t0 >= 0 and grid >= 1 required", who);
+    if (rq->grid_h > rq->max_h || rq->grid_w > rq->max_w)
+      return fail(CRATTN_EINVAL, "%s: grid %dx%d exceeds the table (%dx%d)", who, rq->grid_h,
+                  rq->grid_w, rq->max_h, rq->max_w);
+    const int64_t per_frame = (int64_t)rq->grid_h * rq->grid_w;
+    if (chunk_tokens % per_frame != 0)
+      return fail(CRATTN_EINVAL, "%s: chunk_tokens %lld is not a whole number of %dx%d frames",
+                  who, (long long)chunk_tokens, rq->grid_h, rq->grid_w);
+    const int64_t tok_off = q_pos0 % chunk_tokens;
+    if (tok_off + Lq > chunk_tokens)
+      return fail(CRATTN_EINVAL, "%s: the query rows must lie in one chunk", who);
+    const int64_t last_t = rq->t0 + (tok_off + Lq - 1) / per_frame;
+    if (last_t >= rq->max_t || rq->t0 > kMaxElems)
+      return fail(CRATTN_EINVAL, "%s: time index %lld outside the table (max_t %d)", who,
+                  (long long)last_t, rq->max_t);
+    if (tok_off + Lq > (int64_t(1) << 31))
+      return fail(CRATTN_EINVAL, "%s: token index exceeds 2^31", who);
+    a.table = rq->table;
+    a.max_t = rq->max_t;
+    a.max_h = rq->max_h;
+    a.max_w = rq->max_w;
+    a.t0 = rq->t0;
+    a.tok_off = tok_off;
+    a.grid_h = rq->grid_h;
+    a.grid_w = rq->grid_w;
+  }
   const bool split_ok = workspace != nullptr;
   const crattn::AttnPlan plan =
       crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, split_ok);
   if (split_ok && ws_bytes < plan.ws_bytes)
-    return fail(CRATTN_EINVAL, "chunk_causal_attn: workspace of %zu bytes, %zu needed", ws_bytes,
+    return fail(CRATTN_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, ws_bytes,
                 plan.ws_bytes);
-  crattn::AttnArgs a;
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -290,8 +335,32 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, i
   a.D = D;
   a.Lq = Lq;
   a.scale = scale;
-  return hip_status(crattn::launch_attn(a, plan, static_cast<hipStream_t>(stream)),
-                    "chunk_causal_attn launch");
+  char what[64];
+  snprintf(what, sizeof what, "%s launch", who);
+  return hip_status(crattn::launch_attn(a, plan, static_cast<hipStream_t>(stream)), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
+                      int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens, void *out, float *lse,
+                      void *workspace, size_t ws_bytes, int B, int H, int D, int64_t Lq,
+                      float scale, void *stream) {
+  return attn_call("chunk_causal_attn", nullptr, q, k_cache, v_cache, cap, kv_len, q_pos0,
+                   chunk_tokens, out, lse, workspace, ws_bytes, B, H, D, Lq, scale, stream);
+}
+
+int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max_h, int max_w,
+                           int64_t t0, int grid_h, int grid_w, const void *k_cache,
+                           const void *v_cache, int64_t cap, int64_t kv_len, int64_t q_pos0,
+                           int64_t chunk_tokens, void *out, float *lse, void *workspace,
+                           size_t ws_bytes, int B, int H, int D, int64_t Lq, float scale,
+                           void *stream) {
+  const QRope rq{table, max_t, max_h, max_w, t0, grid_h, grid_w};
+  return attn_call("chunk_causal_attn_rope", &rq, q, k_cache, v_cache, cap, kv_len, q_pos0,
+                   chunk_tokens, out, lse, workspace, ws_bytes, B, H, D, Lq, scale, stream);
 }
 
 const char *crattn_last_error(void) { return g_err; }

@@ -33,6 +33,7 @@
 //   * Softmax in fp32 with base-2 exponent, log2(e) folded into the scale;
 //     P rounded to bf16 for the second product; O kept in fp32.
 #include "crattn_internal.h"
+#include "rope_common.h"
 #include "../../include/crattn.h"
 
 #include <math.h>
@@ -64,6 +65,10 @@ struct AttnKArgs {
   float scale_log2;
   int64_t seg0_rows, tiles0, tiles_full, n_full, last_rows, n_tiles;
   int splits;
+  // Causal-RoPE of the queries on load (the rotating instance only)
+  const float2 *table;
+  TabGeom tg;
+  uint32_t per_frame, gw, t0, tok_off;
 };
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
@@ -152,7 +157,7 @@ struct Pitch {
   static constexpr int V = CPR + 4;
 };
 
-template <int D, int NW, int QB, int MINB>
+template <int D, int NW, int QB, int MINB, bool ROPE>
 __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   constexpr int kBN = 64;
   constexpr int DK = D / 16;    // k-steps of the QK product
@@ -249,6 +254,27 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (ok) x = *reinterpret_cast<const uint4 *>(qp + ks * 16);
       qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    if constexpr (ROPE) {
+      // Causal-RoPE of the query on load.  Row `row` of the call is token
+      // tok_off + row of its chunk (the rows of a rotating call lie in one
+      // chunk).  The lane's 8 features of sub-step ks are pairs
+      // 8 ks + 4 hf + e; each is rotated with the same fp32 arithmetic and
+      // single bf16 rounding as the RoPE/append pass.
+      const Pos p = decode_pos(a.tok_off + (uint32_t)min(row, a.Lq - 1), a.per_frame, a.gw, a.t0);
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
+        uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 cs = pair_cs(a.table, a.tg, (uint32_t)(ks * 8 + hf * 4 + e), p);
+          const float2 r = rotate_pair(__uint_as_float(wv[e] << 16),
+                                       __uint_as_float(wv[e] & 0xffff0000u), cs);
+          wv[e] = pack_bf16(r.x, r.y);
+        }
+        qf[qb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+      }
     }
   }
   // Settle the Q loads here (vmcnt 0; expcnt and lgkmcnt not waited on), in
@@ -684,9 +710,9 @@ FwdShape fwd_shape(int D) {
   return FwdShape{8, 1, 64};
 }
 
-template <int D, int NW, int QB, int MINB>
+template <int D, int NW, int QB, int MINB, bool ROPE>
 hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB, ROPE>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      s, k);
   return hipGetLastError();
 }
@@ -761,11 +787,28 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.ws_o = p.splits > 1 ? static_cast<float *>(a.workspace) : nullptr;
   k.ws_lse = p.splits > 1 ? reinterpret_cast<float *>(static_cast<char *>(a.workspace) + o_bytes)
                           : nullptr;
+  k.table = nullptr;
+  k.tg = TabGeom{};
+  k.per_frame = k.gw = k.t0 = k.tok_off = 0;
+  if (a.rope) {
+    const RopeSplit sp = rope_split(a.D);
+    k.table = reinterpret_cast<const float2 *>(a.table);
+    k.tg.ht = (uint32_t)(sp.dt / 2);
+    k.tg.hh = (uint32_t)(sp.dh / 2);
+    k.tg.base_h = (uint32_t)a.max_t * k.tg.ht;
+    k.tg.base_w = k.tg.base_h + (uint32_t)a.max_h * k.tg.hh;
+    k.per_frame = (uint32_t)a.grid_h * (uint32_t)a.grid_w;
+    k.gw = (uint32_t)a.grid_w;
+    k.t0 = (uint32_t)a.t0;
+    k.tok_off = (uint32_t)a.tok_off;
+  }
   hipError_t e;
   if (a.D == 128)
-    e = launch_fwd<128, 8, 1, 1>(k, p.grid, s);
+    e = a.rope ? launch_fwd<128, 8, 1, 1, true>(k, p.grid, s)
+               : launch_fwd<128, 8, 1, 1, false>(k, p.grid, s);
   else
-    e = launch_fwd<64, 8, 1, 1>(k, p.grid, s);
+    e = a.rope ? launch_fwd<64, 8, 1, 1, true>(k, p.grid, s)
+               : launch_fwd<64, 8, 1, 1, false>(k, p.grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
   CombineArgs c;
   c.ws_o = k.ws_o;

@@ -68,6 +68,12 @@ struct AttnArgs {
   int B, H, D;
   int64_t Lq;
   float scale;
+  // Causal-RoPE of the queries on load (chunk_causal_attn_rope)
+  bool rope;
+  const float *table;
+  int max_t, max_h, max_w;
+  int64_t t0, tok_off;
+  int grid_h, grid_w;
 };
 
 // Launch plan of one attention call: how query rows are tiled and how the

@@ -297,10 +297,9 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
         if (part[i] < 2) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float2 c = cs[i][g][e];
-            const float xr = y[2 * e], yr = y[2 * e + 1];
-            y[2 * e] = xr * c.x - yr * c.y;
-            y[2 * e + 1] = xr * c.y + yr * c.x;
+            const float2 r = rotate_pair(y[2 * e], y[2 * e + 1], cs[i][g][e]);
+            y[2 * e] = r.x;
+            y[2 * e + 1] = r.y;
           }
         }
         wv[g][0] = pack_bf16(y[0], y[1]);

@@ -70,8 +70,8 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 
 // Rotate the bf16 pair packed in one dword (element 2j in the low half).
 __device__ inline uint32_t rot_bf16(uint32_t u, float2 cs) {
-  const float x = bf_lo(u), y = bf_hi(u);
-  return pack_bf16(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
+  const float2 r = rotate_pair(bf_lo(u), bf_hi(u), cs);
+  return pack_bf16(r.x, r.y);
 }
 
 struct AppendGeom {
@@ -125,9 +125,7 @@ __global__ void __launch_bounds__(256) rope_append_bf16_kernel(RopeAppendArgs a,
   }
 }
 
-__device__ inline float2 rot_f32(float x, float y, float2 cs) {
-  return make_float2(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
-}
+__device__ inline float2 rot_f32(float x, float y, float2 cs) { return rotate_pair(x, y, cs); }
 
 // fp32 variant: a 16-byte vector is two pairs.
 __global__ void __launch_bounds__(256) rope_append_f32_kernel(RopeAppendArgs a, AppendGeom g,

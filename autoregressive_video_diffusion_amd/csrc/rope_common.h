@@ -45,4 +45,11 @@ __device__ inline float2 pair_cs(const float2 *__restrict__ tab, const TabGeom &
   return tab[idx];
 }
 
+// Rotation of the pair (x, y) by the angle whose (cos, sin) is cs, in fp32
+// with one fixed rounding order (the two products of each output fused as
+// written), so every kernel that rotates produces the same bits.
+__device__ inline float2 rotate_pair(float x, float y, float2 cs) {
+  return make_float2(__builtin_fmaf(x, cs.x, -(y * cs.y)), __builtin_fmaf(x, cs.y, y * cs.x));
+}
+
 }  // namespace crattn

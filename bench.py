@@ -145,10 +145,27 @@ def time_attn_only(crattn, w, dev, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
-def time_qkv(crattn, w, dev, table, ext, burst=40):
+def burst_ms(call, bursts, n):
+    """Per-launch time (ms) of `bursts` bursts of n back-to-back calls, each
+    burst between two events on the stream; sorted ascending."""
+    import torch
+
+    out = []
+    for _ in range(bursts):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / n)
+    return sorted(out)
+
+
+def time_qkv(crattn, w, dev, table, ext, burst=20, bursts=5):
     """Fused QKV projection + RoPE + append of the chunk (hidden size H*D):
-    average per-launch time (ms) of a burst of back-to-back launches over
-    four hidden-state sets, between two events on the stream."""
+    per-launch time (ms) of bursts of back-to-back launches over four
+    hidden-state sets; sorted ascending, one value per burst."""
     import torch
 
     from workloads import projection_inputs
@@ -164,16 +181,36 @@ def time_qkv(crattn, w, dev, table, ext, burst=40):
         crattn.qkv_rope_append(xs[i % 4], wt, q_out, kc, vc, w.cache_pos, table, *ext, w.t0,
                                w.tok_off, w.grid_h, w.grid_w)
 
-    for i in range(burst):
+    for i in range(2 * burst):
         call(i)
+    torch.cuda.synchronize()
+    return burst_ms(call, bursts, burst)
+
+
+def fused_step_ms(crattn, w, sets, table, ext, ws, reps=20):
+    """The same step with the query rotation folded into attention: the
+    RoPE/append pass writes only K' and V (a cache update), then
+    chunk_causal_attn_rope rotates Q on load.  Average ms per step over reps
+    steps, events on the stream."""
+    import torch
+
+    def step(i):
+        b = sets[i % len(sets)]
+        crattn.rope_apply_append(None, None, b.k, b.v, b.kc, b.vc, w.cache_pos, table, *ext, w.t0,
+                                 w.tok_off, w.grid_h, w.grid_w)
+        crattn.chunk_causal_attn_rope(b.q, table, *ext, w.t0, w.grid_h, w.grid_w, b.kc, b.vc,
+                                      w.kv_len, w.q_pos0, w.chunk_tokens, b.out, b.lse, ws)
+
+    for i in range(4):
+        step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(burst):
-        call(i)
+    for i in range(reps):
+        step(i)
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / burst
+    return e0.elapsed_time(e1) / reps
 
 
 def rollout_ms(crattn, dev, reps=2):
@@ -314,22 +351,23 @@ def main():
     attn_ms = sum(attn_each) / args.steps
     pct = lambda f: attn_each[min(len(attn_each) - 1, int(f * len(attn_each)))]
 
-    # RoPE/append alone: a burst of back-to-back launches over the rotated
-    # buffer sets between two events, so event overhead does not inflate the
-    # per-launch time of this ~10 us kernel.
+    # RoPE/append alone: bursts of back-to-back launches over the rotated
+    # buffer sets, each between two events, so event overhead does not
+    # inflate the per-launch time of this ~15 us kernel; the median burst is
+    # reported (the spread between bursts is a few percent)
     burst = max(4 * len(sets), 40)
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    for i in range(burst):
+
+    def rope_call(i):
         b = sets[i % len(sets)]
         crattn.rope_apply_append(b.q, b.q_out, b.k, b.v, b.kc, b.vc, w.cache_pos, table, *ext,
                                  w.t0, w.tok_off, w.grid_h, w.grid_w)
-    r1.record()
-    torch.cuda.synchronize()
-    rope_burst_ms = r0.elapsed_time(r1) / burst
+
+    rope_bursts = burst_ms(rope_call, 7, burst)
+    rope_burst_ms = rope_bursts[len(rope_bursts) // 2]
 
     # fused QKV projection (the next row of the path), timed on its own
-    qkv_ms = time_qkv(crattn, w, dev, table, ext)
+    qkv_bursts = time_qkv(crattn, w, dev, table, ext)
+    qkv_ms = qkv_bursts[len(qkv_bursts) // 2]
     C = w.H * w.D
     qkv_tflops = qkv_flops(w.B, w.lq, C, w.H, w.D) / (qkv_ms * 1e-3) / 1e12
 
@@ -345,6 +383,7 @@ def main():
         extras["sp480_attn_tflops"] = round(
             attn_flops(1, SP480.H, SP480.lq, SP480.kv_len, SP480.D)
             / (extras["sp480_attn_ms"] * 1e-3) / 1e12, 1)
+        extras["step_fused_qrot_ms"] = round(fused_step_ms(crattn, w, sets, table, ext, ws), 4)
         extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)
         extras["rollout480_ms_per_chunk"] = round(extras["rollout480_ms_total"] / 7, 3)
         torch.cuda.empty_cache()
@@ -377,6 +416,9 @@ def main():
         "attn_tflops": round(attn_tflops, 1),
         "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
         "rope_append_us": round(rope_burst_ms * 1e3, 2),
+        "rope_append_us_p10_p50_p90": [round(rope_bursts[0] * 1e3, 2),
+                                       round(rope_burst_ms * 1e3, 2),
+                                       round(rope_bursts[-1] * 1e3, 2)],
         "rope_append_in_step_us": round(rope_ms * 1e3, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -384,9 +426,10 @@ def main():
                      "traffic": read_traffic()},
         "rope_roofline": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
-                          "bytes_per_launch": rb, "launches_timed": burst,
+                          "bytes_per_launch": rb, "launches_timed": 7 * burst,
                           "traffic": read_traffic("rope")},
         "qkv_rope_append": {"us": round(qkv_ms * 1e3, 2), "hidden": C,
+                            "us_per_burst": [round(x * 1e3, 2) for x in qkv_bursts],
                             "roofline": {"bound": "mfma", "achieved": round(qkv_tflops, 1),
                                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                          "frac": round(qkv_tflops / PEAK_BF16_TFLOPS, 4),

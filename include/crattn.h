@@ -218,6 +218,40 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache,
                       void *out, float *lse, void *workspace, size_t ws_bytes,
                       int B, int H, int D, int64_t Lq, float scale, void *stream);
 
+/*
+ * Chunk-causal flash attention with the queries' Causal-RoPE applied on
+ * load [CRSP §2.B-§2.C; WF]: the same computation as rope_apply_append
+ * followed by chunk_causal_attn on the rotated queries, without writing Q'
+ * to memory.
+ *
+ *   q        device bf16 [B][Lq][H][D]: the queries of this call, NOT
+ *            rotated.  Row i is token (q_pos0 mod chunk_tokens) + i of its
+ *            chunk, in raster order over grid_h x grid_w frames; its time
+ *            index is t0 + that token's frame.  All Lq rows must lie in one
+ *            chunk: (q_pos0 mod chunk_tokens) + Lq <= chunk_tokens.
+ *   table, max_t, max_h, max_w  the cos/sin table of rope_precompute for
+ *            head_dim D, and the extents it was built with.
+ *   t0       global time index of the chunk's first frame.
+ *   grid_h, grid_w  latent grid of one frame; chunk_tokens must be a whole
+ *            number of frames.
+ *   all other arguments as for chunk_causal_attn.
+ *
+ * Arithmetic: each query pair is rotated in fp32 and rounded to bf16 once,
+ * exactly as rope_apply_append does, so the result equals that two-call
+ * sequence bit for bit; the attention arithmetic is chunk_causal_attn's.
+ *
+ * Errors: those of chunk_causal_attn, and EINVAL for a NULL or misaligned
+ * table, table extents outside [1, 2^20], t0 < 0, a grid below 1 or beyond
+ * the table, chunk_tokens not a whole number of frames, query rows that
+ * leave their chunk, or a time index t0 + last frame >= max_t.
+ */
+int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max_h, int max_w,
+                           int64_t t0, int grid_h, int grid_w, const void *k_cache,
+                           const void *v_cache, int64_t cap, int64_t kv_len, int64_t q_pos0,
+                           int64_t chunk_tokens, void *out, float *lse, void *workspace,
+                           size_t ws_bytes, int B, int H, int D, int64_t Lq, float scale,
+                           void *stream);
+
 /* Message describing the last non-zero return on this thread ("" if none). */
 const char *crattn_last_error(void);
 

@@ -126,6 +126,33 @@ def test_chunk_causal_attn_rejects(kw, code):
     assert crattn.crattn_last_error() != ""
 
 
+def _attn_rope(**kw):
+    # tiny geometry: 64-token chunks of one 8x8 frame, the last chunk at t0 3
+    a = dict(q=FAKE, table=FAKE, mt=4, mh=8, mw=8, t0=3, gh=8, gw=8, k=FAKE, v=FAKE, cap=256,
+             kv=256, pos0=192, L=64, out=FAKE, lse=None, ws=None, wsb=0, B=1, H=2, D=64, Lq=64,
+             scale=0.0)
+    a.update(kw)
+    return _lib().chunk_causal_attn_rope(a["q"], a["table"], a["mt"], a["mh"], a["mw"], a["t0"],
+                                         a["gh"], a["gw"], a["k"], a["v"], a["cap"], a["kv"],
+                                         a["pos0"], a["L"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                         a["B"], a["H"], a["D"], a["Lq"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    # the attention checks still apply
+    (dict(q=None), 1), (dict(kv=255), 1), (dict(D=96), 2), (dict(cap=1 << 25), 1),
+    # table and geometry
+    (dict(table=None), 1), (dict(table=MIS), 1), (dict(mt=0), 1), (dict(t0=-1), 1),
+    (dict(t0=4), 1), (dict(gh=9), 1), (dict(gw=0), 1),
+    # chunk_tokens must be whole frames; rows must stay in their chunk
+    (dict(L=96, cap=384, kv=384, pos0=288, Lq=96, mt=8), 1),
+    (dict(pos0=128, Lq=100), 1),
+])
+def test_chunk_causal_attn_rope_rejects(kw, code):
+    assert _attn_rope(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
 def test_rope_precompute_rejects():
     lib = _lib()
     assert lib.rope_precompute(None, 64, 4, 8, 8, 10000.0, None) == 1
