@@ -259,18 +259,35 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       // Causal-RoPE of the query on load.  Row `row` of the call is token
       // tok_off + row of its chunk (the rows of a rotating call lie in one
       // chunk).  The lane's 8 features of sub-step ks are pairs
-      // 8 ks + 4 hf + e; each is rotated with the same fp32 arithmetic and
-      // single bf16 rounding as the RoPE/append pass.
+      // 8 ks + 4 hf + e.  Their (cos, sin) are gathered in one batch from
+      // per-lane pointers into the three axis sections of the table (pair q
+      // of axis a is entry base_a + q), then each pair is rotated with the
+      // same fp32 arithmetic and single bf16 rounding as the RoPE/append pass.
+      constexpr int HT = (D - 4 * (D / 6)) / 2;  // pairs of the t group
+      constexpr int HH = D / 6;                  // pairs of the h (= w) group
       const Pos p = decode_pos(a.tok_off + (uint32_t)min(row, a.Lq - 1), a.per_frame, a.gw, a.t0);
+      const float2 *ax[3] = {a.table + p.t * HT + 4 * hf,
+                             a.table + a.tg.base_h + p.h * HH - HT + 4 * hf,
+                             a.table + a.tg.base_w + p.w * HH - HT - HH + 4 * hf};
+      auto axis = [](int q) { return q < HT ? 0 : q < HT + HH ? 1 : 2; };
+      float2 cs[DK][4];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q0 = ks * 8 + e;  // pair of the low half-wave; the high one is q0 + 4
+          const int a0 = axis(q0), a1 = axis(q0 + 4);
+          const float2 *ptr = a0 == a1 ? ax[a0] : (hf ? ax[a1] : ax[a0]);
+          cs[ks][e] = ptr[q0];
+        }
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
         uint32_t wv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float2 cs = pair_cs(a.table, a.tg, (uint32_t)(ks * 8 + hf * 4 + e), p);
           const float2 r = rotate_pair(__uint_as_float(wv[e] << 16),
-                                       __uint_as_float(wv[e] & 0xffff0000u), cs);
+                                       __uint_as_float(wv[e] & 0xffff0000u), cs[ks][e]);
           wv[e] = pack_bf16(r.x, r.y);
         }
         qf[qb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));

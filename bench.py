@@ -187,14 +187,18 @@ def time_qkv(crattn, w, dev, table, ext, burst=20, bursts=5):
     return burst_ms(call, bursts, burst)
 
 
-def fused_step_ms(crattn, w, sets, table, ext, ws, reps=20):
-    """The same step with the query rotation folded into attention: the
-    RoPE/append pass writes only K' and V (a cache update), then
-    chunk_causal_attn_rope rotates Q on load.  Average ms per step over reps
-    steps, events on the stream."""
+def fused_step_ms(crattn, w, sets, table, ext, ws, reps=10, rounds=3):
+    """The step with the query rotation folded into attention (the
+    RoPE/append pass writes only K' and V, then chunk_causal_attn_rope
+    rotates Q on load) against the plain step, timed in alternating blocks of
+    reps steps in the same window so clock drift hits both alike.  Returns
+    (plain ms, fused ms): the median block of each."""
     import torch
 
-    def step(i):
+    def plain(i):
+        run_step(crattn, w, sets[i % len(sets)], table, ext, ws)
+
+    def fused(i):
         b = sets[i % len(sets)]
         crattn.rope_apply_append(None, None, b.k, b.v, b.kc, b.vc, w.cache_pos, table, *ext, w.t0,
                                  w.tok_off, w.grid_h, w.grid_w)
@@ -202,15 +206,14 @@ def fused_step_ms(crattn, w, sets, table, ext, ws, reps=20):
                                       w.kv_len, w.q_pos0, w.chunk_tokens, b.out, b.lse, ws)
 
     for i in range(4):
-        step(i)
+        plain(i)
+        fused(i)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    tp, tf = [], []
+    for _ in range(rounds):
+        tp += burst_ms(plain, 1, reps)
+        tf += burst_ms(fused, 1, reps)
+    return sorted(tp)[len(tp) // 2], sorted(tf)[len(tf) // 2]
 
 
 def rollout_ms(crattn, dev, reps=2):
@@ -383,7 +386,8 @@ def main():
         extras["sp480_attn_tflops"] = round(
             attn_flops(1, SP480.H, SP480.lq, SP480.kv_len, SP480.D)
             / (extras["sp480_attn_ms"] * 1e-3) / 1e12, 1)
-        extras["step_fused_qrot_ms"] = round(fused_step_ms(crattn, w, sets, table, ext, ws), 4)
+        plain_ms, fused_ms = fused_step_ms(crattn, w, sets, table, ext, ws)
+        extras["step_plain_vs_fused_qrot_ms"] = [round(plain_ms, 4), round(fused_ms, 4)]
         extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)
         extras["rollout480_ms_per_chunk"] = round(extras["rollout480_ms_total"] / 7, 3)
         torch.cuda.empty_cache()
