@@ -20,6 +20,10 @@ Entry points (see include/crattn.h for the full contracts):
   chunk and causal across chunks.
 * ``chunk_causal_attn_rope`` -- the same attention on un-rotated queries,
   rotated on load.
+* ``hsa_pool_bytes`` / ``hsa_pool_keys`` / ``hsa_select`` / ``hsa_attn`` --
+  hierarchical block-sparse attention: pooled frame and block keys, two-level
+  block selection per query block, attention over the own chunk plus the
+  selected blocks.
 """
 from __future__ import annotations
 
@@ -31,7 +35,8 @@ import torch
 __all__ = [
     "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
     "rope_apply_append", "qkv_rope_append", "chunk_causal_attn_workspace_bytes",
-    "chunk_causal_attn", "chunk_causal_attn_rope", "crattn_last_error", "EXPORTS",
+    "chunk_causal_attn", "chunk_causal_attn_rope", "hsa_pool_bytes", "hsa_pool_keys",
+    "hsa_select", "hsa_attn", "crattn_last_error", "EXPORTS", "HSA_QBLOCK", "HSA_KBLOCK",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +48,8 @@ CRATTN_F32, CRATTN_BF16 = 0, 1
 # Every symbol include/crattn.h declares.
 EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append", "qkv_rope_append",
            "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "chunk_causal_attn_rope",
-           "crattn_last_error")
+           "hsa_pool_bytes", "hsa_pool_keys", "hsa_select", "hsa_attn", "crattn_last_error")
+HSA_QBLOCK, HSA_KBLOCK = 256, 64
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -86,6 +92,16 @@ def load():
                                            _i64, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_size_t,
                                            _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
     lib.chunk_causal_attn_rope.restype = _i32
+    lib.hsa_pool_bytes.argtypes = [_i32, _i32, _i64, _i32, _i32]
+    lib.hsa_pool_bytes.restype = ctypes.c_size_t
+    lib.hsa_pool_keys.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _i32, _i32, _i32, _vp]
+    lib.hsa_pool_keys.restype = _i32
+    lib.hsa_select.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _i32, _i32, _vp, _i32, _i32,
+                               _i32, _i64, _vp]
+    lib.hsa_select.restype = _i32
+    lib.hsa_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _i32,
+                             _i32, _i32, _i64, ctypes.c_float, _vp]
+    lib.hsa_attn.restype = _i32
     lib.crattn_last_error.argtypes = []
     lib.crattn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -243,3 +259,60 @@ def chunk_causal_attn_rope(q: torch.Tensor, table: torch.Tensor, max_t: int, max
                                          _ptr(workspace), ws_bytes, B, H, D, Lq, float(scale),
                                          _stream(stream)))
     return out
+
+
+def hsa_pool_bytes(B: int, H: int, cap: int, D: int, per_frame: int) -> int:
+    return int(load().hsa_pool_bytes(B, H, cap, D, per_frame))
+
+
+def hsa_pool_keys(k_cache: torch.Tensor, row0: int, nrows: int, per_frame: int,
+                  pool: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pool the keys of cache rows [row0, row0 + nrows) (whole frames) into
+    `pool` (float32, hsa_pool_bytes bytes): frame means then block means."""
+    B, H, cap, D = k_cache.shape
+    if k_cache.dtype != torch.bfloat16:
+        raise ValueError("k_cache must be bf16 [B, H, cap, D]")
+    if pool.dtype != torch.float32 or pool.numel() * 4 < hsa_pool_bytes(B, H, cap, D, per_frame):
+        raise ValueError("pool must be float32 of at least hsa_pool_bytes(...) bytes")
+    _raise(load().hsa_pool_keys(_ptr(k_cache), cap, row0, nrows, per_frame, _ptr(pool), B, H, D,
+                                _stream(stream)))
+    return pool
+
+
+def hsa_select(q: torch.Tensor, pool: torch.Tensor, cap: int, per_frame: int, q_pos0: int,
+               chunk_tokens: int, kf: int, kb: int, sel: torch.Tensor, stream=None) -> torch.Tensor:
+    """q: [B, Lq, H, D] bf16 (rotated); sel: int32 [B, H, ceil(Lq/256), kb]."""
+    B, Lq, H, D = q.shape
+    if q.dtype != torch.bfloat16 or pool.dtype != torch.float32:
+        raise ValueError("q must be bf16 and pool float32")
+    nqb = -(-Lq // HSA_QBLOCK)
+    if sel.dtype != torch.int32 or tuple(sel.shape) != (B, H, nqb, kb):
+        raise ValueError(f"sel must be int32 [{B}, {H}, {nqb}, {kb}]")
+    _raise(load().hsa_select(_ptr(q), _ptr(pool), cap, per_frame, q_pos0, chunk_tokens, kf, kb,
+                             _ptr(sel), B, H, D, Lq, _stream(stream)))
+    return sel
+
+
+def hsa_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, q_pos0: int,
+             chunk_tokens: int, per_frame: int, sel: torch.Tensor, out: torch.Tensor,
+             lse: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> torch.Tensor:
+    """Attention over the own chunk plus the selected blocks of sel."""
+    B, Lq, H, D = q.shape
+    cap = k_cache.shape[2]
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if tuple(out.shape) != (B, Lq, H, D):
+        raise ValueError("out must have q's shape")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != torch.bfloat16:
+            raise ValueError("caches must be bf16 [B, H, cap, D]")
+    if lse is not None and (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, H, Lq]")
+    nqb = -(-Lq // HSA_QBLOCK)
+    if sel.dtype != torch.int32 or sel.dim() != 4 or tuple(sel.shape[:3]) != (B, H, nqb):
+        raise ValueError(f"sel must be int32 [{B}, {H}, {nqb}, kb]")
+    _raise(load().hsa_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, q_pos0, chunk_tokens,
+                           per_frame, _ptr(sel), sel.shape[3], _ptr(out), _ptr(lse), B, H, D, Lq,
+                           float(scale), _stream(stream)))
+    return out
+

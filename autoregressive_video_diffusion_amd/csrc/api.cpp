@@ -3,6 +3,8 @@
 // documented in include/crattn.h.  Every check runs on the host before any
 // HIP call, so an invalid call launches nothing and writes nothing.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -258,7 +260,14 @@ struct QRope {
   int grid_h, grid_w;
 };
 
-int attn_call(const char *who, const QRope *rq, const void *q, const void *k_cache,
+// Selected key blocks for the block-sparse instance.
+struct Sparse {
+  const int32_t *sel;
+  int kb, per_frame;
+};
+
+int attn_call(const char *who, const QRope *rq, const Sparse *sp, const void *q,
+              const void *k_cache,
               const void *v_cache, int64_t cap, int64_t kv_len, int64_t q_pos0,
               int64_t chunk_tokens, void *out, float *lse, void *workspace, size_t ws_bytes, int B,
               int H, int D, int64_t Lq, float scale, void *stream) {
@@ -280,6 +289,26 @@ int attn_call(const char *who, const QRope *rq, const void *q, const void *k_cac
                 (double)cap * D);
   crattn::AttnArgs a{};
   a.rope = rq != nullptr;
+  if (sp != nullptr) {
+    if (sp->sel == nullptr || !aligned16(sp->sel))
+      return fail(CRATTN_EINVAL, "%s: sel is required, 16-byte aligned", who);
+    if (sp->kb < 1 || sp->kb > CRATTN_HSA_MAX_KB)
+      return fail(CRATTN_EINVAL, "%s: kb %d outside [1, %d]", who, sp->kb, CRATTN_HSA_MAX_KB);
+    if (sp->per_frame < 1 || chunk_tokens % sp->per_frame != 0 || cap % sp->per_frame != 0)
+      return fail(CRATTN_EINVAL, "%s: chunk_tokens and cap must be whole frames of %d tokens",
+                  who, sp->per_frame);
+    if (q_pos0 % chunk_tokens + Lq > chunk_tokens)
+      return fail(CRATTN_EINVAL, "%s: the query rows must lie in one chunk", who);
+    const int nbf = (sp->per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK;
+    const int64_t hist_blocks = q_pos0 / chunk_tokens * (chunk_tokens / sp->per_frame) * nbf;
+    if (hist_blocks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
+      return fail(CRATTN_EINVAL, "%s: history too long for 32-bit block ids", who);
+    a.sel = sp->sel;
+    a.sel_kb = sp->kb;
+    a.sel_nbf = nbf;
+    a.sel_per_frame = sp->per_frame;
+    a.sel_n_hist_blocks = (int)hist_blocks;
+  }
   if (rq != nullptr) {
     if (rq->table == nullptr || !aligned16(rq->table))
       return fail(CRATTN_EINVAL, "%s: table is required, 16-byte aligned", who);
@@ -313,7 +342,7 @@ int attn_call(const char *who, const QRope *rq, const void *q, const void *k_cac
     a.grid_h = rq->grid_h;
     a.grid_w = rq->grid_w;
   }
-  const bool split_ok = workspace != nullptr;
+  const bool split_ok = workspace != nullptr && sp == nullptr;
   const crattn::AttnPlan plan =
       crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, split_ok);
   if (split_ok && ws_bytes < plan.ws_bytes)
@@ -348,7 +377,7 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, i
                       int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens, void *out, float *lse,
                       void *workspace, size_t ws_bytes, int B, int H, int D, int64_t Lq,
                       float scale, void *stream) {
-  return attn_call("chunk_causal_attn", nullptr, q, k_cache, v_cache, cap, kv_len, q_pos0,
+  return attn_call("chunk_causal_attn", nullptr, nullptr, q, k_cache, v_cache, cap, kv_len, q_pos0,
                    chunk_tokens, out, lse, workspace, ws_bytes, B, H, D, Lq, scale, stream);
 }
 
@@ -359,8 +388,116 @@ int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max
                            size_t ws_bytes, int B, int H, int D, int64_t Lq, float scale,
                            void *stream) {
   const QRope rq{table, max_t, max_h, max_w, t0, grid_h, grid_w};
-  return attn_call("chunk_causal_attn_rope", &rq, q, k_cache, v_cache, cap, kv_len, q_pos0,
+  return attn_call("chunk_causal_attn_rope", &rq, nullptr, q, k_cache, v_cache, cap, kv_len, q_pos0,
                    chunk_tokens, out, lse, workspace, ws_bytes, B, H, D, Lq, scale, stream);
+}
+
+size_t hsa_pool_bytes(int B, int H, int64_t cap, int D, int per_frame) {
+  if (B < 1 || H < 1 || per_frame < 1 || cap < 1 || cap % per_frame != 0) return 0;
+  if (D != 64 && D != 128) return 0;
+  const int64_t nf = cap / per_frame;
+  const int64_t nbf = (per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK;
+  const double bytes = (double)B * H * (double)(nf + nf * nbf) * D * 4.0;
+  if (bytes > (double)kMaxElems) return 0;
+  return (size_t)B * H * (size_t)(nf + nf * nbf) * D * 4u;
+}
+
+int hsa_pool_keys(const void *k_cache, int64_t cap, int64_t row0, int64_t nrows, int per_frame,
+                  void *pool, int B, int H, int D, void *stream) {
+  if (k_cache == nullptr || pool == nullptr)
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: k_cache and pool are required");
+  if (!aligned16(k_cache) || !aligned16(pool))
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: pointers must be 16-byte aligned");
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "hsa_pool_keys: head_dim %d not supported (64 or 128)", D);
+  if (B < 1 || H < 1 || per_frame < 1 || cap < 1 || cap % per_frame != 0)
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: B, H, per_frame >= 1 and cap a whole number of "
+                               "frames required");
+  if (row0 < 0 || nrows < 1 || row0 % per_frame != 0 || nrows % per_frame != 0 ||
+      nrows > cap - row0)
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: rows [%lld, %lld) must be whole frames inside "
+                               "[0, %lld)", (long long)row0, (long long)(row0 + nrows),
+                (long long)cap);
+  if (hsa_pool_bytes(B, H, cap, D, per_frame) == 0 || (double)B * H * (double)cap * D > (double)kMaxElems)
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: sizes too large");
+  if ((double)B * H * (double)(nrows / per_frame) >= 2147483648.0 || cap / per_frame >= (1 << 30))
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: too many frames for one launch");
+  crattn::HsaPoolArgs a;
+  a.k = static_cast<const uint16_t *>(k_cache);
+  a.cap = cap;
+  a.per_frame = per_frame;
+  a.nbf = (per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK;
+  a.nf = (int)(cap / per_frame);
+  a.frames = static_cast<float *>(pool);
+  a.blocks = a.frames + (size_t)B * H * a.nf * D;
+  a.frame0 = (int)(row0 / per_frame);
+  a.n_frames = (int)(nrows / per_frame);
+  a.B = B;
+  a.H = H;
+  return hip_status(crattn::launch_hsa_pool(a, D, static_cast<hipStream_t>(stream)),
+                    "hsa_pool_keys launch");
+}
+
+int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int64_t q_pos0,
+               int64_t chunk_tokens, int kf, int kb, int32_t *sel, int B, int H, int D,
+               int64_t Lq, void *stream) {
+  if (q == nullptr || pool == nullptr || sel == nullptr)
+    return fail(CRATTN_EINVAL, "hsa_select: q, pool and sel are required");
+  if (!aligned16(q) || !aligned16(pool) || !aligned16(sel))
+    return fail(CRATTN_EINVAL, "hsa_select: pointers must be 16-byte aligned");
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "hsa_select: head_dim %d not supported (64 or 128)", D);
+  if (B < 1 || H < 1 || Lq < 1 || q_pos0 < 0 || chunk_tokens < 1 || per_frame < 1 || cap < 1)
+    return fail(CRATTN_EINVAL, "hsa_select: B, H, Lq, chunk_tokens, per_frame, cap >= 1 and "
+                               "q_pos0 >= 0 required");
+  if (chunk_tokens % per_frame != 0 || cap % per_frame != 0)
+    return fail(CRATTN_EINVAL, "hsa_select: chunk_tokens and cap must be whole frames");
+  if (q_pos0 > kMaxElems || Lq > kMaxElems || q_pos0 % chunk_tokens + Lq > chunk_tokens)
+    return fail(CRATTN_EINVAL, "hsa_select: the query rows must lie in one chunk");
+  const int64_t q_chunk = q_pos0 / chunk_tokens;
+  if ((q_chunk + 1) * chunk_tokens > cap)
+    return fail(CRATTN_EINVAL, "hsa_select: the query chunk ends past cap");
+  if (kf < 1 || kf > CRATTN_HSA_MAX_KF || kb < 1 || kb > CRATTN_HSA_MAX_KB)
+    return fail(CRATTN_EINVAL, "hsa_select: kf in [1, %d] and kb in [1, %d] required",
+                CRATTN_HSA_MAX_KF, CRATTN_HSA_MAX_KB);
+  const int64_t nbf = (per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK;
+  const int64_t n_hist = q_chunk * (chunk_tokens / per_frame);
+  if (n_hist > CRATTN_HSA_MAX_CAND || std::min<int64_t>(kf, n_hist) * nbf > CRATTN_HSA_MAX_CAND)
+    return fail(CRATTN_EINVAL, "hsa_select: %lld history frames, %lld block candidates: at most "
+                               "%d each", (long long)n_hist,
+                (long long)(std::min<int64_t>(kf, n_hist) * nbf), CRATTN_HSA_MAX_CAND);
+  if (hsa_pool_bytes(B, H, cap, D, per_frame) == 0)
+    return fail(CRATTN_EINVAL, "hsa_select: sizes too large");
+  const int64_t n_qblocks = (Lq + CRATTN_HSA_QBLOCK - 1) / CRATTN_HSA_QBLOCK;
+  if ((double)B * H * (double)n_qblocks >= 2147483648.0)
+    return fail(CRATTN_EINVAL, "hsa_select: too many query blocks for one launch");
+  crattn::HsaSelectArgs a;
+  a.q = static_cast<const uint16_t *>(q);
+  a.nf = (int)(cap / per_frame);
+  a.nbf = (int)nbf;
+  a.frames = static_cast<const float *>(pool);
+  a.blocks = a.frames + (size_t)B * H * a.nf * D;
+  a.sel = sel;
+  a.Lq = Lq;
+  a.n_hist = (int)n_hist;
+  a.kf = kf;
+  a.kb = kb;
+  a.n_qblocks = (int)n_qblocks;
+  a.B = B;
+  a.H = H;
+  return hip_status(crattn::launch_hsa_select(a, D, static_cast<hipStream_t>(stream)),
+                    "hsa_select launch");
+}
+
+int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap, int64_t q_pos0,
+             int64_t chunk_tokens, int per_frame, const int32_t *sel, int kb, void *out,
+             float *lse, int B, int H, int D, int64_t Lq, float scale, void *stream) {
+  const Sparse sp{sel, kb, per_frame};
+  if (chunk_tokens < 1 || q_pos0 < 0 || q_pos0 > kMaxElems)
+    return fail(CRATTN_EINVAL, "hsa_attn: chunk_tokens >= 1 and q_pos0 >= 0 required");
+  const int64_t kv_len = (q_pos0 / chunk_tokens + 1) * chunk_tokens;
+  return attn_call("hsa_attn", nullptr, &sp, q, k_cache, v_cache, cap, kv_len, q_pos0,
+                   chunk_tokens, out, lse, nullptr, 0, B, H, D, Lq, scale, stream);
 }
 
 const char *crattn_last_error(void) { return g_err; }

@@ -51,6 +51,7 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+constexpr int kMaxSelBlocks = CRATTN_HSA_MAX_KB;  // selected blocks per query tile
 
 struct AttnKArgs {
   const uint16_t *q;
@@ -69,6 +70,9 @@ struct AttnKArgs {
   const float2 *table;
   TabGeom tg;
   uint32_t per_frame, gw, t0, tok_off;
+  // block-sparse instance: per (b, h, query tile) kb selected key blocks
+  const int32_t *sel;
+  int kb, nbf, blk_frame, n_hist_blocks;
 };
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
@@ -157,7 +161,7 @@ struct Pitch {
   static constexpr int V = CPR + 4;
 };
 
-template <int D, int NW, int QB, int MINB, bool ROPE>
+template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE>
 __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   constexpr int kBN = 64;
   constexpr int DK = D / 16;    // k-steps of the QK product
@@ -232,7 +236,56 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   const int64_t q_chunk = a.q_pos0 / a.L + seg;
   // keys of one head fit 32-bit indices (the front end bounds cap * D)
   const int limit = (int)min(a.kv_len, (q_chunk + 1) * a.L);
-  const int nkt = (limit + kBN - 1) / kBN;
+  int nkt = (limit + kBN - 1) / kBN;
+
+  // ---- block-sparse key list: the tiles of the own chunk, then the
+  // selected history blocks as (first row, end row), compacted in list
+  // order.  Ids outside [0, n_hist_blocks) are dropped, so nothing outside
+  // the history is ever read and no tile is empty. ----
+  [[maybe_unused]] int own0 = 0, n_own = 0;
+  [[maybe_unused]] int2 *sp_tiles = nullptr;
+  if constexpr (SPARSE) {
+    __shared__ int2 sp_buf[kMaxSelBlocks];
+    __shared__ int sp_count[NW];
+    sp_tiles = sp_buf;
+    own0 = (int)(q_chunk * a.L);
+    n_own = (limit - own0 + kBN - 1) / kBN;
+    const int32_t *sl = a.sel + (((int64_t)b * a.H + h) * a.n_tiles + tile) * a.kb;
+    const int id = tid < a.kb ? sl[tid] : -1;
+    const bool v = id >= 0 && id < a.n_hist_blocks;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(v);
+    const int before = __builtin_popcountll(bal & ((uint64_t(1) << lane) - 1));
+    if (lane == 0) sp_count[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      off += w < wave ? sp_count[w] : 0;
+      tot += sp_count[w];
+    }
+    if (v) {
+      const int f = id / a.nbf, j = id - f * a.nbf;
+      const int start = f * a.blk_frame + j * kBN;
+      sp_buf[off + before] = make_int2(start, start + min(kBN, a.blk_frame - j * kBN));
+    }
+    __syncthreads();
+    nkt = n_own + tot;
+  }
+  // first key row and end of the visible range of tile kt (the visible
+  // rows of a tile are [key0, min(key0 + kBN, lim)))
+  auto tile_key0 = [&](int kt) -> int {
+    if constexpr (SPARSE)
+      return kt < n_own ? own0 + kt * kBN
+                        : __builtin_amdgcn_readfirstlane(sp_tiles[kt - n_own].x);
+    else
+      return kt * kBN;
+  };
+  auto tile_lim = [&](int kt) -> int {
+    if constexpr (SPARSE)
+      return kt < n_own ? limit : __builtin_amdgcn_readfirstlane(sp_tiles[kt - n_own].y);
+    else
+      return limit;
+  };
   const int kt_begin = split * nkt / a.splits;
   const int kt_end = (split + 1) * nkt / a.splits;
 
@@ -350,10 +403,11 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   auto dma = [&](int kt, int stage) {
     const uint32_t kdst = ring_lds + (uint32_t)stage * (STAGE_CELLS * 16);
     const uint32_t vdst = kdst + K_CELLS * 16;
-    const int key0 = kt * kBN;
+    const int key0 = tile_key0(kt);
+    const int lim = tile_lim(kt);
     const uint16_t *kb = kh + key0 * D;
     const uint16_t *vb = vh + key0 * D;
-    if (key0 + kBN <= limit) {
+    if (key0 + kBN <= lim) {
 #pragma unroll
       for (int n = 0; n < K_SLOTS; ++n) {
         const int j = wave + n * NW;
@@ -365,7 +419,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
         if ((n + 1) * NW <= V_INSTR || j < V_INSTR) lds_dma16_sv(vb, dma_v_off[n], vdst + j * 1024);
       }
     } else {
-      const int last = limit - 1 - key0;
+      const int last = lim - 1 - key0;
 #pragma unroll
       for (int n = 0; n < K_SLOTS; ++n) {
         const int j = wave + n * NW;
@@ -449,13 +503,15 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   };
   // ---- softmax, part 2 (branchy, after the tile's products): edge mask,
   // running max, lazy rescale of the row sums and of O ----
-  auto softmax_fix = [&](f32x16_t (&sc)[KB][QB], int key0, float (&mx)[QB]) {
-    if (key0 + kBN > limit) {
+  auto softmax_fix = [&](f32x16_t (&sc)[KB][QB], int kt, float (&mx)[QB]) {
+    const int key0 = tile_key0(kt);
+    const int lim = tile_lim(kt);
+    if (key0 + kBN > lim) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const bool dead = key0 + kb * 32 + acc_key(r, hf) >= limit;
+          const bool dead = key0 + kb * 32 + acc_key(r, hf) >= lim;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             if (dead) sc[kb][qb][r] = -INFINITY;
@@ -526,7 +582,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     qk(0, sbuf[0]);
     float mx[QB];
     row_max(sbuf[0], mx);
-    softmax_fix(sbuf[0], kt_begin * kBN, mx);
+    softmax_fix(sbuf[0], kt_begin, mx);
   }
 
   auto step = [&](int kt, auto P) {
@@ -624,7 +680,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       mx[qb] = half_swap_max(mp[qb]);
       l_run[qb] += rs[qb][0] + rs[qb][1];
     }
-    if (more) softmax_fix(nxt, (kt + 1) * kBN, mx);
+    if (more) softmax_fix(nxt, kt + 1, mx);
   };
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -727,9 +783,9 @@ FwdShape fwd_shape(int D) {
   return FwdShape{8, 1, 64};
 }
 
-template <int D, int NW, int QB, int MINB, bool ROPE>
+template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE>
 hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB, ROPE>), dim3((unsigned)grid), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB, ROPE, SPARSE>), dim3((unsigned)grid), dim3(NW * 64), 0,
                      s, k);
   return hipGetLastError();
 }
@@ -819,13 +875,20 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
     k.t0 = (uint32_t)a.t0;
     k.tok_off = (uint32_t)a.tok_off;
   }
+  k.sel = a.sel;
+  k.kb = a.sel_kb;
+  k.nbf = a.sel_nbf;
+  k.blk_frame = a.sel_per_frame;
+  k.n_hist_blocks = a.sel_n_hist_blocks;
   hipError_t e;
   if (a.D == 128)
-    e = a.rope ? launch_fwd<128, 8, 1, 1, true>(k, p.grid, s)
-               : launch_fwd<128, 8, 1, 1, false>(k, p.grid, s);
+    e = a.sel != nullptr ? launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s)
+        : a.rope         ? launch_fwd<128, 8, 1, 1, true, false>(k, p.grid, s)
+                         : launch_fwd<128, 8, 1, 1, false, false>(k, p.grid, s);
   else
-    e = a.rope ? launch_fwd<64, 8, 1, 1, true>(k, p.grid, s)
-               : launch_fwd<64, 8, 1, 1, false>(k, p.grid, s);
+    e = a.sel != nullptr ? launch_fwd<64, 8, 1, 1, false, true>(k, p.grid, s)
+        : a.rope         ? launch_fwd<64, 8, 1, 1, true, false>(k, p.grid, s)
+                         : launch_fwd<64, 8, 1, 1, false, false>(k, p.grid, s);
   if (e != hipSuccess || p.splits == 1) return e;
   CombineArgs c;
   c.ws_o = k.ws_o;

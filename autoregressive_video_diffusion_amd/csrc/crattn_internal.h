@@ -74,6 +74,32 @@ struct AttnArgs {
   int max_t, max_h, max_w;
   int64_t t0, tok_off;
   int grid_h, grid_w;
+  // block-sparse attention (hsa_attn): selected block ids per query tile
+  const int32_t *sel;
+  int sel_kb, sel_nbf, sel_per_frame, sel_n_hist_blocks;
+};
+
+// Key pooling of whole frames [frame0, frame0 + n_frames) of the cache.
+struct HsaPoolArgs {
+  const uint16_t *k;  // [B][H][cap][D] bf16
+  float *frames;      // [B][H][nf][D]
+  float *blocks;      // [B][H][nf * nbf][D]
+  int64_t cap;
+  int per_frame, nbf, nf;
+  int frame0, n_frames;
+  int B, H;
+};
+
+// Two-level selection of each (b, h, query block).
+struct HsaSelectArgs {
+  const uint16_t *q;     // [B][Lq][H][D] bf16, rotated
+  const float *frames;   // pooled keys (HsaPoolArgs layout)
+  const float *blocks;
+  int32_t *sel;          // [B][H][n_qblocks][kb]
+  int64_t Lq;
+  int nf, nbf, n_hist;   // history = frames [0, n_hist)
+  int kf, kb, n_qblocks;
+  int B, H;
 };
 
 // Launch plan of one attention call: how query rows are tiled and how the
@@ -101,5 +127,7 @@ hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t s);
 hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
 hipError_t launch_qkv_rope(const QkvArgs &a, hipStream_t s);
+hipError_t launch_hsa_pool(const HsaPoolArgs &a, int D, hipStream_t s);
+hipError_t launch_hsa_select(const HsaSelectArgs &a, int D, hipStream_t s);
 
 }  // namespace crattn

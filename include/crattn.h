@@ -71,6 +71,15 @@ extern "C" {
 /* Largest head_dim any entry point accepts. */
 #define CRATTN_MAX_HEAD_DIM 256
 
+/* Hierarchical block-sparse attention: key blocks of 64 tokens inside a
+ * frame, query blocks of 256 rows of a call, at most 512 selected blocks
+ * and 64 selected frames per query block, at most 4096 block candidates. */
+#define CRATTN_HSA_KBLOCK 64
+#define CRATTN_HSA_QBLOCK 256
+#define CRATTN_HSA_MAX_KB 512
+#define CRATTN_HSA_MAX_KF 64
+#define CRATTN_HSA_MAX_CAND 4096
+
 /*
  * Size in bytes of the cos/sin table for head_dim D and position extents
  * (max_t, max_h, max_w): 8 * (max_t*D_t/2 + max_h*D_h/2 + max_w*D_w/2).
@@ -251,6 +260,86 @@ int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max
                            int64_t chunk_tokens, void *out, float *lse, void *workspace,
                            size_t ws_bytes, int B, int H, int D, int64_t Lq, float scale,
                            void *stream);
+
+/*
+ * Hierarchical block-sparse attention (HSA) ["LIGHT FORCING" §2.2]: queries
+ * and keys are compressed by mean pooling at block and frame level; each
+ * query block picks a few history frames with the frame-level keys, then
+ * the best blocks inside those frames with the block-level keys; attention
+ * runs over the query's own chunk plus the selected blocks, so its cost
+ * stays constant as the history grows.
+ *
+ * Geometry.  The cache holds whole frames of per_frame tokens in raster
+ * order (row r is in frame r / per_frame).  Key block j of frame f covers
+ * rows f*per_frame + 64 j .. min(+64, (f+1)*per_frame); its global id is
+ * f * nbf + j with nbf = ceil(per_frame / 64).  Query block i of a call is
+ * rows 256 i .. min(256 i + 256, Lq).  History = the frames before the
+ * query's chunk; the own chunk is always attended in full.
+ *
+ * Pooled keys ("pool"): device float [B][H][nf][D] frame means followed by
+ * [B][H][nf * nbf][D] block means, nf = cap / per_frame;
+ * hsa_pool_bytes(...) bytes (0 for invalid arguments).
+ */
+size_t hsa_pool_bytes(int B, int H, int64_t cap, int D, int per_frame);
+
+/*
+ * Mean-pool the keys of cache rows [row0, row0 + nrows) (whole frames: both
+ * multiples of per_frame) into the frame and block means of `pool`; call
+ * once per chunk after its keys are appended.  Sums in fp32 in a fixed order.
+ *
+ * Errors: EINVAL for NULL or misaligned pointers, B, H, per_frame < 1,
+ * cap not a whole number of frames, a row range that is not whole frames or
+ * leaves [0, cap); ENOTSUP for D other than 64 or 128; EHIP.
+ */
+int hsa_pool_keys(const void *k_cache, int64_t cap, int64_t row0, int64_t nrows,
+                  int per_frame, void *pool, int B, int H, int D, void *stream);
+
+/*
+ * Two-level selection for each (b, h, query block).
+ *
+ *   q        device bf16 [B][Lq][H][D]: the rotated queries of the call (all
+ *            rows in one chunk: (q_pos0 mod chunk_tokens) + Lq <= chunk_tokens).
+ *   pool     pooled keys of the history (hsa_pool_keys).
+ *   kf, kb   frames and blocks kept (1 <= kf <= 64, 1 <= kb <= 512; at most
+ *            4096 block candidates: min(kf, history frames) * nbf).
+ *   sel      device int32 [B][H][ceil(Lq/256)][kb]: the kept block ids in
+ *            ascending order, then -1 for the places left when the kept
+ *            frames hold fewer than kb blocks (all -1 with no history).
+ *
+ * Arithmetic: the query block's mean and the dot products with the pooled
+ * keys in fp32; the k largest scores are kept, equal scores by the lower
+ * index first.
+ *
+ * Errors: EINVAL for NULL or misaligned pointers, B, H, Lq < 1, q_pos0 < 0,
+ * chunk_tokens or per_frame < 1, chunk_tokens or cap not whole frames, query
+ * rows that leave their chunk, a query chunk that ends past cap, kf or kb
+ * outside the limits, too many candidates; ENOTSUP for D not 64 or 128; EHIP.
+ */
+int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int64_t q_pos0,
+               int64_t chunk_tokens, int kf, int kb, int32_t *sel, int B, int H, int D,
+               int64_t Lq, void *stream);
+
+/*
+ * Attention over the own chunk plus the selected blocks.
+ *
+ *   q, k_cache, v_cache, out, lse, scale  as for chunk_causal_attn (q
+ *            rotated; all rows in one chunk).  The own chunk is rows
+ *            [c*chunk_tokens, (c+1)*chunk_tokens) with c = q_pos0 / chunk_tokens.
+ *   sel, kb  the selection (hsa_select's layout).  The ids of a row are used
+ *            up to the end of the row; ids outside the history (negative or
+ *            >= the history's block count) are skipped.
+ *
+ * Arithmetic: chunk_causal_attn's, over the visible rows in list order (own
+ * chunk first).  Selecting every history block gives the dense result up to
+ * summation order.
+ *
+ * Errors: those of chunk_causal_attn (with kv_len = the own chunk's end),
+ * and EINVAL for a NULL or misaligned sel, kb outside [1, 512], per_frame < 1,
+ * chunk_tokens or cap not whole frames, query rows that leave their chunk.
+ */
+int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
+             int64_t q_pos0, int64_t chunk_tokens, int per_frame, const int32_t *sel, int kb,
+             void *out, float *lse, int B, int H, int D, int64_t Lq, float scale, void *stream);
 
 /* Message describing the last non-zero return on this thread ("" if none). */
 const char *crattn_last_error(void);

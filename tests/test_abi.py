@@ -160,3 +160,66 @@ def test_rope_precompute_rejects():
     assert lib.rope_precompute(FAKE, 64, 0, 8, 8, 10000.0, None) == 1
     assert lib.rope_precompute(FAKE, 64, 4, 8, 8, 1.0, None) == 1
     assert lib.rope_precompute(MIS, 64, 4, 8, 8, 10000.0, None) == 1
+
+
+def test_hsa_pool_bytes():
+    # 480P: 21 frames of 1560 tokens, 25 blocks each, head_dim 128, 12 heads
+    assert crattn.hsa_pool_bytes(1, 12, 32760, 128, 1560) == 12 * (21 + 21 * 25) * 128 * 4
+    assert crattn.hsa_pool_bytes(1, 12, 32761, 128, 1560) == 0   # not whole frames
+    assert crattn.hsa_pool_bytes(1, 12, 32760, 96, 1560) == 0
+    assert crattn.hsa_pool_bytes(0, 12, 32760, 128, 1560) == 0
+
+
+def _pool(**kw):
+    a = dict(k=FAKE, cap=256, row0=192, nrows=64, pf=64, pool=FAKE, B=1, H=2, D=64)
+    a.update(kw)
+    return _lib().hsa_pool_keys(a["k"], a["cap"], a["row0"], a["nrows"], a["pf"], a["pool"],
+                                a["B"], a["H"], a["D"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(pool=MIS), 1), (dict(D=96), 2), (dict(pf=0), 1),
+    (dict(cap=250), 1), (dict(row0=100), 1), (dict(nrows=70), 1), (dict(row0=256), 1),
+    (dict(row0=192, nrows=128), 1), (dict(B=0), 1),
+])
+def test_hsa_pool_keys_rejects(kw, code):
+    assert _pool(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def _select(**kw):
+    a = dict(q=FAKE, pool=FAKE, cap=256, pf=64, pos0=192, L=64, kf=2, kb=4, sel=FAKE, B=1, H=2,
+             D=64, Lq=64)
+    a.update(kw)
+    return _lib().hsa_select(a["q"], a["pool"], a["cap"], a["pf"], a["pos0"], a["L"], a["kf"],
+                             a["kb"], a["sel"], a["B"], a["H"], a["D"], a["Lq"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(sel=MIS), 1), (dict(D=32), 2), (dict(kf=0), 1), (dict(kf=65), 1),
+    (dict(kb=0), 1), (dict(kb=513), 1), (dict(pos0=200), 1), (dict(L=96), 1),
+    (dict(pos0=256), 1), (dict(Lq=0), 1),
+    # 4097 history frames exceed the candidate limit
+    (dict(cap=64 * 4098, pos0=64 * 4097, kf=1), 1),
+])
+def test_hsa_select_rejects(kw, code):
+    assert _select(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def _hsa_attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, pos0=192, L=64, pf=64, sel=FAKE, kb=4, out=FAKE,
+             lse=None, B=1, H=2, D=64, Lq=64, scale=0.0)
+    a.update(kw)
+    return _lib().hsa_attn(a["q"], a["k"], a["v"], a["cap"], a["pos0"], a["L"], a["pf"], a["sel"],
+                           a["kb"], a["out"], a["lse"], a["B"], a["H"], a["D"], a["Lq"], a["scale"],
+                           None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sel=None), 1), (dict(sel=MIS), 1), (dict(kb=0), 1), (dict(kb=513), 1), (dict(pf=0), 1),
+    (dict(pf=48), 1), (dict(pos0=200), 1), (dict(D=96), 2), (dict(cap=200), 1), (dict(q=None), 1),
+])
+def test_hsa_attn_rejects(kw, code):
+    assert _hsa_attn(**kw) == code
+    assert crattn.crattn_last_error() != ""

@@ -1,0 +1,234 @@
+"""GPU parity of the hierarchical block-sparse attention (HSA) path against
+the fp64 oracle (oracle/hsa.py).
+
+* Pooling: every frame and block mean within the fp32 summation bound
+  (n + 1) * 2^-24 * mean|x| of its n rows.
+* Selection: a float decides an integer here, so the GPU's choice (fp32) is
+  checked for validity against the exact fp64 scores: its blocks come from
+  at most kf frames that are a top-kf set within the fp32 score bound, the
+  blocks are a top-kb set of those frames' blocks within the bound, the ids
+  ascend, and -1 pads the rest.  Where the exact scores separate the sets by
+  more than the bound, the choice must equal the oracle's.
+* Attention: given the GPU's selection (unique output), every compared row
+  within the bf16 attention bar (max-abs 2e-2, relative L2 5e-3) of the
+  oracle's attention over the own chunk plus those blocks.
+* Keys outside the selection are never read: NaN there leaves the output
+  bit-identical; invalid ids in the list are skipped.
+"""
+import numpy as np
+import pytest
+import torch
+
+import autoregressive_video_diffusion_amd as crattn
+import oracle
+from gpu_helpers import assert_attn_close, dev, f64
+from oracle import hsa
+from workloads import STEP480, normal
+
+pytestmark = pytest.mark.gpu
+EPS = 2.0 ** -24
+
+
+def _inputs(B, H, D, per_frame, F_c, chunks, Lq, q_off, seed):
+    L = F_c * per_frame
+    cap = chunks * L
+    q = normal((B, Lq, H, D), seed).to(dev())
+    kc = normal((B, H, cap, D), seed + 1).to(dev())
+    vc = normal((B, H, cap, D), seed + 2).to(dev())
+    return q, kc, vc, L, cap, (chunks - 1) * L + q_off
+
+
+def _pool(kc, per_frame):
+    B, H, cap, D = kc.shape
+    nbytes = crattn.hsa_pool_bytes(B, H, cap, D, per_frame)
+    pool = torch.empty(nbytes // 4, dtype=torch.float32, device=dev())
+    crattn.hsa_pool_keys(kc, 0, cap, per_frame, pool)
+    torch.cuda.synchronize()
+    nf, nbf = cap // per_frame, hsa.blocks_per_frame(per_frame)
+    fr = pool[:B * H * nf * D].view(B, H, nf, D)
+    bl = pool[B * H * nf * D:B * H * (nf + nf * nbf) * D].view(B, H, nf * nbf, D)
+    return pool, f64(fr), f64(bl)
+
+
+def _select(q, pool, cap, per_frame, q_pos0, L, kf, kb):
+    B, Lq, H, D = q.shape
+    sel = torch.empty(B, H, -(-Lq // 256), kb, dtype=torch.int32, device=dev())
+    crattn.hsa_select(q, pool, cap, per_frame, q_pos0, L, kf, kb, sel)
+    torch.cuda.synchronize()
+    return sel
+
+
+def _hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel):
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=dev())
+    crattn.hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _check_pool(kc, per_frame, fr, bl):
+    k = f64(kc)
+    ef, eb = hsa.pool_keys(k, per_frame)
+    af, ab = hsa.pool_keys(np.abs(k), per_frame)
+    nbf = hsa.blocks_per_frame(per_frame)
+    n_b = np.array([np.subtract(*hsa.block_range(j, per_frame)[::-1]) for j in range(nbf)])
+    n_b = np.tile(n_b, eb.shape[2] // nbf)[None, None, :, None]
+    assert np.all(np.abs(bl - eb) <= (n_b + 1) * EPS * ab + 1e-30)
+    assert np.all(np.abs(fr - ef) <= (per_frame + 1) * EPS * af + 1e-30)
+
+
+def _score_bound(qbar_abs, k_abs, qbar, kbar, n_q, n_k, D):
+    """First-order bound of the fp32 pooled dot product's error: the
+    query mean's and key mean's summation errors and the D-term dot."""
+    return (n_q + 1) * EPS * (qbar_abs * np.abs(kbar)).sum(-1) + \
+        (n_k + 1) * EPS * (np.abs(qbar) * k_abs).sum(-1) + \
+        (D + 2) * EPS * (np.abs(qbar) * np.abs(kbar)).sum(-1)
+
+
+def _check_selection(q, kc, per_frame, L, q_pos0, kf, kb, sel):
+    """Validity of the GPU selection against exact scores; returns the number
+    of query blocks whose choice had to match the oracle exactly."""
+    qe, ke = f64(q), f64(kc)
+    B, Lq, H, D = qe.shape
+    nbf = hsa.blocks_per_frame(per_frame)
+    n_hist = (q_pos0 // L) * (L // per_frame)
+    ef, eb = hsa.pool_keys(ke, per_frame)
+    af, ab = hsa.pool_keys(np.abs(ke), per_frame)
+    qp, qa = hsa.pool_queries(qe), hsa.pool_queries(np.abs(qe))
+    ref = hsa.select(qe, ef, eb, n_hist, per_frame, kf, kb)
+    s = sel.cpu().numpy()
+    exact = 0
+    for b in range(B):
+        for h in range(H):
+            for i in range(qp.shape[2]):
+                got = s[b, h, i]
+                n_q = min(256, Lq - 256 * i)
+                n_valid = int((got >= 0).sum())
+                assert (got[:n_valid] >= 0).all() and (got[n_valid:] == -1).all()
+                assert np.all(np.diff(got[:n_valid]) > 0)
+                n_cand = min(kf, n_hist) * nbf
+                assert n_valid == min(kb, n_cand)
+                if n_hist == 0:
+                    continue
+                fs = ef[b, h, :n_hist] @ qp[b, h, i]
+                ftol = _score_bound(qa[b, h, i], af[b, h, :n_hist], qp[b, h, i],
+                                    ef[b, h, :n_hist], n_q, per_frame, D)
+                frames = np.unique(got[:n_valid] // nbf)
+                assert len(frames) <= kf
+                # the frames the blocks came from must be a top-kf set up to
+                # the bound (a block-empty kept frame cannot be seen, so only
+                # the visible ones are checked)
+                kth = np.sort(fs)[::-1][min(kf, n_hist) - 1]
+                assert np.all(fs[frames] >= kth - ftol[frames] - ftol.max())
+                bs = eb[b, h, got[:n_valid]] @ qp[b, h, i]
+                cand = np.concatenate([np.arange(f * nbf, (f + 1) * nbf) for f in frames])
+                cs = eb[b, h, cand] @ qp[b, h, i]
+                btol = _score_bound(qa[b, h, i], ab[b, h, cand], qp[b, h, i], eb[b, h, cand],
+                                    n_q, 64, D).max()
+                unchosen = np.setdiff1d(cand, got[:n_valid])
+                if len(unchosen):
+                    best_out = (eb[b, h, unchosen] @ qp[b, h, i]).max()
+                    assert bs.min() >= best_out - 2 * btol
+                # unique where the exact scores are well separated
+                srt = np.sort(fs)[::-1]
+                f_sep = n_hist <= kf or srt[kf - 1] - srt[kf] > 4 * ftol.max()
+                all_b = np.concatenate([np.arange(f * nbf, (f + 1) * nbf)
+                                        for f in hsa.topk(fs, kf)])
+                bsr = np.sort(eb[b, h, all_b] @ qp[b, h, i])[::-1]
+                b_sep = len(bsr) <= kb or bsr[kb - 1] - bsr[kb] > 4 * btol
+                if f_sep and b_sep:
+                    assert np.array_equal(got, ref[b, h, i]), (b, h, i)
+                    exact += 1
+    return exact
+
+
+@pytest.mark.parametrize("B,H,D,gh,gw,F_c,chunks,Lq,q_off,kf,kb", [
+    (1, 2, 64, 8, 8, 1, 4, 64, 0, 2, 3),          # tiny geometry: one block per frame
+    (2, 2, 128, 10, 10, 2, 4, 200, 0, 3, 5),      # 100-token frames: blocks of 64 + 36
+    (1, 3, 128, 12, 20, 1, 6, 240, 0, 4, 12),     # 240-token frames, 4 blocks each
+    (1, 2, 64, 9, 9, 2, 3, 100, 62, 2, 64),       # a slice; kb above the candidates: -1 pads
+])
+def test_small_configs_every_row(B, H, D, gh, gw, F_c, chunks, Lq, q_off, kf, kb):
+    per_frame = gh * gw
+    q, kc, vc, L, cap, q_pos0 = _inputs(B, H, D, per_frame, F_c, chunks, Lq, q_off, 31 + D)
+    pool, fr, bl = _pool(kc, per_frame)
+    _check_pool(kc, per_frame, fr, bl)
+    sel = _select(q, pool, cap, per_frame, q_pos0, L, kf, kb)
+    _check_selection(q, kc, per_frame, L, q_pos0, kf, kb, sel)
+    out, lse = _hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel)
+    s64 = sel.cpu().numpy().astype(np.int64)
+    own0 = (q_pos0 // L) * L
+    o_ref, lse_ref = hsa.attn(f64(q), f64(kc), f64(vc), s64, own0, own0 + L, per_frame)
+    assert_attn_close(f64(out), o_ref, "hsa small")
+    np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
+
+
+def test_selecting_everything_matches_dense_attention():
+    B, H, D, per_frame, F_c, chunks, Lq = 1, 2, 128, 100, 2, 5, 200
+    q, kc, vc, L, cap, q_pos0 = _inputs(B, H, D, per_frame, F_c, chunks, Lq, 0, 77)
+    pool, _, _ = _pool(kc, per_frame)
+    n_hist = (chunks - 1) * F_c
+    kb = n_hist * hsa.blocks_per_frame(per_frame)
+    sel = _select(q, pool, cap, per_frame, q_pos0, L, n_hist, kb)
+    assert (sel >= 0).all()
+    out, lse = _hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel)
+    dense = torch.empty_like(q)
+    dlse = torch.empty_like(lse)
+    crattn.chunk_causal_attn(q, kc, vc, cap, q_pos0, L, dense, dlse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn(f64(q), f64(kc), f64(vc), cap, q_pos0, L)
+    assert_attn_close(f64(out), o_ref, "hsa, everything selected")
+    assert_attn_close(f64(dense), o_ref, "dense")
+    np.testing.assert_allclose(f64(lse), f64(dlse), atol=1e-3)
+
+
+def test_unselected_keys_are_never_read_and_bad_ids_are_skipped():
+    B, H, D, per_frame, F_c, chunks, Lq = 1, 2, 128, 130, 1, 6, 130
+    q, kc, vc, L, cap, q_pos0 = _inputs(B, H, D, per_frame, F_c, chunks, Lq, 0, 91)
+    pool, _, _ = _pool(kc, per_frame)
+    sel = _select(q, pool, cap, per_frame, q_pos0, L, 2, 3)
+    out, lse = _hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel)
+    s = sel.cpu().numpy()
+    kc2, vc2 = kc.clone(), vc.clone()
+    for b in range(B):
+        for h in range(H):
+            keep = hsa.visible_keys(s[b, h, 0].astype(np.int64), q_pos0, q_pos0 + L, per_frame)
+            drop = torch.tensor(np.setdiff1d(np.arange(cap), keep), device=dev())
+            kc2[b, h, drop] = float("nan")
+            vc2[b, h, drop] = float("nan")
+    out2, lse2 = _hsa_attn(q, kc2, vc2, q_pos0, L, per_frame, sel)
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # ids that are negative or outside the history are skipped: append junk
+    nbf = hsa.blocks_per_frame(per_frame)
+    n_hist_blocks = (chunks - 1) * nbf
+    junk = torch.tensor([-5, n_hist_blocks, n_hist_blocks + 7, 1 << 30], dtype=torch.int32,
+                        device=dev())
+    sel_j = torch.cat([sel, junk.expand(B, H, sel.shape[2], 4)], dim=3).contiguous()
+    out3, lse3 = _hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel_j)
+    assert torch.equal(out, out3) and torch.equal(lse, lse3)
+
+
+def test_480p_chunk_sampled_rows():
+    # the 1.3B-shape chunk at t0 18: 4680 queries, 12 heads, 7-chunk cache,
+    # 6 of 18 history frames, 32 blocks of 64 keys kept per query block
+    w = STEP480
+    per_frame, L, cap = w.grid_h * w.grid_w, w.chunk_tokens, w.cap
+    q = normal((1, w.lq, w.H, w.D), 4801).to(dev())
+    kc = normal((1, w.H, cap, w.D), 4802).to(dev())
+    vc = normal((1, w.H, cap, w.D), 4803).to(dev())
+    pool, fr, bl = _pool(kc, per_frame)
+    _check_pool(kc, per_frame, fr, bl)
+    sel = _select(q, pool, cap, per_frame, w.q_pos0, L, 6, 32)
+    exact = _check_selection(q, kc, per_frame, L, w.q_pos0, 6, 32, sel)
+    total = sel.shape[1] * sel.shape[2]
+    print(f"  480P: {exact} of {total} query blocks matched exactly", flush=True)
+    # with N(0, 1) data the exact scores are almost always far apart
+    # compared with the fp32 bound, so nearly every choice is unique
+    assert exact >= 0.9 * total
+    out, lse = _hsa_attn(q, kc, vc, w.q_pos0, L, per_frame, sel)
+    rows = np.unique(np.concatenate([np.arange(0, w.lq, 97), [w.lq - 1, 255, 256, 4607, 4608]]))
+    s64 = sel.cpu().numpy().astype(np.int64)
+    o_ref, lse_ref = hsa.attn(f64(q), f64(kc), f64(vc), s64, w.q_pos0, w.q_pos0 + L, per_frame,
+                              rows=rows)
+    assert_attn_close(f64(out)[:, rows], o_ref, "hsa 480P")
+    np.testing.assert_allclose(f64(lse)[:, :, rows], lse_ref, atol=2e-3)
