@@ -187,6 +187,53 @@ def time_qkv(crattn, w, dev, table, ext, burst=20, bursts=5):
     return burst_ms(call, bursts, burst)
 
 
+def time_hsa(crattn, w, b, kf=6, kb=32):
+    """Hierarchical block-sparse attention on the step's chunk (rotated Q' and
+    the 7-chunk cache of buffer set b): per-launch times of the key pooling
+    of one appended chunk, of the selection (kf frames, kb blocks per
+    256-row query block) and of the sparse attention; FLOPs counted over the
+    keys each query block attends (own chunk + selected blocks)."""
+    import torch
+
+    per_frame = w.grid_h * w.grid_w
+    L = w.chunk_tokens
+    pool = torch.empty(crattn.hsa_pool_bytes(w.B, w.H, w.cap, w.D, per_frame) // 4,
+                       dtype=torch.float32, device=b.q_out.device)
+    crattn.hsa_pool_keys(b.kc, 0, w.cap, per_frame, pool)
+    nqb = -(-w.lq // crattn.HSA_QBLOCK)
+    sel = torch.empty(w.B, w.H, nqb, kb, dtype=torch.int32, device=pool.device)
+    own0 = (w.q_pos0 // L) * L
+
+    def pool_call(i):
+        crattn.hsa_pool_keys(b.kc, own0, L, per_frame, pool)
+
+    def select_call(i):
+        crattn.hsa_select(b.q_out, pool, w.cap, per_frame, w.q_pos0, L, kf, kb, sel)
+
+    def attn_call(i):
+        crattn.hsa_attn(b.q_out, b.kc, b.vc, w.q_pos0, L, per_frame, sel, b.out, b.lse)
+
+    for f in (pool_call, select_call, attn_call):
+        for i in range(3):
+            f(i)
+    torch.cuda.synchronize()
+    pool_ms = burst_ms(pool_call, 5, 20)[2]
+    sel_ms = burst_ms(select_call, 5, 20)[2]
+    attn_ms = burst_ms(attn_call, 5, 10)[2]
+    # visible keys of each query block: the own chunk plus its blocks
+    s = sel.cpu()
+    nbf = -(-per_frame // crattn.HSA_KBLOCK)
+    fl = 0
+    for i in range(nqb):
+        rows = min(crattn.HSA_QBLOCK, w.lq - i * crattn.HSA_QBLOCK)
+        for h in range(w.H):
+            ids = [int(x) for x in s[0, h, i] if int(x) >= 0]
+            keys = L + sum(min(crattn.HSA_KBLOCK, per_frame - (x % nbf) * crattn.HSA_KBLOCK)
+                           for x in ids)
+            fl += 4 * rows * keys * w.D
+    return pool_ms, sel_ms, attn_ms, fl
+
+
 def fused_step_ms(crattn, w, sets, table, ext, ws, reps=10, rounds=3):
     """The step with the query rotation folded into attention (the
     RoPE/append pass writes only K' and V, then chunk_causal_attn_rope
@@ -386,6 +433,16 @@ def main():
         extras["sp480_attn_tflops"] = round(
             attn_flops(1, SP480.H, SP480.lq, SP480.kv_len, SP480.D)
             / (extras["sp480_attn_ms"] * 1e-3) / 1e12, 1)
+        hp_ms, hs_ms, ha_ms, h_fl = time_hsa(crattn, w, sets[0])
+        h_tf = h_fl / (ha_ms * 1e-3) / 1e12
+        extras["hsa480"] = {
+            "kf": 6, "kb": 32, "pool_chunk_us": round(hp_ms * 1e3, 2),
+            "select_us": round(hs_ms * 1e3, 2), "attn_ms": round(ha_ms, 4),
+            "visible_flops": h_fl, "attn_tflops": round(h_tf, 1),
+            "speedup_vs_dense_attn": round(attn_ms / ha_ms, 2),
+            "select_overhead_pct": round(100 * hs_ms / ha_ms, 2),
+            "roofline": {"bound": "mfma", "achieved": round(h_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(h_tf / PEAK_BF16_TFLOPS, 4)}}
         plain_ms, fused_ms = fused_step_ms(crattn, w, sets, table, ext, ws)
         extras["step_plain_vs_fused_qrot_ms"] = [round(plain_ms, 4), round(fused_ms, 4)]
         extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)
