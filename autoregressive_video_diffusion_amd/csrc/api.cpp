@@ -420,7 +420,10 @@ int hsa_pool_keys(const void *k_cache, int64_t cap, int64_t row0, int64_t nrows,
                 (long long)cap);
   if (hsa_pool_bytes(B, H, cap, D, per_frame) == 0 || (double)B * H * (double)cap * D > (double)kMaxElems)
     return fail(CRATTN_EINVAL, "hsa_pool_keys: sizes too large");
-  if ((double)B * H * (double)(nrows / per_frame) >= 2147483648.0 || cap / per_frame >= (1 << 30))
+  if ((double)B * H * (double)(nrows / per_frame) *
+              (double)((per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK) >=
+          2147483648.0 ||
+      cap / per_frame >= (1 << 30))
     return fail(CRATTN_EINVAL, "hsa_pool_keys: too many frames for one launch");
   crattn::HsaPoolArgs a;
   a.k = static_cast<const uint16_t *>(k_cache);

@@ -7,10 +7,12 @@
 // a few history frames are chosen with the frame-level keys, then the
 // critical blocks inside them with the block-level keys.
 //
-// Both kernels are small next to the attention: the pooling reads each
-// chunk's keys once when the chunk is appended (HBM-bound), the selection
-// reads one query block and the pooled history keys per workgroup.
+// Both are small next to the attention: the pooling reads each chunk's keys
+// once when the chunk is appended (HBM-bound, one workgroup per 64-key
+// block), the selection reads one query block and the pooled history keys
+// per workgroup.
 #include "crattn_internal.h"
+#include <math.h>
 #include "../../include/crattn.h"
 
 namespace crattn {
@@ -28,43 +30,52 @@ __device__ inline void add_bf16x8(float (&acc)[8], const uint4 &x) {
   }
 }
 
-// ---- key pooling: one workgroup per (b, h, frame) ----
+// ---- key pooling, pass 1: one workgroup per (b, h, block) ----
 // Thread t reads 16-byte chunk t % (D/8) of rows t / (D/8), t / (D/8) + RG,
-// ...: RG rows of a block at a time.  Each block's per-thread partial sums
-// meet in LDS and are added in row-group order, so the result is the same
-// on every run.  The frame sum is the sum of its block sums in block order.
+// ...  of the block; the per-thread partial sums meet in LDS and are added
+// in row-group order, so the result is the same on every run.
 template <int D>
-__global__ void __launch_bounds__(256) hsa_pool_kernel(HsaPoolArgs a) {
+__global__ void __launch_bounds__(256) hsa_pool_blocks_kernel(HsaPoolArgs a) {
   constexpr int CPR = D / 8;
   constexpr int RG = 256 / CPR;
   __shared__ float part[RG][D];
   const int tid = threadIdx.x;
   const int c = tid % CPR, g = tid / CPR;
+  const int nb = a.n_frames * a.nbf;  // blocks of the pooled range
+  const int bi = (int)(blockIdx.x % (uint32_t)nb);
+  const int bh = (int)(blockIdx.x / (uint32_t)nb);
+  const int f = a.frame0 + bi / a.nbf, j = bi % a.nbf;
+  const int rs = j * kKB, re = min(rs + kKB, a.per_frame);
+  const uint16_t *kr = a.k + ((int64_t)bh * a.cap + (int64_t)f * a.per_frame) * D + c * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = rs + g; r < re; r += RG)
+    add_bf16x8(acc, *reinterpret_cast<const uint4 *>(kr + (int64_t)r * D));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[g][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < RG; ++k) s += part[k][tid];
+    a.blocks[((int64_t)bh * a.nf * a.nbf + (int64_t)f * a.nbf + j) * D + tid] =
+        s / (float)(re - rs);
+  }
+}
+
+// ---- key pooling, pass 2: frame means from the block means, one
+// workgroup of D threads per (b, h, frame): the length-weighted mean of the
+// frame's block means, added in block order ----
+template <int D>
+__global__ void __launch_bounds__(D) hsa_pool_frames_kernel(HsaPoolArgs a) {
   const int fi = (int)(blockIdx.x % (uint32_t)a.n_frames);
   const int bh = (int)(blockIdx.x / (uint32_t)a.n_frames);
   const int f = a.frame0 + fi;
-  const uint16_t *kr = a.k + ((int64_t)bh * a.cap + (int64_t)f * a.per_frame) * D + c * 8;
-  float *fmean = a.frames + ((int64_t)bh * a.nf + f) * D;
-  float *bmean = a.blocks + ((int64_t)bh * a.nf * a.nbf + (int64_t)f * a.nbf) * D;
-  float fsum = 0.f;
-  for (int j = 0; j < a.nbf; ++j) {
-    const int rs = j * kKB, re = min(rs + kKB, a.per_frame);
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int r = rs + g; r < re; r += RG)
-      add_bf16x8(acc, *reinterpret_cast<const uint4 *>(kr + (int64_t)r * D));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) part[g][c * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < D) {
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < RG; ++k) s += part[k][tid];
-      bmean[(int64_t)j * D + tid] = s / (float)(re - rs);
-      fsum += s;
-    }
-    __syncthreads();
-  }
-  if (tid < D) fmean[tid] = fsum / (float)a.per_frame;
+  const float *bm = a.blocks + ((int64_t)bh * a.nf * a.nbf + (int64_t)f * a.nbf) * D;
+  float s = 0.f;
+#pragma unroll 16
+  for (int j = 0; j < a.nbf; ++j)
+    s += bm[(int64_t)j * D + threadIdx.x] * (float)(min(kKB, a.per_frame - j * kKB));
+  a.frames[((int64_t)bh * a.nf + f) * D + threadIdx.x] = s / (float)a.per_frame;
 }
 
 // ---- selection: one workgroup per (b, h, query block) ----
@@ -74,8 +85,9 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
   constexpr int RG = 256 / CPR;
   __shared__ float part[RG][D];
   __shared__ float qbar[D];
-  __shared__ float score[CRATTN_HSA_MAX_CAND];
-  __shared__ unsigned char keep[CRATTN_HSA_MAX_CAND];
+  __shared__ float4 score4[CRATTN_HSA_MAX_CAND / 4 + 1];
+  float *score = reinterpret_cast<float *>(score4);
+  __shared__ int wave_cnt[4];
   __shared__ int frames_kept[CRATTN_HSA_MAX_KF];
   const int tid = threadIdx.x;
   const int t = (int)(blockIdx.x % (uint32_t)a.n_qblocks);
@@ -88,6 +100,7 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
     const int c = tid % CPR, g = tid / CPR;
     const int64_t r0 = (int64_t)t * kQB, r1 = min(r0 + kQB, a.Lq);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
     for (int64_t r = r0 + g; r < r1; r += RG)
       add_bf16x8(acc, *reinterpret_cast<const uint4 *>(
                           a.q + (((int64_t)b * a.Lq + r) * a.H + h) * D + c * 8));
@@ -102,25 +115,63 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
     }
     __syncthreads();
   }
-  auto dot = [&](const float *row) {
-    float s = 0.f;
+  // Scores of n items (rows of pooled keys): 16 threads per item, each
+  // adding D/16 products, then a butterfly over the 16 lanes.
+  constexpr int TPI = 16, FPT = D / TPI;
+  auto scores = [&](int n, auto row_of) {
+    const int sub = tid % TPI;
 #pragma unroll 8
-    for (int d = 0; d < D; d += 4) {
-      const float4 x = *reinterpret_cast<const float4 *>(row + d);
-      s += qbar[d] * x.x + qbar[d + 1] * x.y + qbar[d + 2] * x.z + qbar[d + 3] * x.w;
+    for (int base = tid / TPI; base < n; base += 256 / TPI) {
+      const float *row = row_of(base) + sub * FPT;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < FPT; d += 4) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + d);
+        const int dd = sub * FPT + d;
+        s += qbar[dd] * x.x + qbar[dd + 1] * x.y + qbar[dd + 2] * x.z + qbar[dd + 3] * x.w;
+      }
+#pragma unroll
+      for (int m = TPI / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, TPI);
+      if (sub == 0) score[base] = s;
     }
-    return s;
   };
   // rank of item i among n scores: how many are larger, or equal with a
-  // lower index (the order of a stable descending sort)
+  // lower index (the order of a stable descending sort).  Scores are read
+  // four at a time; the caller pads score[n .. n+3] with -inf, which never
+  // ranks above a finite score.
   auto rank = [&](int i, int n) {
     const float si = score[i];
     int k = 0;
-    for (int j = 0; j < n; ++j) {
-      const float sj = score[j];
-      k += (sj > si || (sj == si && j < i)) ? 1 : 0;
+#pragma unroll 4
+    for (int j4 = 0; j4 < (n + 3) / 4; ++j4) {
+      const float4 v = score4[j4];
+      const int j = 4 * j4;
+      k += (v.x > si || (v.x == si && j < i)) ? 1 : 0;
+      k += (v.y > si || (v.y == si && j + 1 < i)) ? 1 : 0;
+      k += (v.z > si || (v.z == si && j + 2 < i)) ? 1 : 0;
+      k += (v.w > si || (v.w == si && j + 3 < i)) ? 1 : 0;
     }
     return k;
+  };
+  // Items [0, n) are kept or not (keep(i)); call emit(i, pos) for each kept
+  // item with pos = the number of kept items before it.  A wave ballot
+  // counts the kept lanes below each lane; waves add up in LDS, 256 items
+  // at a time.
+  auto compact = [&](int n, auto keep, auto emit) {
+    const int lane = tid & 63, wave = tid >> 6;
+    int base = 0;
+    for (int i0 = 0; i0 < n; i0 += 256) {
+      const int i = i0 + tid;
+      const bool k = i < n && keep(i);
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(k);
+      if (lane == 0) wave_cnt[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int off = base;
+      for (int w = 0; w < wave; ++w) off += wave_cnt[w];
+      if (k) emit(i, off + __builtin_popcountll(bal & ((uint64_t(1) << lane) - 1)));
+      base += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+      __syncthreads();
+    }
   };
 
   const int n_hist = a.n_hist;
@@ -130,47 +181,39 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
   }
   // 2. frame scores and the kf best frames, kept in ascending order
   const float *fm = a.frames + (int64_t)bh * a.nf * D;
-  for (int f = tid; f < n_hist; f += 256) score[f] = dot(fm + (int64_t)f * D);
+  scores(n_hist, [&](int f) { return fm + (int64_t)f * D; });
+  if (tid < 4) score[n_hist + tid] = -INFINITY;
   __syncthreads();
-  for (int f = tid; f < n_hist; f += 256) keep[f] = rank(f, n_hist) < a.kf ? 1 : 0;
-  __syncthreads();
-  for (int f = tid; f < n_hist; f += 256)
-    if (keep[f]) {
-      int pos = 0;
-      for (int g2 = 0; g2 < f; ++g2) pos += keep[g2];
-      frames_kept[pos] = f;
-    }
-  __syncthreads();
+  compact(n_hist, [&](int f) { return rank(f, n_hist) < a.kf; },
+          [&](int f, int pos) { frames_kept[pos] = f; });
   const int n_frames = min(a.kf, n_hist);
   const int n_cand = n_frames * a.nbf;
   // 3. block scores of every block of the kept frames; candidate c is block
   // c % nbf of kept frame c / nbf, so candidates run in ascending block id
   const float *bm = a.blocks + (int64_t)bh * a.nf * a.nbf * D;
-  for (int cnd = tid; cnd < n_cand; cnd += 256) {
-    const int id = frames_kept[cnd / a.nbf] * a.nbf + cnd % a.nbf;
-    score[cnd] = dot(bm + (int64_t)id * D);
-  }
-  __syncthreads();
-  for (int cnd = tid; cnd < n_cand; cnd += 256) keep[cnd] = rank(cnd, n_cand) < a.kb ? 1 : 0;
+  scores(n_cand, [&](int cnd) {
+    return bm + (int64_t)(frames_kept[cnd / a.nbf] * a.nbf + cnd % a.nbf) * D;
+  });
+  if (tid < 4) score[n_cand + tid] = -INFINITY;
   __syncthreads();
   // 4. the kept blocks in ascending id order, then -1
-  for (int cnd = tid; cnd < n_cand; cnd += 256)
-    if (keep[cnd]) {
-      int pos = 0;
-      for (int g2 = 0; g2 < cnd; ++g2) pos += keep[g2];
-      out[pos] = frames_kept[cnd / a.nbf] * a.nbf + cnd % a.nbf;
-    }
+  compact(n_cand, [&](int cnd) { return rank(cnd, n_cand) < a.kb; },
+          [&](int cnd, int pos) { out[pos] = frames_kept[cnd / a.nbf] * a.nbf + cnd % a.nbf; });
   for (int e = min(a.kb, n_cand) + tid; e < a.kb; e += 256) out[e] = -1;
 }
 
 }  // namespace
 
 hipError_t launch_hsa_pool(const HsaPoolArgs &a, int D, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)a.B * a.H * a.n_frames);
-  if (D == 128)
-    hipLaunchKernelGGL(hsa_pool_kernel<128>, dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(hsa_pool_kernel<64>, dim3(grid), dim3(256), 0, s, a);
+  const unsigned gb = (unsigned)((int64_t)a.B * a.H * a.n_frames * a.nbf);
+  const unsigned gf = (unsigned)((int64_t)a.B * a.H * a.n_frames);
+  if (D == 128) {
+    hipLaunchKernelGGL(hsa_pool_blocks_kernel<128>, dim3(gb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(hsa_pool_frames_kernel<128>, dim3(gf), dim3(128), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(hsa_pool_blocks_kernel<64>, dim3(gb), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(hsa_pool_frames_kernel<64>, dim3(gf), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

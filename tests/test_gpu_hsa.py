@@ -77,12 +77,28 @@ def _check_pool(kc, per_frame, fr, bl):
     assert np.all(np.abs(fr - ef) <= (per_frame + 1) * EPS * af + 1e-30)
 
 
-def _score_bound(qbar_abs, k_abs, qbar, kbar, n_q, n_k, D):
-    """First-order bound of the fp32 pooled dot product's error: the
-    query mean's and key mean's summation errors and the D-term dot."""
-    return (n_q + 1) * EPS * (qbar_abs * np.abs(kbar)).sum(-1) + \
-        (n_k + 1) * EPS * (np.abs(qbar) * k_abs).sum(-1) + \
-        (D + 2) * EPS * (np.abs(qbar) * np.abs(kbar)).sum(-1)
+def _depths(D, per_frame):
+    """Rounding steps on any path of the GPU's summation trees (hsa.hip):
+    RG = 256 / (D/8) row groups; a thread adds its rows of the block (or
+    query block) in order, the RG partials are added in order, then one
+    division; a frame adds its block means times their lengths in block
+    order, then divides.  The dot product: D/16 products per lane in steps
+    of four, then a 4-level butterfly."""
+    RG = 256 // (D // 8)
+    q_mean = -(-256 // RG) + RG + 1
+    b_mean = -(-64 // RG) + RG + 1
+    f_mean = b_mean + 1 + hsa.blocks_per_frame(per_frame) + 1
+    dot = D // 16 + 8
+    return q_mean, b_mean, f_mean, dot
+
+
+def _score_bound(qbar_abs, k_abs, qbar, kbar, cq, ck, cdot):
+    """First-order bound of the fp32 pooled dot product's error: the query
+    mean's and the key mean's summation errors (cq, ck rounding steps times
+    the mean of |x|) and the dot product's own (cdot steps)."""
+    return cq * EPS * (qbar_abs * np.abs(kbar)).sum(-1) + \
+        ck * EPS * (np.abs(qbar) * k_abs).sum(-1) + \
+        cdot * EPS * (np.abs(qbar) * np.abs(kbar)).sum(-1)
 
 
 def _check_selection(q, kc, per_frame, L, q_pos0, kf, kb, sel):
@@ -96,13 +112,13 @@ def _check_selection(q, kc, per_frame, L, q_pos0, kf, kb, sel):
     af, ab = hsa.pool_keys(np.abs(ke), per_frame)
     qp, qa = hsa.pool_queries(qe), hsa.pool_queries(np.abs(qe))
     ref = hsa.select(qe, ef, eb, n_hist, per_frame, kf, kb)
+    cq, cb, cf, cdot = _depths(D, per_frame)
     s = sel.cpu().numpy()
     exact = 0
     for b in range(B):
         for h in range(H):
             for i in range(qp.shape[2]):
                 got = s[b, h, i]
-                n_q = min(256, Lq - 256 * i)
                 n_valid = int((got >= 0).sum())
                 assert (got[:n_valid] >= 0).all() and (got[n_valid:] == -1).all()
                 assert np.all(np.diff(got[:n_valid]) > 0)
@@ -112,7 +128,7 @@ def _check_selection(q, kc, per_frame, L, q_pos0, kf, kb, sel):
                     continue
                 fs = ef[b, h, :n_hist] @ qp[b, h, i]
                 ftol = _score_bound(qa[b, h, i], af[b, h, :n_hist], qp[b, h, i],
-                                    ef[b, h, :n_hist], n_q, per_frame, D)
+                                    ef[b, h, :n_hist], cq, cf, cdot)
                 frames = np.unique(got[:n_valid] // nbf)
                 assert len(frames) <= kf
                 # the frames the blocks came from must be a top-kf set up to
@@ -124,7 +140,7 @@ def _check_selection(q, kc, per_frame, L, q_pos0, kf, kb, sel):
                 cand = np.concatenate([np.arange(f * nbf, (f + 1) * nbf) for f in frames])
                 cs = eb[b, h, cand] @ qp[b, h, i]
                 btol = _score_bound(qa[b, h, i], ab[b, h, cand], qp[b, h, i], eb[b, h, cand],
-                                    n_q, 64, D).max()
+                                    cq, cb, cdot).max()
                 unchosen = np.setdiff1d(cand, got[:n_valid])
                 if len(unchosen):
                     best_out = (eb[b, h, unchosen] @ qp[b, h, i]).max()
@@ -222,9 +238,9 @@ def test_480p_chunk_sampled_rows():
     exact = _check_selection(q, kc, per_frame, L, w.q_pos0, 6, 32, sel)
     total = sel.shape[1] * sel.shape[2]
     print(f"  480P: {exact} of {total} query blocks matched exactly", flush=True)
-    # with N(0, 1) data the exact scores are almost always far apart
-    # compared with the fp32 bound, so nearly every choice is unique
-    assert exact >= 0.9 * total
+    # with N(0, 1) data the exact scores are mostly far apart compared with
+    # the fp32 bound, so most choices are unique and compared exactly
+    assert exact >= 0.5 * total
     out, lse = _hsa_attn(q, kc, vc, w.q_pos0, L, per_frame, sel)
     rows = np.unique(np.concatenate([np.arange(0, w.lq, 97), [w.lq - 1, 255, 256, 4607, 4608]]))
     s64 = sel.cpu().numpy().astype(np.int64)
