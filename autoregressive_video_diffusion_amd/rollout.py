@@ -8,6 +8,12 @@ Generation Inference with Sequential-Parallel 3D Positional Encoding Using a
 Global Time Index" §1: KV caching with rolling windows, §2.B: rotation from
 the chunk's start frame).
 
+Optionally the attention of each denoising step is the hierarchical
+block-sparse attention of "LIGHT FORCING" §2.2 (HSA): the keys of each
+chunk are mean-pooled per frame and per 64-token block when its clean K/V
+are stored, and every denoising call keeps, per 256-row query block, the kf
+best history frames and the kb best blocks inside them.
+
 This class only sequences the C-ABI calls; every step runs in the library's
 kernels.  Cache layout: ``window`` chunk slots of ``chunk_tokens`` rows per
 (batch, head); chunk c lives in slot c mod window.  While the ring fills, a
@@ -19,14 +25,19 @@ from __future__ import annotations
 
 import torch
 
-from . import (chunk_causal_attn, chunk_causal_attn_workspace_bytes, rope_apply_append,
-               rope_precompute, rope_table_bytes)
+from . import (HSA_QBLOCK, chunk_causal_attn, chunk_causal_attn_workspace_bytes, hsa_attn,
+               hsa_pool_bytes, hsa_pool_keys, hsa_select, rope_apply_append, rope_precompute,
+               rope_table_bytes)
 
 
 class ChunkRollout:
     def __init__(self, B: int, H: int, D: int, frames: int, grid_h: int, grid_w: int,
                  window: int, max_chunks: int, theta: float = 10000.0,
-                 device: str | torch.device = "cuda", dtype: torch.dtype = torch.bfloat16):
+                 device: str | torch.device = "cuda", dtype: torch.dtype = torch.bfloat16,
+                 hsa: tuple[int, int] | None = None):
+        """hsa = (kf, kb) switches the denoising attention to HSA with kf
+        frames and kb blocks kept per query block (chunks 0 .. window-1: the
+        selection's history is the slots before the chunk's own)."""
         self.B, self.H, self.D = B, H, D
         self.frames, self.grid_h, self.grid_w = frames, grid_h, grid_w
         self.window = window
@@ -42,6 +53,13 @@ class ChunkRollout:
         self.v_cache = torch.zeros(B, H, self.cap, D, dtype=dtype, device=dev)
         ws = max(self.workspace_bytes(c) for c in range(min(max_chunks, window + 1)))
         self.workspace = torch.empty(max(ws, 16) // 4 + 4, dtype=torch.float32, device=dev)
+        self.hsa = hsa
+        if hsa is not None:
+            self.per_frame = grid_h * grid_w
+            self.pool = torch.empty(hsa_pool_bytes(B, H, self.cap, D, self.per_frame) // 4,
+                                    dtype=torch.float32, device=dev)
+            self.sel = torch.empty(B, H, -(-self.L // HSA_QBLOCK), hsa[1], dtype=torch.int32,
+                                   device=dev)
 
     def slot(self, c: int) -> int:
         return c % self.window
@@ -68,12 +86,26 @@ class ChunkRollout:
     def denoise(self, c: int, q, k, v, q_out, out, lse=None, tok_off: int = 0):
         """One denoising step of chunk c: rotate Q/K, write the (noisy) K/V into
         the chunk's slot, attend.  q, k, v, q_out, out: [B, n, H, D]."""
+        if self.hsa is not None and c >= self.window:
+            raise NotImplementedError("HSA in a full ring window: the selection's history is "
+                                      "the slots before the chunk's own")
         self._rope(c, q, q_out, k, v, tok_off)
         kv_len, q0 = self.visible(c)
-        chunk_causal_attn(q_out, self.k_cache, self.v_cache, kv_len, q0 + tok_off, self.L, out,
-                          lse, self.workspace)
+        if self.hsa is None:
+            chunk_causal_attn(q_out, self.k_cache, self.v_cache, kv_len, q0 + tok_off, self.L,
+                              out, lse, self.workspace)
+            return out
+        n = q_out.shape[1]
+        sel = self.sel[:, :, :-(-n // HSA_QBLOCK)].contiguous() if n != self.L else self.sel
+        hsa_select(q_out, self.pool, self.cap, self.per_frame, q0 + tok_off, self.L,
+                   self.hsa[0], self.hsa[1], sel)
+        hsa_attn(q_out, self.k_cache, self.v_cache, q0 + tok_off, self.L, self.per_frame, sel,
+                 out, lse)
         return out
 
     def update(self, c: int, k, v, tok_off: int = 0):
-        """Cache update of chunk c: rotate the clean K and store it with V."""
+        """Cache update of chunk c: rotate the clean K and store it with V
+        (and, with HSA, pool the chunk's keys once the whole chunk is in)."""
         self._rope(c, None, None, k, v, tok_off)
+        if self.hsa is not None and tok_off + k.shape[1] == self.L:
+            hsa_pool_keys(self.k_cache, self.slot(c) * self.L, self.L, self.per_frame, self.pool)

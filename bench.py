@@ -263,15 +263,16 @@ def fused_step_ms(crattn, w, sets, table, ext, ws, reps=10, rounds=3):
     return sorted(tp)[len(tp) // 2], sorted(tf)[len(tf) // 2]
 
 
-def rollout_ms(crattn, dev, reps=2):
-    """Whole 480P rollout: 7 chunks x (4 denoising calls + 1 cache update)."""
+def rollout_ms(crattn, dev, reps=2, hsa=None):
+    """Whole 480P rollout: 7 chunks x (4 denoising calls + 1 cache update),
+    with dense or (hsa = (kf, kb)) block-sparse attention."""
     import torch
 
     from autoregressive_video_diffusion_amd.rollout import ChunkRollout
     from workloads import ROLLOUT480 as w
 
     ro = ChunkRollout(w.B, w.H, w.D, w.frames, w.grid_h, w.grid_w, window=7, max_chunks=7,
-                      device=dev)
+                      device=dev, hsa=hsa)
     n = w.chunk_tokens
     qkv = [tuple(torch.randn(w.B, n, w.H, w.D, device=dev).to(torch.bfloat16) for _ in range(3))
            for _ in range(5)]
@@ -447,6 +448,7 @@ def main():
         extras["step_plain_vs_fused_qrot_ms"] = [round(plain_ms, 4), round(fused_ms, 4)]
         extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)
         extras["rollout480_ms_per_chunk"] = round(extras["rollout480_ms_total"] / 7, 3)
+        extras["rollout480_hsa_ms_total"] = round(rollout_ms(crattn, dev, hsa=(6, 32)), 3)
         torch.cuda.empty_cache()
         del sets
         torch.cuda.empty_cache()

@@ -248,3 +248,33 @@ def test_480p_chunk_sampled_rows():
                               rows=rows)
     assert_attn_close(f64(out)[:, rows], o_ref, "hsa 480P")
     np.testing.assert_allclose(f64(lse)[:, :, rows], lse_ref, atol=2e-3)
+
+
+def test_rollout_with_hsa_every_chunk():
+    # a 4-chunk rollout (one 8x8 frame per chunk, 2 heads of 64) with HSA
+    # keeping 2 frames and 2 blocks: each denoising call is checked against
+    # the oracle on the rollout's own selection and cache contents
+    from autoregressive_video_diffusion_amd.rollout import ChunkRollout
+
+    B, H, D, gh, gw = 1, 2, 64, 8, 8
+    ro = ChunkRollout(B, H, D, 1, gh, gw, window=4, max_chunks=5, device=dev(), hsa=(2, 2))
+    L = ro.L
+    for c in range(4):
+        q = normal((B, L, H, D), 700 + 3 * c).to(dev())
+        k = normal((B, L, H, D), 701 + 3 * c).to(dev())
+        v = normal((B, L, H, D), 702 + 3 * c).to(dev())
+        q_out, out = torch.empty_like(q), torch.empty_like(q)
+        ro.denoise(c, q, k, v, q_out, out)
+        torch.cuda.synchronize()
+        sel = ro.sel.cpu().numpy().astype(np.int64)
+        if c == 0:
+            assert (sel == -1).all()
+        else:
+            assert (sel[..., :min(2, c)] >= 0).all()
+        o_ref, _ = hsa.attn(f64(q_out), f64(ro.k_cache), f64(ro.v_cache), sel, c * L, (c + 1) * L,
+                            gh * gw)
+        assert_attn_close(f64(out), o_ref, f"hsa rollout chunk {c}")
+        ro.update(c, k, v)
+    with pytest.raises(NotImplementedError):
+        q = normal((B, L, H, D), 900).to(dev())
+        ro.denoise(4, q, q, q, torch.empty_like(q), torch.empty_like(q))
