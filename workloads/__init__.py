@@ -131,3 +131,24 @@ def projection_inputs(w: Workload, call_index: int, hidden: int | None = None):
     wt = (torch.randn(3 * w.H * w.D, C, generator=g, dtype=torch.float32) / C ** 0.5)
     return x, wt.to(torch.bfloat16)
 
+
+
+def planted_clusters(batch_shape, n: int, C: int, D: int, seed: int, spread: float = 0.05,
+                     dtype: torch.dtype = torch.bfloat16):
+    """Tokens grouped around C centres: x [*batch_shape, n, D] and the centre
+    of every token, labels [*batch_shape, n] (int64).  Centres ~ N(0, 1);
+    each token = its centre + spread * N(0, 1).  Token floor(c n / C) belongs
+    to centre c, every other token to a uniformly drawn centre, so every
+    centre has at least one token and the tokens of a centre are scattered
+    over the sequence."""
+    g = torch.Generator().manual_seed(int(seed))
+    nb = 1
+    for s in batch_shape:
+        nb *= int(s)
+    centres = torch.randn(nb, C, D, generator=g, dtype=torch.float32)
+    labels = torch.randint(0, C, (nb, n), generator=g)
+    labels[:, [c * n // C for c in range(C)]] = torch.arange(C)
+    noise = torch.randn(nb, n, D, generator=g, dtype=torch.float32)
+    x = torch.gather(centres, 1, labels[..., None].expand(nb, n, D)) + spread * noise
+    x = x.reshape(*batch_shape, n, D)
+    return (x if dtype == torch.float32 else x.to(dtype)), labels.reshape(*batch_shape, n)
