@@ -24,6 +24,11 @@ Entry points (see include/crattn.h for the full contracts):
   hierarchical block-sparse attention: pooled frame and block keys, two-level
   block selection per query block, attention over the own chunk plus the
   selected blocks.
+* ``svg2_kmeans_workspace_bytes`` / ``svg2_kmeans`` / ``svg2_n_slots`` /
+  ``svg2_plan`` / ``svg2_attn_workspace_bytes`` / ``svg2_attn`` --
+  semantic-permutation sparse attention: k-means of queries and keys with the
+  reordering by cluster, centroid top-p selection with the key lists and
+  query tiles, attention of the query tiles over their key lists.
 """
 from __future__ import annotations
 
@@ -36,7 +41,9 @@ __all__ = [
     "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
     "rope_apply_append", "qkv_rope_append", "chunk_causal_attn_workspace_bytes",
     "chunk_causal_attn", "chunk_causal_attn_rope", "hsa_pool_bytes", "hsa_pool_keys",
-    "hsa_select", "hsa_attn", "crattn_last_error", "EXPORTS", "HSA_QBLOCK", "HSA_KBLOCK",
+    "hsa_select", "hsa_attn", "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots",
+    "svg2_plan", "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error", "EXPORTS",
+    "HSA_QBLOCK", "HSA_KBLOCK", "SVG2_QTILE",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,8 +55,11 @@ CRATTN_F32, CRATTN_BF16 = 0, 1
 # Every symbol include/crattn.h declares.
 EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append", "qkv_rope_append",
            "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "chunk_causal_attn_rope",
-           "hsa_pool_bytes", "hsa_pool_keys", "hsa_select", "hsa_attn", "crattn_last_error")
+           "hsa_pool_bytes", "hsa_pool_keys", "hsa_select", "hsa_attn",
+           "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots", "svg2_plan",
+           "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error")
 HSA_QBLOCK, HSA_KBLOCK = 256, 64
+SVG2_QTILE = 256
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -102,6 +112,23 @@ def load():
     lib.hsa_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _i32,
                              _i32, _i32, _i64, ctypes.c_float, _vp]
     lib.hsa_attn.restype = _i32
+    lib.svg2_kmeans_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    lib.svg2_kmeans_workspace_bytes.restype = ctypes.c_size_t
+    lib.svg2_kmeans.argtypes = [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _vp, _i64, _vp, _i64, _vp, _i64, _vp, ctypes.c_size_t, _vp]
+    lib.svg2_kmeans.restype = _i32
+    lib.svg2_n_slots.argtypes = [_i64, _i32]
+    lib.svg2_n_slots.restype = _i32
+    lib.svg2_plan.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                              _i64, _i64, ctypes.c_float, ctypes.c_float, _vp, _vp, _i64, _vp,
+                              _vp, _i32, _vp]
+    lib.svg2_plan.restype = _i32
+    lib.svg2_attn_workspace_bytes.argtypes = [_i32, _i32, _i64, _i32, _i32]
+    lib.svg2_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.svg2_attn.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32,
+                              _vp, _vp, _vp, ctypes.c_size_t, _i32, _i32, _i32, _i64,
+                              ctypes.c_float, _vp]
+    lib.svg2_attn.restype = _i32
     lib.crattn_last_error.argtypes = []
     lib.crattn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -316,3 +343,117 @@ def hsa_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, q_po
                            float(scale), _stream(stream)))
     return out
 
+
+
+def svg2_kmeans_workspace_bytes(B: int, H: int, n: int, C: int) -> int:
+    return int(load().svg2_kmeans_workspace_bytes(B, H, n, C))
+
+
+def _view_ptr(t: torch.Tensor, what: str, dtype: torch.dtype, inner: int):
+    """Start of a strided device view whose last `inner` dims are dense, and
+    its per-head stride (batch stride = H x head stride)."""
+    if not t.is_cuda or t.dtype != dtype:
+        raise ValueError(f"{what} must be a {dtype} device tensor")
+    size, st = t.shape, t.stride()
+    dense = 1
+    for d in range(t.dim() - 1, t.dim() - 1 - inner, -1):
+        if st[d] != dense:
+            raise ValueError(f"{what}: the last {inner} dims must be contiguous")
+        dense *= size[d]
+    if size[0] > 1 and st[0] != size[1] * st[1]:
+        raise ValueError(f"{what}: batch stride must be H x head stride")
+    return t.data_ptr(), st[1]
+
+
+def svg2_kmeans(x: torch.Tensor, C: int, iters: int, from_tokens: bool,
+                centroids: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor,
+                workspace: torch.Tensor, stream=None):
+    """k-means of the tokens of every head, then their reordering by cluster.
+
+    x: a bf16 view with logical shape [B, H, n, D] (any strides, last dim
+    dense): q.permute(0, 2, 1, 3) for queries [B, Lq, H, D], or
+    k_cache[:, :, r0:r0 + n] for one chunk slot of a cache.  centroids: float
+    view [B, H, C, D] (in/out); perm: int32 view [B, H, n]; offsets: int32
+    view [B, H, C + 1] (each dense inside a head, e.g. slices [:, :, s] of
+    per-slot arrays)."""
+    B, H, n, D = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(3) != 1:
+        raise ValueError("x must be a bf16 device view with a dense last dim")
+    if tuple(centroids.shape) != (B, H, C, D) or tuple(perm.shape) != (B, H, n) or \
+            tuple(offsets.shape) != (B, H, C + 1):
+        raise ValueError("centroids [B, H, C, D], perm [B, H, n], offsets [B, H, C+1] required")
+    cp, cs = _view_ptr(centroids, "centroids", torch.float32, 2)
+    pp, ps = _view_ptr(perm, "perm", torch.int32, 1)
+    op, os_ = _view_ptr(offsets, "offsets", torch.int32, 1)
+    _raise(load().svg2_kmeans(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, n, D, C,
+                              iters, int(bool(from_tokens)), cp, cs, pp, ps, op, os_,
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+    return centroids, perm, offsets
+
+
+def svg2_n_slots(Lq: int, Cq: int) -> int:
+    return int(load().svg2_n_slots(Lq, Cq))
+
+
+def svg2_plan(q_cent: torch.Tensor, q_off: torch.Tensor, k_cent: torch.Tensor,
+              k_off: torch.Tensor, k_perm: torch.Tensor, n_vis: int, Lq: int, p: float,
+              lists: torch.Tensor, list_len: torch.Tensor, slots: torch.Tensor,
+              sel: torch.Tensor | None = None, scale: float = 0.0, stream=None):
+    """q_cent [B, H, Cq, D] f32, q_off [B, H, Cq+1] i32; k_cent [B, H, S, Ck, D],
+    k_off [B, H, S, Ck+1], k_perm [B, H, S, L]; lists [B, H, Cq, list_cap],
+    list_len [B, H, Cq], slots [B, H, n_slots, 4], sel [B, H, Cq, n_vis*Ck]
+    (all int32 but the centroids)."""
+    B, H, Cq, D = q_cent.shape
+    _, _, S, Ck, _ = k_cent.shape
+    L = k_perm.shape[3]
+    for t, name in ((q_off, "q_off"), (k_off, "k_off"), (k_perm, "k_perm"), (lists, "lists"),
+                    (list_len, "list_len"), (slots, "slots")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    if q_cent.dtype != torch.float32 or k_cent.dtype != torch.float32:
+        raise ValueError("centroids must be float32")
+    if tuple(q_off.shape) != (B, H, Cq + 1) or tuple(k_off.shape) != (B, H, S, Ck + 1) or \
+            tuple(k_perm.shape[:3]) != (B, H, S) or tuple(lists.shape[:3]) != (B, H, Cq) or \
+            tuple(list_len.shape) != (B, H, Cq) or slots.dim() != 4 or \
+            tuple(slots.shape[:2]) != (B, H) or slots.shape[3] != 4:
+        raise ValueError("inconsistent shapes")
+    if sel is not None and (sel.dtype != torch.int32 or
+                            tuple(sel.shape) != (B, H, Cq, n_vis * Ck)):
+        raise ValueError(f"sel must be int32 [{B}, {H}, {Cq}, {n_vis * Ck}]")
+    _raise(load().svg2_plan(_ptr(q_cent), _ptr(q_off), _ptr(k_cent), _ptr(k_off), _ptr(k_perm),
+                            B, H, D, Cq, Ck, S, n_vis, L, Lq, float(p), float(scale), _ptr(sel),
+                            _ptr(lists), lists.shape[3], _ptr(list_len), _ptr(slots),
+                            slots.shape[2], _stream(stream)))
+    return lists, list_len, slots
+
+
+def svg2_attn_workspace_bytes(B: int, H: int, Lq: int, D: int, splits: int) -> int:
+    return int(load().svg2_attn_workspace_bytes(B, H, Lq, D, splits))
+
+
+def svg2_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              q_perm: torch.Tensor, slots: torch.Tensor, lists: torch.Tensor,
+              list_len: torch.Tensor, out: torch.Tensor, lse: torch.Tensor | None = None,
+              splits: int = 1, workspace: torch.Tensor | None = None, scale: float = 0.0,
+              stream=None) -> torch.Tensor:
+    """Attention of the query tiles of `slots` over their clusters' key lists.
+    q, out: [B, Lq, H, D] bf16; caches [B, H, cap, D] bf16; q_perm [B, H, Lq]."""
+    B, Lq, H, D = q.shape
+    cap = k_cache.shape[2]
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q and out must be bf16 of one shape")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != torch.bfloat16:
+            raise ValueError("caches must be bf16 [B, H, cap, D]")
+    if tuple(q_perm.shape) != (B, H, Lq) or q_perm.dtype != torch.int32:
+        raise ValueError("q_perm must be int32 [B, H, Lq]")
+    if lse is not None and (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, H, Lq]")
+    Cq, list_cap = lists.shape[2], lists.shape[3]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _raise(load().svg2_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, _ptr(q_perm),
+                            _ptr(slots), slots.shape[2], _ptr(lists), list_cap, _ptr(list_len),
+                            Cq, splits, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, B, H, D,
+                            Lq, float(scale), _stream(stream)))
+    return out

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libcrattn.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "rope.hip", "attn.hip", "qkv.hip", "hsa.hip"]
+SOURCES = ["api.cpp", "rope.hip", "attn.hip", "qkv.hip", "hsa.hip", "svg2.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

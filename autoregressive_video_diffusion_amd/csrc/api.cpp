@@ -503,6 +503,204 @@ int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t ca
                    chunk_tokens, out, lse, nullptr, 0, B, H, D, Lq, scale, stream);
 }
 
+size_t svg2_kmeans_workspace_bytes(int B, int H, int n, int C) {
+  if (B < 1 || H < 1 || n < 1 || n > CRATTN_SVG2_MAX_N || C < 1 || C > CRATTN_SVG2_MAX_C)
+    return 0;
+  if ((double)B * H * CRATTN_SVG2_MAX_N >= 2147483648.0) return 0;
+  const size_t assign = ((size_t)B * H * n * 4u + 255u) & ~size_t(255);
+  return assign + (size_t)B * H * C * 4u;
+}
+
+int svg2_kmeans(const void *x, int64_t stride_b, int64_t stride_h, int64_t stride_row, int B,
+                int H, int n, int D, int C, int iters, int from_tokens, float *centroids,
+                int64_t cent_stride, int32_t *perm, int64_t perm_stride, int32_t *offsets,
+                int64_t off_stride, void *workspace, size_t ws_bytes, void *stream) {
+  if (x == nullptr || centroids == nullptr || perm == nullptr || offsets == nullptr ||
+      workspace == nullptr)
+    return fail(CRATTN_EINVAL, "svg2_kmeans: x, centroids, perm, offsets, workspace required");
+  if (!aligned16(x) || !aligned16(centroids) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(perm) & 3u) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return fail(CRATTN_EINVAL, "svg2_kmeans: x, centroids, workspace 16-byte aligned required");
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "svg2_kmeans: head_dim %d not supported (64 or 128)", D);
+  if (B < 1 || H < 1 || n < 1 || n > CRATTN_SVG2_MAX_N)
+    return fail(CRATTN_EINVAL, "svg2_kmeans: B, H >= 1 and n in [1, %d] required",
+                CRATTN_SVG2_MAX_N);
+  if (C < 1 || C > CRATTN_SVG2_MAX_C || iters < 1 || iters > CRATTN_SVG2_MAX_ITERS)
+    return fail(CRATTN_EINVAL, "svg2_kmeans: C in [1, %d] and iters in [1, %d] required",
+                CRATTN_SVG2_MAX_C, CRATTN_SVG2_MAX_ITERS);
+  if (stride_b < 0 || stride_h < 0 || stride_row < 0 || stride_b % 8 || stride_h % 8 ||
+      stride_row % 8 || stride_b > kMaxElems || stride_h > kMaxElems || stride_row > kMaxElems)
+    return fail(CRATTN_EINVAL, "svg2_kmeans: strides must be non-negative multiples of 8");
+  if (cent_stride < (int64_t)C * D || cent_stride % 4 || perm_stride < n ||
+      off_stride < C + 1 || cent_stride > kMaxElems || perm_stride > kMaxElems ||
+      off_stride > kMaxElems)
+    return fail(CRATTN_EINVAL, "svg2_kmeans: output strides smaller than one head's extent");
+  const size_t need = svg2_kmeans_workspace_bytes(B, H, n, C);
+  if (need == 0 || ws_bytes < need)
+    return fail(CRATTN_EINVAL, "svg2_kmeans: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  crattn::KmArgs a;
+  a.x = static_cast<const uint16_t *>(x);
+  a.sb = stride_b;
+  a.sh = stride_h;
+  a.sr = stride_row;
+  a.B = B;
+  a.H = H;
+  a.n = n;
+  a.C = C;
+  a.cent = centroids;
+  a.cent_s = cent_stride;
+  a.perm = perm;
+  a.perm_s = perm_stride;
+  a.off = offsets;
+  a.off_s = off_stride;
+  a.assign = static_cast<int32_t *>(workspace);
+  a.norm = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                     (((size_t)B * H * n * 4u + 255u) & ~size_t(255)));
+  return hip_status(crattn::launch_svg2_kmeans(a, D, iters, from_tokens != 0,
+                                               static_cast<hipStream_t>(stream)),
+                    "svg2_kmeans launch");
+}
+
+int svg2_n_slots(int64_t Lq, int Cq) {
+  if (Lq < 1 || Lq > kMaxElems || Cq < 1 || Cq > CRATTN_SVG2_MAX_C) return 0;
+  const int64_t v = (Lq + CRATTN_SVG2_QTILE - 1) / CRATTN_SVG2_QTILE + Cq;
+  return v >= (int64_t(1) << 30) ? 0 : (int)v;
+}
+
+int svg2_plan(const float *q_cent, const int32_t *q_off, const float *k_cent,
+              const int32_t *k_off, const int32_t *k_perm, int B, int H, int D, int Cq, int Ck,
+              int S, int n_vis, int64_t L, int64_t Lq, float p, float scale, int32_t *sel,
+              int32_t *lists, int64_t list_cap, int32_t *list_len, int32_t *slots, int n_slots,
+              void *stream) {
+  if (q_cent == nullptr || q_off == nullptr || k_cent == nullptr || k_off == nullptr ||
+      k_perm == nullptr || lists == nullptr || list_len == nullptr || slots == nullptr)
+    return fail(CRATTN_EINVAL, "svg2_plan: every pointer but sel is required");
+  if (!aligned16(q_cent) || !aligned16(k_cent) || !aligned16(slots) || !aligned16(sel) ||
+      !aligned16(lists) || !aligned16(list_len) || !aligned16(q_off) || !aligned16(k_off) ||
+      !aligned16(k_perm))
+    return fail(CRATTN_EINVAL, "svg2_plan: pointers must be 16-byte aligned");
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "svg2_plan: head_dim %d not supported (64 or 128)", D);
+  if (B < 1 || H < 1 || Lq < 1 || Lq > kMaxElems)
+    return fail(CRATTN_EINVAL, "svg2_plan: B, H, Lq >= 1 required");
+  if (Cq < 1 || Cq > CRATTN_SVG2_MAX_C || Ck < 1 || Ck > CRATTN_SVG2_MAX_C)
+    return fail(CRATTN_EINVAL, "svg2_plan: Cq and Ck in [1, %d] required", CRATTN_SVG2_MAX_C);
+  if (S < 1 || n_vis < 1 || n_vis > S || (int64_t)n_vis * Ck > CRATTN_SVG2_MAX_CAND)
+    return fail(CRATTN_EINVAL, "svg2_plan: 1 <= n_vis <= S and n_vis*Ck <= %d required",
+                CRATTN_SVG2_MAX_CAND);
+  if (L < 1 || L > CRATTN_SVG2_MAX_N)
+    return fail(CRATTN_EINVAL, "svg2_plan: L in [1, %d] required", CRATTN_SVG2_MAX_N);
+  if (!(p > 0.f) || !isfinite(p) || !(scale >= 0.f) || !isfinite(scale))
+    return fail(CRATTN_EINVAL, "svg2_plan: p > 0 and a finite scale >= 0 required");
+  if (list_cap % 64 != 0 || list_cap < (int64_t)n_vis * L || list_cap > kMaxElems)
+    return fail(CRATTN_EINVAL, "svg2_plan: list_cap must be a multiple of 64, >= %lld",
+                (long long)((int64_t)n_vis * L));
+  if (n_slots < svg2_n_slots(Lq, Cq) || svg2_n_slots(Lq, Cq) == 0)
+    return fail(CRATTN_EINVAL, "svg2_plan: n_slots %d below %d", n_slots, svg2_n_slots(Lq, Cq));
+  if ((double)B * H * Cq >= 2147483648.0 || (double)S * L * B * H > (double)kMaxElems)
+    return fail(CRATTN_EINVAL, "svg2_plan: sizes too large");
+  crattn::SvgPlanArgs a;
+  a.q_cent = q_cent;
+  a.q_off = q_off;
+  a.k_cent = k_cent;
+  a.k_off = k_off;
+  a.k_perm = k_perm;
+  a.B = B;
+  a.H = H;
+  a.Cq = Cq;
+  a.Ck = Ck;
+  a.S = S;
+  a.n_vis = n_vis;
+  a.L = L;
+  a.p = p;
+  a.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
+  a.sel = sel;
+  a.lists = lists;
+  a.list_cap = list_cap;
+  a.list_len = list_len;
+  a.slots = slots;
+  a.n_slots = n_slots;
+  a.qtile = CRATTN_SVG2_QTILE;
+  return hip_status(crattn::launch_svg2_plan(a, D, static_cast<hipStream_t>(stream)),
+                    "svg2_plan launch");
+}
+
+size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int splits) {
+  if (B < 1 || H < 1 || Lq < 1 || Lq > kMaxElems || (D != 64 && D != 128) || splits < 1 ||
+      splits > 16)
+    return 0;
+  return splits > 1 ? (size_t)splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0;
+}
+
+int svg2_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
+              const int32_t *q_perm, const int32_t *slots, int n_slots, const int32_t *lists,
+              int64_t list_cap, const int32_t *list_len, int Cq, int splits, void *out,
+              float *lse, void *workspace, size_t ws_bytes, int B, int H, int D, int64_t Lq,
+              float scale, void *stream) {
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr ||
+      q_perm == nullptr || slots == nullptr || lists == nullptr || list_len == nullptr)
+    return fail(CRATTN_EINVAL, "svg2_attn: q, caches, q_perm, slots, lists, list_len and out "
+                               "are required");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) ||
+      !aligned16(lse) || !aligned16(workspace) || !aligned16(slots) || !aligned16(lists) ||
+      !aligned16(q_perm) || !aligned16(list_len))
+    return fail(CRATTN_EINVAL, "svg2_attn: pointers must be 16-byte aligned");
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "svg2_attn: head_dim %d not supported (64 or 128)", D);
+  if (B < 1 || H < 1 || Lq < 1 || Lq > kMaxElems || cap < 1 || n_slots < 1)
+    return fail(CRATTN_EINVAL, "svg2_attn: B, H, Lq, cap, n_slots >= 1 required");
+  if (Cq < 1 || Cq > CRATTN_SVG2_MAX_C)
+    return fail(CRATTN_EINVAL, "svg2_attn: Cq in [1, %d] required", CRATTN_SVG2_MAX_C);
+  if (list_cap < 64 || list_cap % 64 != 0 || list_cap >= (int64_t(1) << 31))
+    return fail(CRATTN_EINVAL, "svg2_attn: list_cap must be a positive multiple of 64");
+  if (splits < 1 || splits > 16)
+    return fail(CRATTN_EINVAL, "svg2_attn: splits in [1, 16] required");
+  if (!(scale >= 0.f) || !isfinite(scale))
+    return fail(CRATTN_EINVAL, "svg2_attn: scale must be finite and >= 0");
+  if ((double)cap * D >= 2147483648.0 || (double)B * H * (double)cap * D > (double)kMaxElems)
+    return fail(CRATTN_EINVAL, "svg2_attn: cap * head_dim must be below 2^31");
+  if ((double)B * H * (double)Lq * (D / 4) >= 4294967296.0 ||
+      (double)B * H * (double)n_slots * splits >= 2147483648.0 || Lq >= (int64_t(1) << 31))
+    return fail(CRATTN_EINVAL, "svg2_attn: too large for one launch");
+  const size_t need = svg2_attn_workspace_bytes(B, H, Lq, D, splits);
+  if (splits > 1 && (workspace == nullptr || ws_bytes < need))
+    return fail(CRATTN_EINVAL, "svg2_attn: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  crattn::AttnPlan plan{};
+  plan.d = D;
+  plan.bm = CRATTN_SVG2_QTILE;
+  plan.bn = 64;
+  plan.n_tiles = n_slots;
+  plan.splits = splits;
+  plan.grid = (int64_t)B * H * n_slots * splits;
+  plan.ws_bytes = need;
+  crattn::AttnArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.cap = cap;
+  a.kv_len = cap;
+  a.q_pos0 = 0;
+  a.chunk_tokens = 1;
+  a.out = out;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.ws_bytes = ws_bytes;
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.Lq = Lq;
+  a.scale = scale;
+  a.q_perm = q_perm;
+  a.gslots = slots;
+  a.lists = lists;
+  a.list_len = list_len;
+  a.list_cap = list_cap;
+  a.cq = Cq;
+  return hip_status(crattn::launch_attn(a, plan, static_cast<hipStream_t>(stream)),
+                    "svg2_attn launch");
+}
+
 const char *crattn_last_error(void) { return g_err; }
 
 }  // extern "C"

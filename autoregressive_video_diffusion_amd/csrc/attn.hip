@@ -73,6 +73,13 @@ struct AttnKArgs {
   // block-sparse instance: per (b, h, query tile) kb selected key blocks
   const int32_t *sel;
   int kb, nbf, blk_frame, n_hist_blocks;
+  // gather instance: query tiles of query clusters and their key lists
+  const int32_t *q_perm;    // [B][H][Lq]
+  const int32_t *gslots;    // [B][H][n_tiles][4]
+  const int32_t *lists;     // [B][H][cq][list_cap]
+  const int32_t *list_len;  // [B][H][cq]
+  int64_t list_cap;
+  int cq;
 };
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
@@ -152,6 +159,13 @@ __device__ inline void lds_dma16_sv(const void *gbase, uint32_t voff, uint32_t l
                : "s"(lds_addr), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+// The same with 4 bytes per lane (lane i fills LDS bytes 4i .. 4i + 3).
+__device__ inline void lds_dma4_sv(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 template <int D>
@@ -161,7 +175,7 @@ struct Pitch {
   static constexpr int V = CPR + 4;
 };
 
-template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE>
+template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE, bool GATHER>
 __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   constexpr int kBN = 64;
   constexpr int DK = D / 16;    // k-steps of the QK product
@@ -210,6 +224,27 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   const int h = (int)(bid % a.H);
   const int b = (int)(bid / a.H);
 
+  // Gather instance: the work item is query tile `tile` of the head's
+  // slot table: reordered query positions [first, first + rows) of one
+  // query cluster, attending to the key rows listed for that cluster.  A
+  // slot with no rows (or out of range) has nothing to do.
+  int64_t row0, nrows, q_chunk = 0;
+  int limit;
+  [[maybe_unused]] const int32_t *g_list = nullptr;
+  [[maybe_unused]] const int32_t *g_qperm = nullptr;
+  if constexpr (GATHER) {
+    const int64_t bhi = (int64_t)b * a.H + h;
+    const int4 sl = reinterpret_cast<const int4 *>(a.gslots)[bhi * a.n_tiles + tile];
+    if (sl.y <= 0 || sl.y > BM || sl.x < 0 || (int64_t)sl.x + sl.y > a.Lq || sl.z < 0 ||
+        sl.z >= a.cq)
+      return;
+    row0 = sl.x;
+    nrows = sl.y;
+    const int64_t li = bhi * a.cq + sl.z;
+    limit = (int)min((int64_t)max(a.list_len[li], 0), a.list_cap);
+    g_list = a.lists + li * a.list_cap;
+    g_qperm = a.q_perm + bhi * a.Lq;
+  } else {
   int64_t seg, t_in, seg_row0, seg_rows;
   if (tile < a.tiles0) {
     seg = 0;
@@ -231,11 +266,12 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       seg_rows = a.last_rows;
     }
   }
-  const int64_t row0 = seg_row0 + t_in * BM;
-  const int64_t nrows = min((int64_t)BM, seg_rows - t_in * BM);
-  const int64_t q_chunk = a.q_pos0 / a.L + seg;
+  row0 = seg_row0 + t_in * BM;
+  nrows = min((int64_t)BM, seg_rows - t_in * BM);
+  q_chunk = a.q_pos0 / a.L + seg;
   // keys of one head fit 32-bit indices (the front end bounds cap * D)
-  const int limit = (int)min(a.kv_len, (q_chunk + 1) * a.L);
+  limit = (int)min(a.kv_len, (q_chunk + 1) * a.L);
+  }
   int nkt = (limit + kBN - 1) / kBN;
 
   // ---- block-sparse key list: the tiles of the own chunk, then the
@@ -301,7 +337,9 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const int64_t row = wrow0 + qb * 32 + l32;
     const bool ok = row < row0 + nrows;
-    const uint16_t *qp = a.q + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 8;
+    int64_t mrow = row;  // the query's row in memory
+    if constexpr (GATHER) mrow = ok ? min((uint32_t)g_qperm[row], (uint32_t)(a.Lq - 1)) : 0;
+    const uint16_t *qp = a.q + (((int64_t)b * a.Lq + mrow) * a.H + h) * D + hf * 8;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks) {
       uint4 x = make_uint4(0, 0, 0, 0);
@@ -400,9 +438,46 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(lds_ring));
   // (slots n with (n + 1) * NW <= instructions exist for every wavefront:
   // the test is decided at compile time)
+  // Gather instance: the rows of tile kt are list entries 64 kt .. 64 kt + 63,
+  // whose key rows sit in LDS ring entry kt mod 8 (copied there earlier,
+  // see the key loop).  A lane's cell keeps its row-in-tile and column; the
+  // key row comes from the ring, clamped to the head's rows.  Entries past
+  // the list's end re-read its last key (masked, as in the edge tile).
+  [[maybe_unused]] int *g_idx = nullptr;
+  [[maybe_unused]] uint32_t g_idx_lds = 0;
+  if constexpr (GATHER) {
+    __shared__ int idx_ring[8 * kBN];
+    g_idx = idx_ring;
+    g_idx_lds = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(idx_ring));
+  }
   auto dma = [&](int kt, int stage) {
     const uint32_t kdst = ring_lds + (uint32_t)stage * (STAGE_CELLS * 16);
     const uint32_t vdst = kdst + K_CELLS * 16;
+    if constexpr (GATHER) {
+      const int last = min(kBN, limit - kt * kBN) - 1;
+      const int *ir = g_idx + (kt & 7) * kBN;
+      const uint32_t rows_max = (uint32_t)a.cap - 1u;
+#pragma unroll
+      for (int n = 0; n < K_SLOTS; ++n) {
+        const int j = wave + n * NW;
+        if ((n + 1) * NW <= K_INSTR || j < K_INSTR) {
+          const int r = min((int)(dma_k_off[n] / kRowBytes), last);
+          const uint32_t key = min((uint32_t)ir[r], rows_max);
+          lds_dma16_sv(kh, key * kRowBytes + dma_k_off[n] % kRowBytes, kdst + j * 1024);
+        }
+      }
+#pragma unroll
+      for (int n = 0; n < V_SLOTS; ++n) {
+        const int j = wave + n * NW;
+        if ((n + 1) * NW <= V_INSTR || j < V_INSTR) {
+          const int r = min((int)(dma_v_off[n] / kRowBytes), last);
+          const uint32_t key = min((uint32_t)ir[r], rows_max);
+          lds_dma16_sv(vh, key * kRowBytes + dma_v_off[n] % kRowBytes, vdst + j * 1024);
+        }
+      }
+      return;
+    }
     const int key0 = tile_key0(kt);
     const int lim = tile_lim(kt);
     const uint16_t *kb = kh + key0 * D;
@@ -568,6 +643,15 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   // instructions in this order while letting LDS reads and scalar work move.
   constexpr int kSlotMask = 0x0100 | 0x0004;  // DS reads, SALU may cross
   f32x16_t sbuf[2][KB][QB];
+  if constexpr (GATHER) {
+    // key rows of the first five tiles; later ones are copied five tiles
+    // ahead inside the loop
+    for (int e = tid; e < 5 * kBN; e += NW * 64) {
+      const int t = kt_begin + e / kBN;
+      if (t < kt_end) g_idx[(t & 7) * kBN + e % kBN] = g_list[(int64_t)t * kBN + e % kBN];
+    }
+    __syncthreads();
+  }
   if (kt_begin < kt_end) dma(kt_begin, 0);
   if (kt_begin + 1 < kt_end) dma(kt_begin + 1, 1);
   if (kt_begin + 2 < kt_end) dma(kt_begin + 2, 2);
@@ -603,6 +687,15 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
       // every wavefront now sees tile kt+1 and has finished tile kt-1, whose
       // stage the copy of tile kt+3 refills
       __syncthreads();
+      if constexpr (GATHER) {
+        // Key rows of tile kt+5, issued before tile kt+3's copies: the wait
+        // for tile kt+3 (two steps on) then covers them too, so they are in
+        // LDS, behind a barrier, when tile kt+5's copy reads them.  Ring
+        // entry (kt+5) mod 8 last served tile kt-3, copied three steps ago.
+        if (wave == NW - 1 && kt + 5 < kt_end)
+          lds_dma4_sv(g_list + (int64_t)(kt + 5) * kBN, (uint32_t)lane * 4u,
+                      g_idx_lds + (uint32_t)((kt + 5) & 7) * (kBN * 4));
+      }
       if (kt + 3 < kt_end) dma(kt + 3, (stage + 3) & (NS - 1));
     }
     if (!active) return;
@@ -697,10 +790,12 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     const float lt = half_swap_sum(l_run[qb]);
     const int64_t row = wrow0 + qb * 32 + l32;
     if (row >= row0 + nrows) continue;
+    int64_t mrow = row;
+    if constexpr (GATHER) mrow = min((uint32_t)g_qperm[row], (uint32_t)(a.Lq - 1));
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const float lse2 = lt > 0.f ? m_run[qb] + __log2f(lt) : -INFINITY;
     if (a.splits == 1) {
-      uint16_t *op = a.out + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 4;
+      uint16_t *op = a.out + (((int64_t)b * a.Lq + mrow) * a.H + h) * D + hf * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -711,9 +806,9 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
           w.y = pack_bf16(acc[i4 * 4 + 2] * inv, acc[i4 * 4 + 3] * inv);
           *reinterpret_cast<uint2 *>(op + db * 32 + i4 * 8) = w;
         }
-      if (hf == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Lq + row] = lse2 * kLn2;
+      if (hf == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Lq + mrow] = lse2 * kLn2;
     } else {
-      const int64_t prow = (((int64_t)split * a.B + b) * a.H + h) * a.Lq + row;
+      const int64_t prow = (((int64_t)split * a.B + b) * a.H + h) * a.Lq + mrow;
       float *op = a.ws_o + prow * D + hf * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -783,10 +878,10 @@ FwdShape fwd_shape(int D) {
   return FwdShape{8, 1, 64};
 }
 
-template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE>
+template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE, bool GATHER = false>
 hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB, ROPE, SPARSE>), dim3((unsigned)grid), dim3(NW * 64), 0,
-                     s, k);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, NW, QB, MINB, ROPE, SPARSE, GATHER>), dim3((unsigned)grid),
+                     dim3(NW * 64), 0, s, k);
   return hipGetLastError();
 }
 
@@ -880,8 +975,17 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.nbf = a.sel_nbf;
   k.blk_frame = a.sel_per_frame;
   k.n_hist_blocks = a.sel_n_hist_blocks;
+  k.q_perm = a.q_perm;
+  k.gslots = a.gslots;
+  k.lists = a.lists;
+  k.list_len = a.list_len;
+  k.list_cap = a.list_cap;
+  k.cq = a.cq;
   hipError_t e;
-  if (a.D == 128)
+  if (a.gslots != nullptr)
+    e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, p.grid, s)
+                   : launch_fwd<64, 8, 1, 1, false, false, true>(k, p.grid, s);
+  else if (a.D == 128)
     e = a.sel != nullptr ? launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s)
         : a.rope         ? launch_fwd<128, 8, 1, 1, true, false>(k, p.grid, s)
                          : launch_fwd<128, 8, 1, 1, false, false>(k, p.grid, s);

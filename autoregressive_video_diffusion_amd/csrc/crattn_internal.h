@@ -77,6 +77,14 @@ struct AttnArgs {
   // block-sparse attention (hsa_attn): selected block ids per query tile
   const int32_t *sel;
   int sel_kb, sel_nbf, sel_per_frame, sel_n_hist_blocks;
+  // cluster-sparse attention (svg2_attn): query tiles of query clusters,
+  // each with an explicit list of key rows
+  const int32_t *q_perm;    // [B][H][Lq] query row of each reordered position
+  const int32_t *gslots;    // [B][H][n_slots][4] (first position, rows, cluster, 0)
+  const int32_t *lists;     // [B][H][Cq][list_cap] key rows
+  const int32_t *list_len;  // [B][H][Cq]
+  int64_t list_cap;
+  int n_slots, cq, splits;
 };
 
 // Key pooling of whole frames [frame0, frame0 + n_frames) of the cache.
@@ -100,6 +108,41 @@ struct HsaSelectArgs {
   int nf, nbf, n_hist;   // history = frames [0, n_hist)
   int kf, kb, n_qblocks;
   int B, H;
+};
+
+// k-means of one token set per (b, h) and its stable reordering by cluster.
+// Token t of (b, h) is x + b*sb + h*sh + t*sr (bf16).  Per-head outputs sit
+// at stride cent_s / perm_s / off_s elements from one head to the next.
+struct KmArgs {
+  const uint16_t *x;
+  int64_t sb, sh, sr;
+  int B, H, n, C;
+  float *cent;     // [.., C, D]
+  int64_t cent_s;
+  int32_t *perm;   // [.., n]
+  int64_t perm_s;
+  int32_t *off;    // [.., C + 1]
+  int64_t off_s;
+  int32_t *assign;  // workspace [B*H][n]
+  float *norm;      // workspace [B*H][C]
+};
+
+// Centroid top-p selection and key lists of every (b, h, query cluster).
+struct SvgPlanArgs {
+  const float *q_cent;     // [B][H][Cq][D]
+  const int32_t *q_off;    // [B][H][Cq + 1]
+  const float *k_cent;     // [B][H][S][Ck][D]
+  const int32_t *k_off;    // [B][H][S][Ck + 1]
+  const int32_t *k_perm;   // [B][H][S][L]
+  int B, H, Cq, Ck, S, n_vis;
+  int64_t L;
+  float p, scale;
+  int32_t *sel;            // [B][H][Cq][n_vis * Ck] or null
+  int32_t *lists;          // [B][H][Cq][list_cap]
+  int64_t list_cap;
+  int32_t *list_len;       // [B][H][Cq]
+  int32_t *slots;          // [B][H][n_slots][4]
+  int n_slots, qtile;
 };
 
 // Launch plan of one attention call: how query rows are tiled and how the
@@ -129,5 +172,7 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
 hipError_t launch_qkv_rope(const QkvArgs &a, hipStream_t s);
 hipError_t launch_hsa_pool(const HsaPoolArgs &a, int D, hipStream_t s);
 hipError_t launch_hsa_select(const HsaSelectArgs &a, int D, hipStream_t s);
+hipError_t launch_svg2_kmeans(const KmArgs &a, int D, int iters, bool from_tokens, hipStream_t s);
+hipError_t launch_svg2_plan(const SvgPlanArgs &a, int D, hipStream_t s);
 
 }  // namespace crattn

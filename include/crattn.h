@@ -80,6 +80,15 @@ extern "C" {
 #define CRATTN_HSA_MAX_KF 64
 #define CRATTN_HSA_MAX_CAND 4096
 
+/* Semantic-permutation sparse attention: at most 256 clusters and 16384
+ * tokens per k-means call, 64 Lloyd iterations, 1024 key-cluster candidates
+ * per selection; query tiles of 256 rows. */
+#define CRATTN_SVG2_MAX_C 256
+#define CRATTN_SVG2_MAX_N 16384
+#define CRATTN_SVG2_MAX_ITERS 64
+#define CRATTN_SVG2_MAX_CAND 1024
+#define CRATTN_SVG2_QTILE 256
+
 /*
  * Size in bytes of the cos/sin table for head_dim D and position extents
  * (max_t, max_h, max_w): 8 * (max_t*D_t/2 + max_h*D_h/2 + max_w*D_w/2).
@@ -340,6 +349,135 @@ int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int6
 int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
              int64_t q_pos0, int64_t chunk_tokens, int per_frame, const int32_t *sel, int kb,
              void *out, float *lse, int B, int H, int D, int64_t Lq, float scale, void *stream);
+
+/*
+ * Semantic-aware permutation with centroid top-p sparse attention
+ * ["Sparse VideoGen2" §2.A-§2.C]: the queries and the keys of every head are
+ * clustered by k-means, tokens are reordered so that each cluster is
+ * contiguous, each query cluster keeps the key clusters of highest
+ * estimated attention share (centroid scores) until their cumulative share
+ * reaches p, and attention runs densely over the query tiles of a cluster,
+ * loading the kept keys through a list of their rows.  The keys of a cache
+ * are clustered chunk slot by chunk slot (a stored chunk's keys are
+ * clustered once, when stored), the queries of a call as one set.
+ *
+ * Bytes of workspace svg2_kmeans needs (0 for invalid arguments).
+ */
+size_t svg2_kmeans_workspace_bytes(int B, int H, int n, int C);
+
+/*
+ * k-means (Lloyd) on the n tokens of every (b, h), then their stable
+ * reordering by cluster.
+ *
+ *   x           device bf16; token t of (b, h) at x + b*stride_b + h*stride_h
+ *               + t*stride_row elements (strides multiples of 8, x 16-byte
+ *               aligned).  Q [B][Lq][H][D]: (Lq*H*D, D, H*D); one chunk slot
+ *               of a cache [B][H][cap][D]: x = slot's first row, (H*cap*D,
+ *               cap*D, D).
+ *   C, iters    clusters (1..256) and Lloyd iterations (1..64).
+ *   from_tokens 1: centroid c starts at token floor(c n / C); 0: the
+ *               centroids already in `centroids` start (the previous step's).
+ *   centroids   device float, head (b, h) at centroids + (b*H + h)*cent_stride:
+ *               [C][D], in/out.  After the call: the means of the final
+ *               assignment's clusters (an empty cluster keeps its centroid).
+ *   perm        device int32, head at perm + (b*H + h)*perm_stride: [n], the
+ *               token at each reordered position (clusters in id order, tokens
+ *               ascending inside a cluster).
+ *   offsets     device int32, head at offsets + (b*H + h)*off_stride: [C + 1],
+ *               cluster c = positions offsets[c] .. offsets[c+1].
+ *   workspace   device, svg2_kmeans_workspace_bytes(B, H, n, C) bytes.
+ *
+ * Arithmetic: the distance to centroid c is |c|^2 - 2 x.c in fp32 (the
+ * nearest centroid, the lower index on a tie); means are fp32 sums in
+ * reordered order divided by the count.
+ *
+ * Errors: EINVAL for NULL or misaligned pointers, B, H < 1, n outside
+ * [1, 16384], C or iters outside their range, strides not multiples of 8 or
+ * negative, output strides smaller than a head's extent (cent_stride >= C*D
+ * and a multiple of 4, perm_stride >= n, off_stride >= C + 1), a short
+ * workspace; ENOTSUP for D not 64 or 128; EHIP.
+ */
+int svg2_kmeans(const void *x, int64_t stride_b, int64_t stride_h, int64_t stride_row, int B,
+                int H, int n, int D, int C, int iters, int from_tokens, float *centroids,
+                int64_t cent_stride, int32_t *perm, int64_t perm_stride, int32_t *offsets,
+                int64_t off_stride, void *workspace, size_t ws_bytes, void *stream);
+
+/* Query tiles of a call with Lq queries in Cq clusters: ceil(Lq / 256) + Cq
+ * (an upper bound of sum over clusters of ceil(size / 256)); 0 if invalid. */
+int svg2_n_slots(int64_t Lq, int Cq);
+
+/*
+ * Centroid top-p selection and the sparse attention's work lists.
+ *
+ *   q_cent, q_off  the queries' clusters (svg2_kmeans on Q, cent_stride
+ *               Cq*D, off_stride Cq + 1): float [B][H][Cq][D], int32
+ *               [B][H][Cq + 1].
+ *   k_cent, k_off, k_perm  the keys' clusters of S chunk slots of L rows
+ *               each: float [B][H][S][Ck][D], int32 [B][H][S][Ck + 1] and
+ *               [B][H][S][L] (svg2_kmeans per slot).  Slots 0 .. n_vis-1 are
+ *               visible; candidate j = slot j / Ck, cluster j mod Ck; its
+ *               keys are cache rows slot*L + k_perm[..].
+ *   p, scale    top-p threshold (0 < p; p >= 1 keeps every non-empty cluster)
+ *               and the score scale (0: 1/sqrt(D)).
+ *   sel         NULL or device int32 [B][H][Cq][n_vis*Ck]: kept candidates in
+ *               ascending id order, then -1.
+ *   lists       device int32 [B][H][Cq][list_cap]: the key rows of every query
+ *               cluster, kept clusters in id order, each in its reordered
+ *               order; list_len int32 [B][H][Cq] their counts (0 for an empty
+ *               query cluster).  list_cap: a multiple of 64, at least n_vis*L.
+ *   slots       device int32 [B][H][n_slots][4]: query tiles (first reordered
+ *               position, rows <= 256, query cluster, 0), cluster by cluster;
+ *               unused slots have 0 rows.  n_slots >= svg2_n_slots(Lq, Cq).
+ *
+ * Arithmetic: scores s_j = scale qc.kc_j in fp32; share w_j = n_j
+ * exp(s_j - max s) (0 for an empty cluster); candidates ranked by decreasing
+ * share (lower id first on a tie); a candidate is kept while the shares
+ * ranked before it add up to less than p times the total (fp32, fixed
+ * order).
+ *
+ * Errors: EINVAL for NULL or misaligned pointers, B, H, Lq < 1, Cq or Ck
+ * outside [1, 256], n_vis outside [1, S], more than 1024 candidates, L
+ * outside [1, 16384], p not positive, scale negative or not finite, list_cap
+ * or n_slots too small; ENOTSUP for D not 64 or 128; EHIP.
+ */
+int svg2_plan(const float *q_cent, const int32_t *q_off, const float *k_cent,
+              const int32_t *k_off, const int32_t *k_perm, int B, int H, int D, int Cq, int Ck,
+              int S, int n_vis, int64_t L, int64_t Lq, float p, float scale, int32_t *sel,
+              int32_t *lists, int64_t list_cap, int32_t *list_len, int32_t *slots, int n_slots,
+              void *stream);
+
+/* Workspace bytes of svg2_attn with `splits` key-range splits (0 when
+ * splits == 1 or for invalid arguments). */
+size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int splits);
+
+/*
+ * Attention of every query tile over its cluster's key list.
+ *
+ *   q           device bf16 [B][Lq][H][D] (rotated); out the same layout.
+ *   k_cache, v_cache  device bf16 [B][H][cap][D].
+ *   q_perm      device int32 [B][H][Lq]: the query row of each reordered
+ *               position (svg2_kmeans perm of Q).
+ *   slots, n_slots, lists, list_cap, list_len, Cq  svg2_plan's outputs.
+ *   splits      key-range splits per query tile (1..16); with splits > 1 the
+ *               partial results are merged by log-sum-exp in `workspace`
+ *               (svg2_attn_workspace_bytes).
+ *   lse         NULL or device float [B][H][Lq] (natural log).
+ *
+ * Arithmetic: chunk_causal_attn's (bf16 products, fp32 online softmax) over
+ * the listed keys in list order.  Key rows past cap - 1 and query rows past
+ * Lq - 1 are clamped, so no access leaves the buffers; a query row in no
+ * tile is not written.
+ *
+ * Errors: EINVAL for NULL or misaligned pointers, B, H, Lq, cap, n_slots < 1,
+ * Cq outside [1, 256], list_cap not a positive multiple of 64, splits outside
+ * [1, 16], a missing or short workspace, cap * D >= 2^31; ENOTSUP for D not
+ * 64 or 128; EHIP.
+ */
+int svg2_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
+              const int32_t *q_perm, const int32_t *slots, int n_slots, const int32_t *lists,
+              int64_t list_cap, const int32_t *list_len, int Cq, int splits, void *out,
+              float *lse, void *workspace, size_t ws_bytes, int B, int H, int D, int64_t Lq,
+              float scale, void *stream);
 
 /* Message describing the last non-zero return on this thread ("" if none). */
 const char *crattn_last_error(void);

@@ -223,3 +223,85 @@ def _hsa_attn(**kw):
 def test_hsa_attn_rejects(kw, code):
     assert _hsa_attn(**kw) == code
     assert crattn.crattn_last_error() != ""
+
+
+def test_svg2_sizes():
+    # one 480P chunk of keys (4680 tokens) of 12 heads, 64 clusters
+    a = (12 * 4680 * 4 + 255) // 256 * 256
+    assert crattn.svg2_kmeans_workspace_bytes(1, 12, 4680, 64) == a + 12 * 64 * 4
+    assert crattn.svg2_kmeans_workspace_bytes(1, 12, 16385, 64) == 0
+    assert crattn.svg2_kmeans_workspace_bytes(1, 12, 4680, 257) == 0
+    assert crattn.svg2_n_slots(4680, 20) == 19 + 20
+    assert crattn.svg2_n_slots(256, 1) == 2 and crattn.svg2_n_slots(257, 1) == 3
+    assert crattn.svg2_n_slots(0, 1) == 0 and crattn.svg2_n_slots(10, 0) == 0
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 1) == 0
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 4) == 4 * 12 * 4680 * 129 * 4
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 17) == 0
+
+
+def _kmeans(**kw):
+    a = dict(x=FAKE, sb=2 * 64 * 64, sh=64, sr=2 * 64, B=1, H=2, n=64, D=64, C=8, iters=2,
+             init=1, cent=FAKE, cs=8 * 64, perm=FAKE, ps=64, off=FAKE, os=9, ws=FAKE,
+             wsb=1 << 20)
+    a.update(kw)
+    return _lib().svg2_kmeans(a["x"], a["sb"], a["sh"], a["sr"], a["B"], a["H"], a["n"], a["D"],
+                              a["C"], a["iters"], a["init"], a["cent"], a["cs"], a["perm"],
+                              a["ps"], a["off"], a["os"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(ws=None), 1), (dict(x=MIS), 1), (dict(D=96), 2), (dict(n=0), 1),
+    (dict(n=16385), 1), (dict(C=0), 1), (dict(C=257), 1), (dict(iters=0), 1),
+    (dict(iters=65), 1), (dict(sr=100), 1), (dict(sh=-8), 1), (dict(cs=8 * 64 - 4), 1),
+    (dict(cs=8 * 64 + 2), 1), (dict(ps=63), 1), (dict(os=8), 1), (dict(wsb=100), 1),
+    (dict(B=0), 1),
+])
+def test_svg2_kmeans_rejects(kw, code):
+    assert _kmeans(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def _plan(**kw):
+    a = dict(qc=FAKE, qo=FAKE, kc=FAKE, ko=FAKE, kp=FAKE, B=1, H=2, D=64, Cq=4, Ck=8, S=3, nv=2,
+             L=64, Lq=64, p=0.9, scale=0.0, sel=None, lists=FAKE, cap=128, ll=FAKE, slots=FAKE,
+             ns=5)
+    a.update(kw)
+    return _lib().svg2_plan(a["qc"], a["qo"], a["kc"], a["ko"], a["kp"], a["B"], a["H"], a["D"],
+                            a["Cq"], a["Ck"], a["S"], a["nv"], a["L"], a["Lq"], a["p"],
+                            a["scale"], a["sel"], a["lists"], a["cap"], a["ll"], a["slots"],
+                            a["ns"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qc=None), 1), (dict(slots=MIS), 1), (dict(sel=MIS), 1), (dict(D=32), 2),
+    (dict(Cq=0), 1), (dict(Ck=257), 1), (dict(nv=0), 1), (dict(nv=4), 1),
+    (dict(Ck=256, S=5, nv=5), 1),  # 1280 candidates
+    (dict(L=0), 1), (dict(L=16385), 1), (dict(p=0.0), 1), (dict(p=float("nan")), 1),
+    (dict(scale=-1.0), 1), (dict(cap=120), 1), (dict(cap=64), 1), (dict(ns=4), 1),
+    (dict(Lq=0), 1),
+])
+def test_svg2_plan_rejects(kw, code):
+    assert _plan(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def _svg2_attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, qp=FAKE, slots=FAKE, ns=5, lists=FAKE, lc=256,
+             ll=FAKE, Cq=4, splits=1, out=FAKE, lse=None, ws=None, wsb=0, B=1, H=2, D=64, Lq=64,
+             scale=0.0)
+    a.update(kw)
+    return _lib().svg2_attn(a["q"], a["k"], a["v"], a["cap"], a["qp"], a["slots"], a["ns"],
+                            a["lists"], a["lc"], a["ll"], a["Cq"], a["splits"], a["out"], a["lse"],
+                            a["ws"], a["wsb"], a["B"], a["H"], a["D"], a["Lq"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(qp=None), 1), (dict(slots=MIS), 1), (dict(D=96), 2),
+    (dict(ns=0), 1), (dict(Cq=0), 1), (dict(Cq=257), 1), (dict(lc=100), 1), (dict(lc=0), 1),
+    (dict(splits=0), 1), (dict(splits=17), 1), (dict(splits=2), 1),  # no workspace
+    (dict(splits=2, ws=FAKE, wsb=100), 1), (dict(cap=1 << 24, D=128), 1), (dict(scale=-2.0), 1),
+    (dict(Lq=0), 1),
+])
+def test_svg2_attn_rejects(kw, code):
+    assert _svg2_attn(**kw) == code
+    assert crattn.crattn_last_error() != ""
