@@ -398,8 +398,8 @@ def svg2_n_slots(Lq: int, Cq: int) -> int:
 
 def svg2_plan(q_cent: torch.Tensor, q_off: torch.Tensor, k_cent: torch.Tensor,
               k_off: torch.Tensor, k_perm: torch.Tensor, n_vis: int, Lq: int, p: float,
-              lists: torch.Tensor, list_len: torch.Tensor, slots: torch.Tensor,
-              sel: torch.Tensor | None = None, scale: float = 0.0, stream=None):
+              sel: torch.Tensor, lists: torch.Tensor, list_len: torch.Tensor,
+              slots: torch.Tensor, scale: float = 0.0, stream=None):
     """q_cent [B, H, Cq, D] f32, q_off [B, H, Cq+1] i32; k_cent [B, H, S, Ck, D],
     k_off [B, H, S, Ck+1], k_perm [B, H, S, L]; lists [B, H, Cq, list_cap],
     list_len [B, H, Cq], slots [B, H, n_slots, 4], sel [B, H, Cq, n_vis*Ck]
@@ -418,14 +418,13 @@ def svg2_plan(q_cent: torch.Tensor, q_off: torch.Tensor, k_cent: torch.Tensor,
             tuple(list_len.shape) != (B, H, Cq) or slots.dim() != 4 or \
             tuple(slots.shape[:2]) != (B, H) or slots.shape[3] != 4:
         raise ValueError("inconsistent shapes")
-    if sel is not None and (sel.dtype != torch.int32 or
-                            tuple(sel.shape) != (B, H, Cq, n_vis * Ck)):
+    if sel.dtype != torch.int32 or tuple(sel.shape) != (B, H, Cq, n_vis * Ck):
         raise ValueError(f"sel must be int32 [{B}, {H}, {Cq}, {n_vis * Ck}]")
     _raise(load().svg2_plan(_ptr(q_cent), _ptr(q_off), _ptr(k_cent), _ptr(k_off), _ptr(k_perm),
                             B, H, D, Cq, Ck, S, n_vis, L, Lq, float(p), float(scale), _ptr(sel),
                             _ptr(lists), lists.shape[3], _ptr(list_len), _ptr(slots),
                             slots.shape[2], _stream(stream)))
-    return lists, list_len, slots
+    return sel, lists, list_len, slots
 
 
 def svg2_attn_workspace_bytes(B: int, H: int, Lq: int, D: int, splits: int) -> int:

@@ -507,8 +507,9 @@ size_t svg2_kmeans_workspace_bytes(int B, int H, int n, int C) {
   if (B < 1 || H < 1 || n < 1 || n > CRATTN_SVG2_MAX_N || C < 1 || C > CRATTN_SVG2_MAX_C)
     return 0;
   if ((double)B * H * CRATTN_SVG2_MAX_N >= 2147483648.0) return 0;
+  // every token's cluster and rank, then every 128-token block's counts
   const size_t assign = ((size_t)B * H * n * 4u + 255u) & ~size_t(255);
-  return assign + (size_t)B * H * C * 4u;
+  return assign + (size_t)B * H * ((n + 127) / 128) * C * 4u;
 }
 
 int svg2_kmeans(const void *x, int64_t stride_b, int64_t stride_h, int64_t stride_row, int B,
@@ -555,8 +556,8 @@ int svg2_kmeans(const void *x, int64_t stride_b, int64_t stride_h, int64_t strid
   a.off = offsets;
   a.off_s = off_stride;
   a.assign = static_cast<int32_t *>(workspace);
-  a.norm = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                     (((size_t)B * H * n * 4u + 255u) & ~size_t(255)));
+  a.bcnt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                       (((size_t)B * H * n * 4u + 255u) & ~size_t(255)));
   return hip_status(crattn::launch_svg2_kmeans(a, D, iters, from_tokens != 0,
                                                static_cast<hipStream_t>(stream)),
                     "svg2_kmeans launch");
@@ -574,8 +575,9 @@ int svg2_plan(const float *q_cent, const int32_t *q_off, const float *k_cent,
               int32_t *lists, int64_t list_cap, int32_t *list_len, int32_t *slots, int n_slots,
               void *stream) {
   if (q_cent == nullptr || q_off == nullptr || k_cent == nullptr || k_off == nullptr ||
-      k_perm == nullptr || lists == nullptr || list_len == nullptr || slots == nullptr)
-    return fail(CRATTN_EINVAL, "svg2_plan: every pointer but sel is required");
+      k_perm == nullptr || sel == nullptr || lists == nullptr || list_len == nullptr ||
+      slots == nullptr)
+    return fail(CRATTN_EINVAL, "svg2_plan: every pointer is required");
   if (!aligned16(q_cent) || !aligned16(k_cent) || !aligned16(slots) || !aligned16(sel) ||
       !aligned16(lists) || !aligned16(list_len) || !aligned16(q_off) || !aligned16(k_off) ||
       !aligned16(k_perm))

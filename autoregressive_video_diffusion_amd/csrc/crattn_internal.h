@@ -123,8 +123,8 @@ struct KmArgs {
   int64_t perm_s;
   int32_t *off;    // [.., C + 1]
   int64_t off_s;
-  int32_t *assign;  // workspace [B*H][n]
-  float *norm;      // workspace [B*H][C]
+  int32_t *assign;  // workspace [B*H][n]: cluster | rank in its block << 16
+  int32_t *bcnt;    // workspace [B*H][ceil(n/128)][C]: cluster counts per block
 };
 
 // Centroid top-p selection and key lists of every (b, h, query cluster).
@@ -137,7 +137,7 @@ struct SvgPlanArgs {
   int B, H, Cq, Ck, S, n_vis;
   int64_t L;
   float p, scale;
-  int32_t *sel;            // [B][H][Cq][n_vis * Ck] or null
+  int32_t *sel;            // [B][H][Cq][n_vis * Ck]
   int32_t *lists;          // [B][H][Cq][list_cap]
   int64_t list_cap;
   int32_t *list_len;       // [B][H][Cq]

@@ -419,7 +419,7 @@ int svg2_n_slots(int64_t Lq, int Cq);
  *               keys are cache rows slot*L + k_perm[..].
  *   p, scale    top-p threshold (0 < p; p >= 1 keeps every non-empty cluster)
  *               and the score scale (0: 1/sqrt(D)).
- *   sel         NULL or device int32 [B][H][Cq][n_vis*Ck]: kept candidates in
+ *   sel         device int32 [B][H][Cq][n_vis*Ck]: kept candidates in
  *               ascending id order, then -1.
  *   lists       device int32 [B][H][Cq][list_cap]: the key rows of every query
  *               cluster, kept clusters in id order, each in its reordered

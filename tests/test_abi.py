@@ -228,7 +228,7 @@ def test_hsa_attn_rejects(kw, code):
 def test_svg2_sizes():
     # one 480P chunk of keys (4680 tokens) of 12 heads, 64 clusters
     a = (12 * 4680 * 4 + 255) // 256 * 256
-    assert crattn.svg2_kmeans_workspace_bytes(1, 12, 4680, 64) == a + 12 * 64 * 4
+    assert crattn.svg2_kmeans_workspace_bytes(1, 12, 4680, 64) == a + 12 * 37 * 64 * 4
     assert crattn.svg2_kmeans_workspace_bytes(1, 12, 16385, 64) == 0
     assert crattn.svg2_kmeans_workspace_bytes(1, 12, 4680, 257) == 0
     assert crattn.svg2_n_slots(4680, 20) == 19 + 20
@@ -263,7 +263,7 @@ def test_svg2_kmeans_rejects(kw, code):
 
 def _plan(**kw):
     a = dict(qc=FAKE, qo=FAKE, kc=FAKE, ko=FAKE, kp=FAKE, B=1, H=2, D=64, Cq=4, Ck=8, S=3, nv=2,
-             L=64, Lq=64, p=0.9, scale=0.0, sel=None, lists=FAKE, cap=128, ll=FAKE, slots=FAKE,
+             L=64, Lq=64, p=0.9, scale=0.0, sel=FAKE, lists=FAKE, cap=128, ll=FAKE, slots=FAKE,
              ns=5)
     a.update(kw)
     return _lib().svg2_plan(a["qc"], a["qo"], a["kc"], a["ko"], a["kp"], a["B"], a["H"], a["D"],
@@ -273,7 +273,8 @@ def _plan(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(qc=None), 1), (dict(slots=MIS), 1), (dict(sel=MIS), 1), (dict(D=32), 2),
+    (dict(qc=None), 1), (dict(slots=MIS), 1), (dict(sel=MIS), 1), (dict(sel=None), 1),
+    (dict(D=32), 2),
     (dict(Cq=0), 1), (dict(Ck=257), 1), (dict(nv=0), 1), (dict(nv=4), 1),
     (dict(Ck=256, S=5, nv=5), 1),  # 1280 candidates
     (dict(L=0), 1), (dict(L=16385), 1), (dict(p=0.0), 1), (dict(p=float("nan")), 1),

@@ -72,7 +72,7 @@ def _pipeline(q, kc, vc, L, n_vis, Cq, Ck, iters, p, splits=1):
     ns = crattn.svg2_n_slots(Lq, Cq)
     slots = torch.empty(B, H, ns, 4, dtype=torch.int32, device=dev())
     sel = torch.empty(B, H, Cq, n_vis * Ck, dtype=torch.int32, device=dev())
-    crattn.svg2_plan(qcent, qoff, kcent, koff, kperm, n_vis, Lq, p, lists, llen, slots, sel)
+    crattn.svg2_plan(qcent, qoff, kcent, koff, kperm, n_vis, Lq, p, sel, lists, llen, slots)
     out = torch.empty_like(q)
     lse = torch.empty(B, H, Lq, dtype=torch.float32, device=dev())
     wsa = _ws(crattn.svg2_attn_workspace_bytes(B, H, Lq, D, splits)) if splits > 1 else None
