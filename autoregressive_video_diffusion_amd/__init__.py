@@ -123,7 +123,7 @@ def load():
                               _i64, _i64, ctypes.c_float, ctypes.c_float, _vp, _vp, _i64, _vp,
                               _vp, _i32, _vp]
     lib.svg2_plan.restype = _i32
-    lib.svg2_attn_workspace_bytes.argtypes = [_i32, _i32, _i64, _i32, _i32]
+    lib.svg2_attn_workspace_bytes.argtypes = [_i32, _i32, _i64, _i32, _i32, _i32]
     lib.svg2_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.svg2_attn.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _i32, _vp, _i64, _vp, _i32, _i32,
                               _vp, _vp, _vp, ctypes.c_size_t, _i32, _i32, _i32, _i64,
@@ -427,8 +427,8 @@ def svg2_plan(q_cent: torch.Tensor, q_off: torch.Tensor, k_cent: torch.Tensor,
     return sel, lists, list_len, slots
 
 
-def svg2_attn_workspace_bytes(B: int, H: int, Lq: int, D: int, splits: int) -> int:
-    return int(load().svg2_attn_workspace_bytes(B, H, Lq, D, splits))
+def svg2_attn_workspace_bytes(B: int, H: int, Lq: int, D: int, n_slots: int, splits: int) -> int:
+    return int(load().svg2_attn_workspace_bytes(B, H, Lq, D, n_slots, splits))
 
 
 def svg2_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
@@ -437,7 +437,9 @@ def svg2_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
               splits: int = 1, workspace: torch.Tensor | None = None, scale: float = 0.0,
               stream=None) -> torch.Tensor:
     """Attention of the query tiles of `slots` over their clusters' key lists.
-    q, out: [B, Lq, H, D] bf16; caches [B, H, cap, D] bf16; q_perm [B, H, Lq]."""
+    q, out: [B, Lq, H, D] bf16; caches [B, H, cap, D] bf16; q_perm [B, H, Lq];
+    workspace: a device buffer of svg2_attn_workspace_bytes(...) bytes
+    (required: it holds the work counter of the persistent launch)."""
     B, Lq, H, D = q.shape
     cap = k_cache.shape[2]
     if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape):

@@ -628,11 +628,14 @@ int svg2_plan(const float *q_cent, const int32_t *q_off, const float *k_cent,
                     "svg2_plan launch");
 }
 
-size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int splits) {
+size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int n_slots, int splits) {
   if (B < 1 || H < 1 || Lq < 1 || Lq > kMaxElems || (D != 64 && D != 128) || splits < 1 ||
-      splits > 16)
+      splits > 16 || n_slots < 1 || (double)B * H * n_slots >= 1073741824.0)
     return 0;
-  return splits > 1 ? (size_t)splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0;
+  // the work counter and slot count, the work order, then the split partials
+  const size_t order = ((size_t)B * H * n_slots * 4u + 255u) & ~size_t(255);
+  return 256u + order +
+         (splits > 1 ? (size_t)splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0);
 }
 
 int svg2_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
@@ -665,8 +668,8 @@ int svg2_attn(const void *q, const void *k_cache, const void *v_cache, int64_t c
   if ((double)B * H * (double)Lq * (D / 4) >= 4294967296.0 ||
       (double)B * H * (double)n_slots * splits >= 2147483648.0 || Lq >= (int64_t(1) << 31))
     return fail(CRATTN_EINVAL, "svg2_attn: too large for one launch");
-  const size_t need = svg2_attn_workspace_bytes(B, H, Lq, D, splits);
-  if (splits > 1 && (workspace == nullptr || ws_bytes < need))
+  const size_t need = svg2_attn_workspace_bytes(B, H, Lq, D, n_slots, splits);
+  if (workspace == nullptr || ws_bytes < need)
     return fail(CRATTN_EINVAL, "svg2_attn: workspace of %zu bytes, %zu needed", ws_bytes, need);
   crattn::AttnPlan plan{};
   plan.d = D;

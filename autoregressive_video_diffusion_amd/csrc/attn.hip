@@ -80,6 +80,9 @@ struct AttnKArgs {
   const int32_t *list_len;  // [B][H][cq]
   int64_t list_cap;
   int cq;
+  unsigned long long *work;  // next work item (set to the grid size before launch)
+  const int32_t *order;      // (b, h, slot) of the non-empty slots, costliest first
+  const int32_t *n_real;     // their number
 };
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
@@ -210,15 +213,30 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   // Workgroups are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8).
   // Renumber so that consecutive work items -- the query tiles of one head,
   // which stream the same K/V -- land on the same XCD and share its L2.
-  int64_t bid;
-  {
+  // The gather instance is persistent instead: one workgroup per compute
+  // unit takes work items in order from a device counter until none are
+  // left, since its tiles differ widely in cost (list lengths, rows).
+  int64_t item;
+  if constexpr (GATHER) {
+    item = blockIdx.x;
+  } else {
     const int64_t G = gridDim.x;
     const int64_t xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
     const int64_t q = G / kXcds, r = G % kXcds;
-    bid = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    item = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
   }
+  [[maybe_unused]] __shared__ int64_t next_item;
+  [[maybe_unused]] int64_t n_items = 0;
+  if constexpr (GATHER)  // uniform, so the loop below has a uniform exit
+    n_items = (int64_t)__builtin_amdgcn_readfirstlane(*a.n_real) * a.splits;
+  for (;;) {
+  if constexpr (GATHER)
+    if (item >= n_items) break;
+  int64_t bid = item;
   const int split = (int)(bid % a.splits);
   bid /= a.splits;
+  if constexpr (GATHER)  // (b, h, slot), costliest first
+    bid = __builtin_amdgcn_readfirstlane(a.order[bid]);
   const int64_t tile = bid % a.n_tiles;
   bid /= a.n_tiles;
   const int h = (int)(bid % a.H);
@@ -233,15 +251,22 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   [[maybe_unused]] const int32_t *g_list = nullptr;
   [[maybe_unused]] const int32_t *g_qperm = nullptr;
   if constexpr (GATHER) {
+    // an empty (or out of range) slot runs with no rows and no keys
+    // (loads inside the persistent loop are not known to be uniform: the
+    // values are made wave-uniform explicitly)
     const int64_t bhi = (int64_t)b * a.H + h;
-    const int4 sl = reinterpret_cast<const int4 *>(a.gslots)[bhi * a.n_tiles + tile];
-    if (sl.y <= 0 || sl.y > BM || sl.x < 0 || (int64_t)sl.x + sl.y > a.Lq || sl.z < 0 ||
-        sl.z >= a.cq)
-      return;
-    row0 = sl.x;
-    nrows = sl.y;
-    const int64_t li = bhi * a.cq + sl.z;
-    limit = (int)min((int64_t)max(a.list_len[li], 0), a.list_cap);
+    const int4 sv = reinterpret_cast<const int4 *>(a.gslots)[bhi * a.n_tiles + tile];
+    const int4 sl = make_int4(__builtin_amdgcn_readfirstlane(sv.x),
+                              __builtin_amdgcn_readfirstlane(sv.y),
+                              __builtin_amdgcn_readfirstlane(sv.z), 0);
+    const bool ok = !(sl.y <= 0 || sl.y > BM || sl.x < 0 || (int64_t)sl.x + sl.y > a.Lq ||
+                      sl.z < 0 || sl.z >= a.cq);
+    row0 = ok ? sl.x : 0;
+    nrows = ok ? sl.y : 0;
+    const int64_t li = bhi * a.cq + (ok ? sl.z : 0);
+    limit = ok ? (int)min((int64_t)max(__builtin_amdgcn_readfirstlane(a.list_len[li]), 0),
+                          a.list_cap)
+               : 0;
     g_list = a.lists + li * a.list_cap;
     g_qperm = a.q_perm + bhi * a.Lq;
   } else {
@@ -451,30 +476,42 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     g_idx_lds = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(idx_ring));
   }
+  // The byte offsets of one gathered tile are read from the ring a step
+  // before its copy is issued (gather_offsets), so the LDS reads do not sit
+  // between the barrier and the copy.
+  [[maybe_unused]] uint32_t g_off[K_SLOTS + V_SLOTS];
+#pragma unroll
+  for (int n = 0; n < K_SLOTS + V_SLOTS; ++n) g_off[n] = 0;
+  [[maybe_unused]] auto gather_offsets = [&](int kt) {
+    const int last = min(kBN, limit - kt * kBN) - 1;
+    const int *ir = g_idx + (kt & 7) * kBN;
+    const uint32_t rows_max = (uint32_t)a.cap - 1u;
+#pragma unroll
+    for (int n = 0; n < K_SLOTS; ++n) {
+      const int r = min((int)(dma_k_off[n] / kRowBytes), last);
+      g_off[n] = min((uint32_t)ir[r], rows_max) * kRowBytes + dma_k_off[n] % kRowBytes;
+    }
+#pragma unroll
+    for (int n = 0; n < V_SLOTS; ++n) {
+      const int r = min((int)(dma_v_off[n] / kRowBytes), last);
+      g_off[K_SLOTS + n] = min((uint32_t)ir[r], rows_max) * kRowBytes + dma_v_off[n] % kRowBytes;
+    }
+  };
   auto dma = [&](int kt, int stage) {
     const uint32_t kdst = ring_lds + (uint32_t)stage * (STAGE_CELLS * 16);
     const uint32_t vdst = kdst + K_CELLS * 16;
     if constexpr (GATHER) {
-      const int last = min(kBN, limit - kt * kBN) - 1;
-      const int *ir = g_idx + (kt & 7) * kBN;
-      const uint32_t rows_max = (uint32_t)a.cap - 1u;
+      // the offsets of tile kt are in g_off
 #pragma unroll
       for (int n = 0; n < K_SLOTS; ++n) {
         const int j = wave + n * NW;
-        if ((n + 1) * NW <= K_INSTR || j < K_INSTR) {
-          const int r = min((int)(dma_k_off[n] / kRowBytes), last);
-          const uint32_t key = min((uint32_t)ir[r], rows_max);
-          lds_dma16_sv(kh, key * kRowBytes + dma_k_off[n] % kRowBytes, kdst + j * 1024);
-        }
+        if ((n + 1) * NW <= K_INSTR || j < K_INSTR) lds_dma16_sv(kh, g_off[n], kdst + j * 1024);
       }
 #pragma unroll
       for (int n = 0; n < V_SLOTS; ++n) {
         const int j = wave + n * NW;
-        if ((n + 1) * NW <= V_INSTR || j < V_INSTR) {
-          const int r = min((int)(dma_v_off[n] / kRowBytes), last);
-          const uint32_t key = min((uint32_t)ir[r], rows_max);
-          lds_dma16_sv(vh, key * kRowBytes + dma_v_off[n] % kRowBytes, vdst + j * 1024);
-        }
+        if ((n + 1) * NW <= V_INSTR || j < V_INSTR)
+          lds_dma16_sv(vh, g_off[K_SLOTS + n], vdst + j * 1024);
       }
       return;
     }
@@ -652,9 +689,17 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     }
     __syncthreads();
   }
-  if (kt_begin < kt_end) dma(kt_begin, 0);
-  if (kt_begin + 1 < kt_end) dma(kt_begin + 1, 1);
-  if (kt_begin + 2 < kt_end) dma(kt_begin + 2, 2);
+  if constexpr (GATHER) {
+    for (int t = 0; t < 3 && kt_begin + t < kt_end; ++t) {
+      gather_offsets(kt_begin + t);
+      dma(kt_begin + t, t);
+    }
+    if (kt_begin + 3 < kt_end) gather_offsets(kt_begin + 3);
+  } else {
+    if (kt_begin < kt_end) dma(kt_begin, 0);
+    if (kt_begin + 1 < kt_end) dma(kt_begin + 1, 1);
+    if (kt_begin + 2 < kt_end) dma(kt_begin + 2, 2);
+  }
   if (kt_begin + 2 < kt_end)
     wait_vmcnt<2 * kDmaMin>();
   else if (kt_begin + 1 < kt_end)
@@ -694,9 +739,14 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
         // entry (kt+5) mod 8 last served tile kt-3, copied three steps ago.
         if (wave == NW - 1 && kt + 5 < kt_end)
           lds_dma4_sv(g_list + (int64_t)(kt + 5) * kBN, (uint32_t)lane * 4u,
-                      g_idx_lds + (uint32_t)((kt + 5) & 7) * (kBN * 4));
+                      __builtin_amdgcn_readfirstlane(g_idx_lds +
+                                                     (uint32_t)((kt + 5) & 7) * (kBN * 4)));
       }
       if (kt + 3 < kt_end) dma(kt + 3, (stage + 3) & (NS - 1));
+      // (gather) tile kt+4's key rows arrived with the copies of tile kt+2
+      // or earlier and are behind this barrier
+      if constexpr (GATHER)
+        if (kt + 4 < kt_end) gather_offsets(kt + 4);
     }
     if (!active) return;
     f32x16_t (&cur)[KB][QB] = sbuf[par];
@@ -783,10 +833,9 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
     step(kt++, P1{});
   }
 
-  if (!active) return;
   // ---- epilogue: normalise and store ----
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+  for (int qb = 0; qb < QB && active; ++qb) {
     const float lt = half_swap_sum(l_run[qb]);
     const int64_t row = wrow0 + qb * 32 + l32;
     if (row >= row0 + nrows) continue;
@@ -821,6 +870,15 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
         }
       if (hf == 0) a.ws_lse[prow] = lse2;
     }
+  }
+  if constexpr (!GATHER) break;
+  // every wavefront is done with this item's LDS before the next one's
+  // copies start
+  __syncthreads();
+  if (tid == 0) next_item = (int64_t)atomicAdd(a.work, 1ull);
+  __syncthreads();
+  // (item < 2^31: the front end bounds the work count)
+  item = (int64_t)__builtin_amdgcn_readfirstlane((int)min(next_item, (int64_t)0x7fffffff));
   }
 }
 
@@ -876,6 +934,70 @@ struct FwdShape {
 FwdShape fwd_shape(int D) {
   (void)D;
   return FwdShape{8, 1, 64};
+}
+
+// Starts the work counter of a persistent launch at its grid size.
+__global__ void set_counter_kernel(unsigned long long *c, unsigned long long v) { *c = v; }
+
+// Work order of the gather instance: the (b, h, slot) entries with rows,
+// by decreasing key-tile count (a counting sort over 2048 cost bins; the
+// order inside a bin is whatever the atomics give, which changes no
+// result), so the persistent workgroups take the longest tiles first.
+constexpr int kCostBins = 2048;
+
+__global__ void __launch_bounds__(1024) gather_order_kernel(AttnKArgs a, int n_entries) {
+  __shared__ int hist[kCostBins];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int c = tid; c < kCostBins; c += 1024) hist[c] = 0;
+  __syncthreads();
+  // bin (kCostBins - 1 - tiles) of entry e, or -1 without rows
+  auto bin_of = [&](int e) {
+    const int4 sl = reinterpret_cast<const int4 *>(a.gslots)[e];
+    if (sl.y <= 0 || sl.z < 0 || sl.z >= a.cq) return -1;
+    const int64_t bh = e / a.n_tiles;
+    const int len = min(max(a.list_len[bh * a.cq + sl.z], 0), (int)a.list_cap);
+    return kCostBins - 1 - min((len + 63) / 64, kCostBins - 1);
+  };
+  for (int e = tid; e < n_entries; e += 1024) {
+    const int b = bin_of(e);
+    if (b >= 0) atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the bins: two per thread, then over the 16 waves
+  const int h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+  int inc = h0 + h1;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int base = inc - h0 - h1;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  __syncthreads();
+  hist[2 * tid] = base;
+  hist[2 * tid + 1] = base + h0;
+  if (tid == 1023) *const_cast<int32_t *>(a.n_real) = base + h0 + h1;
+  __syncthreads();
+  int32_t *order = const_cast<int32_t *>(a.order);
+  for (int e = tid; e < n_entries; e += 1024) {
+    const int b = bin_of(e);
+    if (b >= 0) order[atomicAdd(&hist[b], 1)] = e;
+  }
+}
+
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n < 1)
+      n = 256;
+  }
+  return n;
 }
 
 template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE, bool GATHER = false>
@@ -981,18 +1103,39 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.list_len = a.list_len;
   k.list_cap = a.list_cap;
   k.cq = a.cq;
+  k.work = nullptr;
+  k.order = nullptr;
+  k.n_real = nullptr;
   hipError_t e;
-  if (a.gslots != nullptr)
-    e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, p.grid, s)
-                   : launch_fwd<64, 8, 1, 1, false, false, true>(k, p.grid, s);
-  else if (a.D == 128)
+  if (a.gslots != nullptr) {
+    // persistent: the workspace holds the work counter and the number of
+    // non-empty slots (first 256 bytes), their order, then the split
+    // partials
+    char *ws = static_cast<char *>(a.workspace);
+    const int64_t n_entries = (int64_t)a.B * a.H * p.n_tiles;
+    const size_t order_bytes = ((size_t)n_entries * 4u + 255u) & ~size_t(255);
+    k.work = reinterpret_cast<unsigned long long *>(ws);
+    k.n_real = reinterpret_cast<const int32_t *>(ws + 8);
+    k.order = reinterpret_cast<const int32_t *>(ws + 256);
+    if (p.splits > 1) {
+      k.ws_o = reinterpret_cast<float *>(ws + 256 + order_bytes);
+      k.ws_lse = reinterpret_cast<float *>(ws + 256 + order_bytes + o_bytes);
+    }
+    const int64_t grid = std::min<int64_t>(p.grid, cu_count());
+    hipLaunchKernelGGL(set_counter_kernel, dim3(1), dim3(1), 0, s, k.work,
+                       (unsigned long long)grid);
+    hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(1024), 0, s, k, (int)n_entries);
+    e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, grid, s)
+                   : launch_fwd<64, 8, 1, 1, false, false, true>(k, grid, s);
+  } else if (a.D == 128) {
     e = a.sel != nullptr ? launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s)
         : a.rope         ? launch_fwd<128, 8, 1, 1, true, false>(k, p.grid, s)
                          : launch_fwd<128, 8, 1, 1, false, false>(k, p.grid, s);
-  else
+  } else {
     e = a.sel != nullptr ? launch_fwd<64, 8, 1, 1, false, true>(k, p.grid, s)
         : a.rope         ? launch_fwd<64, 8, 1, 1, true, false>(k, p.grid, s)
                          : launch_fwd<64, 8, 1, 1, false, false>(k, p.grid, s);
+  }
   if (e != hipSuccess || p.splits == 1) return e;
   CombineArgs c;
   c.ws_o = k.ws_o;

@@ -234,18 +234,19 @@ def time_hsa(crattn, w, b, kf=6, kb=32):
     return pool_ms, sel_ms, attn_ms, fl
 
 
-def time_svg2(crattn, w, b, Cq=20, Ck=64, iters=2, p=0.9, splits=4):
-    """Semantic-permutation sparse attention on the step's chunk (rotated Q'
-    and the 7-chunk cache of buffer set b).  The keys of every chunk slot are
-    clustered first (Ck clusters, from tokens, 3 iterations: a stored
-    chunk's clusters are made once).  Per denoising call: k-means of the own
-    slot's keys and of the queries started from the previous call's
-    centroids (`iters` iterations each), the plan (top-p selection, key
-    lists, query tiles) and the attention over the lists.  Returns
-    per-launch times (ms) and the FLOPs over the listed keys."""
+def time_svg2(crattn, w, q, kc, vc, out, lse, Cq=20, Ck=64, iters=2, p=0.9, splits=2):
+    """Semantic-permutation sparse attention on one chunk's call: rotated
+    queries q [B, lq, H, D] against the cache kc, vc.  The keys of every
+    chunk slot are clustered first (Ck clusters, from tokens, 3 iterations:
+    a stored chunk's clusters are made once).  A denoising call then runs
+    k-means of the own slot's keys and of the queries (on two streams, each
+    started from the previous call's centroids, `iters` iterations), the
+    plan (top-p selection, key lists, query tiles) and the attention over
+    the lists.  Returns per-launch times (ms) of each part and of the whole
+    call, and the FLOPs over the listed keys."""
     import torch
 
-    dev = b.q_out.device
+    dev = q.device
     B, H, D, L, Lq = w.B, w.H, w.D, w.chunk_tokens, w.lq
     S = w.cap // L
     n_vis = w.kv_len // L
@@ -253,58 +254,111 @@ def time_svg2(crattn, w, b, Cq=20, Ck=64, iters=2, p=0.9, splits=4):
     kcent = torch.empty(B, H, S, Ck, D, dtype=torch.float32, device=dev)
     kperm = torch.empty(B, H, S, L, dtype=torch.int32, device=dev)
     koff = torch.empty(B, H, S, Ck + 1, dtype=torch.int32, device=dev)
-    ws = torch.empty(max(crattn.svg2_kmeans_workspace_bytes(B, H, L, Ck),
-                         crattn.svg2_kmeans_workspace_bytes(B, H, Lq, Cq)) // 4 + 4,
-                     dtype=torch.float32, device=dev)
+    wsk = torch.empty(crattn.svg2_kmeans_workspace_bytes(B, H, L, Ck) // 4 + 4,
+                      dtype=torch.float32, device=dev)
+    wsq = torch.empty(crattn.svg2_kmeans_workspace_bytes(B, H, Lq, Cq) // 4 + 4,
+                      dtype=torch.float32, device=dev)
     for s in range(n_vis):
-        crattn.svg2_kmeans(b.kc[:, :, s * L:(s + 1) * L], Ck, 3, True, kcent[:, :, s],
-                           kperm[:, :, s], koff[:, :, s], ws)
+        crattn.svg2_kmeans(kc[:, :, s * L:(s + 1) * L], Ck, 3, True, kcent[:, :, s],
+                           kperm[:, :, s], koff[:, :, s], wsk)
     qcent = torch.empty(B, H, Cq, D, dtype=torch.float32, device=dev)
     qperm = torch.empty(B, H, Lq, dtype=torch.int32, device=dev)
     qoff = torch.empty(B, H, Cq + 1, dtype=torch.int32, device=dev)
-    qv = b.q_out.permute(0, 2, 1, 3)
-    crattn.svg2_kmeans(qv, Cq, 3, True, qcent, qperm, qoff, ws)
+    qv = q.permute(0, 2, 1, 3)
+    crattn.svg2_kmeans(qv, Cq, 3, True, qcent, qperm, qoff, wsq)
     cap_l = -(-n_vis * L // 64) * 64
     lists = torch.empty(B, H, Cq, cap_l, dtype=torch.int32, device=dev)
     llen = torch.empty(B, H, Cq, dtype=torch.int32, device=dev)
     ns = crattn.svg2_n_slots(Lq, Cq)
     slots = torch.empty(B, H, ns, 4, dtype=torch.int32, device=dev)
     sel = torch.empty(B, H, Cq, n_vis * Ck, dtype=torch.int32, device=dev)
-    wsa = torch.empty(max(crattn.svg2_attn_workspace_bytes(B, H, Lq, D, splits), 16) // 4,
+    wsa = torch.empty(crattn.svg2_attn_workspace_bytes(B, H, Lq, D, ns, splits) // 4,
                       dtype=torch.float32, device=dev)
-    ks = b.kc[:, :, own * L:(own + 1) * L]
+    ks = kc[:, :, own * L:(own + 1) * L]
+    side = torch.cuda.Stream(device=dev)  # default priority
+    main = torch.cuda.current_stream(dev)
 
     def key_call(i):
         crattn.svg2_kmeans(ks, Ck, iters, False, kcent[:, :, own], kperm[:, :, own],
-                           koff[:, :, own], ws)
+                           koff[:, :, own], wsk)
 
-    def query_call(i):
-        crattn.svg2_kmeans(qv, Cq, iters, False, qcent, qperm, qoff, ws)
+    def query_call(i, stream=None):
+        crattn.svg2_kmeans(qv, Cq, iters, False, qcent, qperm, qoff, wsq, stream=stream)
 
     def plan_call(i):
         crattn.svg2_plan(qcent, qoff, kcent, koff, kperm, n_vis, Lq, p, sel, lists, llen, slots)
 
     def attn_call(i):
-        crattn.svg2_attn(b.q_out, b.kc, b.vc, qperm, slots, lists, llen, b.out, b.lse, splits,
-                         wsa)
+        crattn.svg2_attn(q, kc, vc, qperm, slots, lists, llen, out, lse, splits, wsa)
+
+    def whole_call(i):
+        # the query k-means on a second stream, overlapping the key k-means
+        side.wait_stream(main)
+        query_call(i, side)
+        key_call(i)
+        main.wait_stream(side)
+        plan_call(i)
+        attn_call(i)
 
     def cold_call(i):
         crattn.svg2_kmeans(ks, Ck, 3, True, kcent[:, :, own], kperm[:, :, own],
-                           koff[:, :, own], ws)
+                           koff[:, :, own], wsk)
 
-    for f in (key_call, query_call, plan_call, attn_call):
+    for f in (key_call, query_call, plan_call, attn_call, whole_call):
         for i in range(3):
             f(i)
     torch.cuda.synchronize()
     t = {"keys": burst_ms(key_call, 5, 10)[2], "queries": burst_ms(query_call, 5, 10)[2],
          "plan": burst_ms(plan_call, 5, 10)[2], "attn": burst_ms(attn_call, 5, 10)[2],
-         "keys_cold": burst_ms(cold_call, 3, 5)[1]}
+         "call": burst_ms(whole_call, 5, 10)[2], "keys_cold": burst_ms(cold_call, 3, 5)[1]}
     key_call(0)  # leave the own slot's clusters warm, as before the timed calls
     plan_call(0)
     torch.cuda.synchronize()
     sizes = (qoff[..., 1:] - qoff[..., :-1]).to(torch.int64).cpu()
     fl = int(4 * D * (sizes * llen.to(torch.int64).cpu()).sum())
     return t, fl
+
+
+def svg2_extras(crattn, w, dev, dense_attn_ms, dense_flops, Cq=20, Ck=64, iters=2, p=0.9,
+                splits=2):
+    """The semantic-permutation call at the step's shape on two inputs:
+    clustered queries and keys (the structure the method relies on) and the
+    step's N(0, 1) inputs (attention nearly uniform, so density ~ p)."""
+    import torch
+
+    from workloads import clustered_qk, prior_cache
+
+    res = {"Cq": Cq, "Ck_per_chunk": Ck, "kmeans_iters_per_call": iters, "p": p,
+           "splits": splits}
+    _, vc = prior_cache(w)
+    vc = vc.to(dev)
+    out = torch.empty(w.B, w.lq, w.H, w.D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(w.B, w.H, w.lq, dtype=torch.float32, device=dev)
+    for tag in ("clustered", "normal"):
+        if tag == "clustered":
+            q, kc = clustered_qk(w)
+        else:
+            q = torch.randn(w.B, w.lq, w.H, w.D, generator=torch.Generator().manual_seed(77),
+                            dtype=torch.float32).to(torch.bfloat16)
+            kc, _ = prior_cache(w)
+        q, kc = q.to(dev), kc.to(dev)
+        t, sfl = time_svg2(crattn, w, q, kc, vc, out, lse, Cq, Ck, iters, p, splits)
+        tf = sfl / (t["attn"] * 1e-3) / 1e12
+        res[tag] = {
+            "density": round(sfl / dense_flops, 4),
+            "kmeans_own_keys_us": round(t["keys"] * 1e3, 1),
+            "kmeans_own_keys_cold_3it_us": round(t["keys_cold"] * 1e3, 1),
+            "kmeans_queries_us": round(t["queries"] * 1e3, 1),
+            "plan_us": round(t["plan"] * 1e3, 1), "attn_us": round(t["attn"] * 1e3, 1),
+            "call_us": round(t["call"] * 1e3, 1), "listed_flops": sfl,
+            "attn_tflops": round(tf, 1),
+            "call_speedup_vs_dense_attn": round(dense_attn_ms / t["call"], 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+        del q, kc
+    del vc, out, lse
+    torch.cuda.empty_cache()
+    return res
 
 
 def fused_step_ms(crattn, w, sets, table, ext, ws, reps=10, rounds=3):
@@ -517,22 +571,7 @@ def main():
             "select_overhead_pct": round(100 * hs_ms / ha_ms, 2),
             "roofline": {"bound": "mfma", "achieved": round(h_tf, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(h_tf / PEAK_BF16_TFLOPS, 4)}}
-        sv, sv_fl = time_svg2(crattn, w, sets[0])
-        sv_tf = sv_fl / (sv["attn"] * 1e-3) / 1e12
-        sv_call = sv["keys"] + sv["queries"] + sv["plan"] + sv["attn"]
-        extras["svg2_480"] = {
-            "Cq": 20, "Ck_per_chunk": 64, "kmeans_iters_warm": 2, "p": 0.9, "splits": 4,
-            "density": round(sv_fl / fl, 4),
-            "kmeans_own_keys_us": round(sv["keys"] * 1e3, 2),
-            "kmeans_own_keys_cold_3it_us": round(sv["keys_cold"] * 1e3, 2),
-            "kmeans_queries_us": round(sv["queries"] * 1e3, 2),
-            "plan_us": round(sv["plan"] * 1e3, 2), "attn_ms": round(sv["attn"], 4),
-            "call_ms": round(sv_call, 4), "listed_flops": sv_fl,
-            "attn_tflops": round(sv_tf, 1),
-            "speedup_vs_dense_attn": round(attn_ms / sv_call, 2),
-            "roofline": {"bound": "mfma", "achieved": round(sv_tf, 1),
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(sv_tf / PEAK_BF16_TFLOPS, 4)}}
+        extras["svg2_480"] = svg2_extras(crattn, w, dev, attn_ms, fl)
         plain_ms, fused_ms = fused_step_ms(crattn, w, sets, table, ext, ws)
         extras["step_plain_vs_fused_qrot_ms"] = [round(plain_ms, 4), round(fused_ms, 4)]
         extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)

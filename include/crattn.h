@@ -446,9 +446,11 @@ int svg2_plan(const float *q_cent, const int32_t *q_off, const float *k_cent,
               int32_t *lists, int64_t list_cap, int32_t *list_len, int32_t *slots, int n_slots,
               void *stream);
 
-/* Workspace bytes of svg2_attn with `splits` key-range splits (0 when
- * splits == 1 or for invalid arguments). */
-size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int splits);
+/* Workspace bytes of svg2_attn with n_slots query tiles per head and
+ * `splits` key-range splits: 256 (the work counter of its persistent
+ * launch), the work order (4 bytes per slot, rounded up to 256) and the
+ * split partials; 0 for invalid arguments. */
+size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int n_slots, int splits);
 
 /*
  * Attention of every query tile over its cluster's key list.
@@ -459,8 +461,14 @@ size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int splits);
  *               position (svg2_kmeans perm of Q).
  *   slots, n_slots, lists, list_cap, list_len, Cq  svg2_plan's outputs.
  *   splits      key-range splits per query tile (1..16); with splits > 1 the
- *               partial results are merged by log-sum-exp in `workspace`
- *               (svg2_attn_workspace_bytes).
+ *               partial results are merged by log-sum-exp.
+ *   workspace   device, svg2_attn_workspace_bytes(B, H, Lq, D, n_slots, splits)
+ *               bytes, 16-byte aligned (a work counter, the work order, the
+ *               partials).  Calls that overlap on one workspace race.
+ *
+ * Launch: one workgroup per compute unit takes the non-empty query tiles,
+ * longest key list first, from a counter in the workspace (reset by the
+ * call) until none are left.
  *   lse         NULL or device float [B][H][Lq] (natural log).
  *
  * Arithmetic: chunk_causal_attn's (bf16 products, fp32 online softmax) over

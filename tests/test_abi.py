@@ -234,9 +234,12 @@ def test_svg2_sizes():
     assert crattn.svg2_n_slots(4680, 20) == 19 + 20
     assert crattn.svg2_n_slots(256, 1) == 2 and crattn.svg2_n_slots(257, 1) == 3
     assert crattn.svg2_n_slots(0, 1) == 0 and crattn.svg2_n_slots(10, 0) == 0
-    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 1) == 0
-    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 4) == 4 * 12 * 4680 * 129 * 4
-    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 17) == 0
+    order = (12 * 39 * 4 + 255) // 256 * 256
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 39, 1) == 256 + order
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 39, 4) == \
+        256 + order + 4 * 12 * 4680 * 129 * 4
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 39, 17) == 0
+    assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 0, 1) == 0
 
 
 def _kmeans(**kw):
@@ -288,8 +291,8 @@ def test_svg2_plan_rejects(kw, code):
 
 def _svg2_attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, qp=FAKE, slots=FAKE, ns=5, lists=FAKE, lc=256,
-             ll=FAKE, Cq=4, splits=1, out=FAKE, lse=None, ws=None, wsb=0, B=1, H=2, D=64, Lq=64,
-             scale=0.0)
+             ll=FAKE, Cq=4, splits=1, out=FAKE, lse=None, ws=FAKE, wsb=512, B=1, H=2, D=64,
+             Lq=64, scale=0.0)
     a.update(kw)
     return _lib().svg2_attn(a["q"], a["k"], a["v"], a["cap"], a["qp"], a["slots"], a["ns"],
                             a["lists"], a["lc"], a["ll"], a["Cq"], a["splits"], a["out"], a["lse"],
@@ -299,7 +302,8 @@ def _svg2_attn(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(qp=None), 1), (dict(slots=MIS), 1), (dict(D=96), 2),
     (dict(ns=0), 1), (dict(Cq=0), 1), (dict(Cq=257), 1), (dict(lc=100), 1), (dict(lc=0), 1),
-    (dict(splits=0), 1), (dict(splits=17), 1), (dict(splits=2), 1),  # no workspace
+    (dict(splits=0), 1), (dict(splits=17), 1), (dict(splits=2), 1),  # short workspace
+    (dict(ws=None), 1), (dict(wsb=511), 1),
     (dict(splits=2, ws=FAKE, wsb=100), 1), (dict(cap=1 << 24, D=128), 1), (dict(scale=-2.0), 1),
     (dict(Lq=0), 1),
 ])

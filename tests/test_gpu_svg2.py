@@ -75,7 +75,7 @@ def _pipeline(q, kc, vc, L, n_vis, Cq, Ck, iters, p, splits=1):
     crattn.svg2_plan(qcent, qoff, kcent, koff, kperm, n_vis, Lq, p, sel, lists, llen, slots)
     out = torch.empty_like(q)
     lse = torch.empty(B, H, Lq, dtype=torch.float32, device=dev())
-    wsa = _ws(crattn.svg2_attn_workspace_bytes(B, H, Lq, D, splits)) if splits > 1 else None
+    wsa = _ws(crattn.svg2_attn_workspace_bytes(B, H, Lq, D, ns, splits))
     crattn.svg2_attn(q, kc, vc, qperm, slots, lists, llen, out, lse, splits, wsa)
     torch.cuda.synchronize()
     return dict(kcent=kcent, kperm=kperm, koff=koff, qcent=qcent, qperm=qperm, qoff=qoff,
@@ -319,7 +319,8 @@ def test_keys_outside_the_lists_are_never_read():
     kc2[~used.to(dev())] = float("nan")
     vc2[~used.to(dev())] = float("nan")
     out2 = torch.empty_like(q)
-    crattn.svg2_attn(q, kc2, vc2, r["qperm"], r["slots"], r["lists"], r["llen"], out2)
+    crattn.svg2_attn(q, kc2, vc2, r["qperm"], r["slots"], r["lists"], r["llen"], out2,
+                     workspace=r["wsa"])
     torch.cuda.synchronize()
     assert torch.equal(out2, r["out"])
 
@@ -354,3 +355,48 @@ def test_480p_chunk_pipeline_sampled():
         o_ref, _ = svg2.attn(q64[0, :, h], k64, v64, groups)
         rows = np.concatenate([g[0] for g in groups])
         assert_attn_close(got[0, rows, h], o_ref[rows], f"480P h{h}")
+
+
+# ------------------------------------------------------------ rollout
+
+@pytest.mark.parametrize("p", [0.7, 1.0])
+def test_rollout_with_svg2_through_a_full_ring(p):
+    # six one-frame chunks (8x8) through a ring of 4 slots; every denoising
+    # call is checked against the oracle over the rollout's own lists, and
+    # with p = 1 against the dense attention of the visible cache
+    from autoregressive_video_diffusion_amd.rollout import ChunkRollout
+
+    B, H, D, gh, gw = 1, 2, 64, 8, 8
+    ro = ChunkRollout(B, H, D, 1, gh, gw, window=4, max_chunks=7, device=dev(),
+                      svg2=(3, 4, p))
+    L = ro.L
+    for c in range(6):
+        for step in range(2):
+            q = normal((B, L, H, D), 800 + 5 * c + step).to(dev())
+            k = normal((B, L, H, D), 820 + 5 * c + step).to(dev())
+            v = normal((B, L, H, D), 840 + 5 * c + step).to(dev())
+            q_out, out = torch.empty_like(q), torch.empty_like(q)
+            ro.denoise(c, q, k, v, q_out, out)
+            torch.cuda.synchronize()
+            n_vis = min(c + 1, 4)
+            q64, k64, v64 = f64(q_out), f64(ro.k_cache), f64(ro.v_cache)
+            for h in range(H):
+                qperm, qoff = ro.qperm[0, h].cpu().numpy(), ro.qoff[0, h].cpu().numpy()
+                groups = []
+                for i in range(3):
+                    if qoff[i + 1] > qoff[i]:
+                        keys = ro.lists[0, h, i, :int(ro.llen[0, h, i])].cpu().numpy()
+                        assert (keys >= 0).all() and (keys < n_vis * L).all()
+                        if p == 1.0:
+                            assert len(keys) == n_vis * L
+                        groups.append((qperm[qoff[i]:qoff[i + 1]], keys.astype(np.int64)))
+                o_ref, _ = svg2.attn(q64[0, :, h], k64[0, h], v64[0, h], groups)
+                assert_attn_close(f64(out[0, :, h]), o_ref, f"svg2 rollout c{c} s{step} h{h}")
+            if p == 1.0:
+                kv_len, q0 = ro.visible(c)
+                o_d, _ = oracle.attn(q64, k64, v64, kv_len, q0, L)
+                assert_attn_close(f64(out), o_d, f"svg2 rollout p=1 c{c}")
+        ro.update(c, k, v)
+    with pytest.raises(NotImplementedError):
+        q = normal((B, L // 2, H, D), 900).to(dev())
+        ro.denoise(6, q, q, q, torch.empty_like(q), torch.empty_like(q), tok_off=L // 2)

@@ -152,3 +152,22 @@ def planted_clusters(batch_shape, n: int, C: int, D: int, seed: int, spread: flo
     x = torch.gather(centres, 1, labels[..., None].expand(nb, n, D)) + spread * noise
     x = x.reshape(*batch_shape, n, D)
     return (x if dtype == torch.float32 else x.to(dtype)), labels.reshape(*batch_shape, n)
+
+
+def clustered_qk(w: Workload, n_qc: int = 20, n_kc: int = 64, scale: float = 1.6,
+                 noise: float = 0.3, seed: int = 0):
+    """Queries and cache keys with semantic structure: in every head the
+    chunk's queries fall into n_qc groups and every chunk slot's keys into
+    n_kc groups (planted_clusters), each token = scale * (its group's N(0, 1)
+    centre) + noise * N(0, 1).  Returns q [B, lq, H, D] and k [B, H, cap, D]
+    (bf16; every slot of the cache filled)."""
+    L = w.chunk_tokens
+    qh, _ = planted_clusters((w.B, w.H), w.lq, n_qc, w.D, 7000 + seed, spread=noise / scale,
+                             dtype=torch.float32)
+    q = (qh * scale).permute(0, 2, 1, 3).contiguous().to(torch.bfloat16)
+    k = torch.empty(w.B, w.H, w.cap, w.D, dtype=torch.bfloat16)
+    for s in range(w.cap // L):
+        kh, _ = planted_clusters((w.B, w.H), L, n_kc, w.D, 7100 + seed + s, spread=noise / scale,
+                                 dtype=torch.float32)
+        k[:, :, s * L:(s + 1) * L] = (kh * scale).to(torch.bfloat16)
+    return q, k
