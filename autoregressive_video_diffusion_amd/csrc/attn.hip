@@ -936,19 +936,19 @@ FwdShape fwd_shape(int D) {
   return FwdShape{8, 1, 64};
 }
 
-// Starts the work counter of a persistent launch at its grid size.
-__global__ void set_counter_kernel(unsigned long long *c, unsigned long long v) { *c = v; }
-
 // Work order of the gather instance: the (b, h, slot) entries with rows,
 // by decreasing key-tile count (a counting sort over 2048 cost bins; the
 // order inside a bin is whatever the atomics give, which changes no
 // result), so the persistent workgroups take the longest tiles first.
 constexpr int kCostBins = 2048;
 
-__global__ void __launch_bounds__(1024) gather_order_kernel(AttnKArgs a, int n_entries) {
+// It also starts the work counter at the persistent grid's size.
+__global__ void __launch_bounds__(1024) gather_order_kernel(AttnKArgs a, int n_entries,
+                                                            unsigned long long grid) {
   __shared__ int hist[kCostBins];
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) *a.work = grid;
   for (int c = tid; c < kCostBins; c += 1024) hist[c] = 0;
   __syncthreads();
   // bin (kCostBins - 1 - tiles) of entry e, or -1 without rows
@@ -1122,9 +1122,8 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
       k.ws_lse = reinterpret_cast<float *>(ws + 256 + order_bytes + o_bytes);
     }
     const int64_t grid = std::min<int64_t>(p.grid, cu_count());
-    hipLaunchKernelGGL(set_counter_kernel, dim3(1), dim3(1), 0, s, k.work,
+    hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(1024), 0, s, k, (int)n_entries,
                        (unsigned long long)grid);
-    hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(1024), 0, s, k, (int)n_entries);
     e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, grid, s)
                    : launch_fwd<64, 8, 1, 1, false, false, true>(k, grid, s);
   } else if (a.D == 128) {

@@ -316,6 +316,31 @@ __global__ void __launch_bounds__(256) svg2_update_kernel(KmArgs a) {
   }
 }
 
+// ---- query tiles: every query cluster split into tiles of qtile rows, in
+// cluster order; unused slots get zero rows.  Run by the first wave of the
+// first query cluster's workgroup of each (b, h). ----
+__device__ void write_query_tiles(const SvgPlanArgs &a, int64_t bh, int lane) {
+  const int32_t *qo = a.q_off + bh * (a.Cq + 1);
+  int4 *sl = reinterpret_cast<int4 *>(a.slots) + bh * a.n_slots;
+  int base = 0;
+  for (int i0 = 0; i0 < a.Cq; i0 += 64) {
+    const int i = i0 + lane;
+    const int cnt = i < a.Cq ? max(qo[i + 1] - qo[i], 0) : 0;
+    const int nt = (cnt + a.qtile - 1) / a.qtile;
+    int inc = nt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    const int first = base + inc - nt;
+    for (int t = 0; t < nt && first + t < a.n_slots; ++t)
+      sl[first + t] = make_int4(qo[i] + t * a.qtile, min(a.qtile, cnt - t * a.qtile), i, 0);
+    base += __shfl(inc, 63, 64);
+  }
+  for (int s = base + lane; s < a.n_slots; s += 64) sl[s] = make_int4(0, 0, 0, 0);
+}
+
 // ---- selection and key list of one (b, h, query cluster) ----
 // Scores of the candidates (4 lanes per candidate); shares
 // w_j = n_j exp(s_j - max s); the candidates in decreasing share (ties:
@@ -355,6 +380,7 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
     const int64_t e = min(max((int64_t)koff[s * (a.Ck + 1) + c + 1], (int64_t)0), a.L);
     return (int)max(e - start_of(j), (int64_t)0);
   };
+  if (i == 0 && wave == 0) write_query_tiles(a, bh, lane);
   if (qo[i + 1] <= qo[i]) {
     if (tid == 0) a.list_len[bh * a.Cq + i] = 0;
     for (int e = tid; e < NC; e += 256) sel[e] = -1;
@@ -579,32 +605,6 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
   }
 }
 
-// ---- query tiles: every query cluster split into tiles of qtile rows, in
-// cluster order; unused slots get zero rows.  One wave per (b, h). ----
-__global__ void __launch_bounds__(64) svg2_slots_kernel(SvgPlanArgs a) {
-  const int64_t bh = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int32_t *qo = a.q_off + bh * (a.Cq + 1);
-  int4 *sl = reinterpret_cast<int4 *>(a.slots) + bh * a.n_slots;
-  int base = 0;
-  for (int i0 = 0; i0 < a.Cq; i0 += 64) {
-    const int i = i0 + lane;
-    const int cnt = i < a.Cq ? max(qo[i + 1] - qo[i], 0) : 0;
-    const int nt = (cnt + a.qtile - 1) / a.qtile;
-    int inc = nt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += y;
-    }
-    const int first = base + inc - nt;
-    for (int t = 0; t < nt && first + t < a.n_slots; ++t)
-      sl[first + t] = make_int4(qo[i] + t * a.qtile, min(a.qtile, cnt - t * a.qtile), i, 0);
-    base += __shfl(inc, 63, 64);
-  }
-  for (int s = base + lane; s < a.n_slots; s += 64) sl[s] = make_int4(0, 0, 0, 0);
-}
-
 template <int D>
 hipError_t kmeans_d(const KmArgs &a, int iters, bool from_tokens, hipStream_t s) {
   const unsigned gc = (unsigned)((int64_t)a.B * a.H * a.C);
@@ -640,7 +640,6 @@ hipError_t launch_svg2_plan(const SvgPlanArgs &a, int D, hipStream_t s) {
     hipLaunchKernelGGL(svg2_select_kernel<128>, dim3(gq), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(svg2_select_kernel<64>, dim3(gq), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(svg2_slots_kernel, dim3((unsigned)((int64_t)a.B * a.H)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -479,6 +479,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--svg2-only", action="store_true",
+                    help="only the semantic-permutation call (for profiling it)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -498,6 +500,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = STEP480
+    if args.svg2_only:
+        fl = attn_flops(w.B, w.H, w.lq, w.kv_len, w.D)
+        print(json.dumps({"svg2_480": svg2_extras(crattn, w, dev, float("nan"), fl)}))
+        return
     table, ext = make_table(w, dev)
     sets = [StepBuffers(w, dev, i) for i in range(args.sets)]
     wsb = crattn.chunk_causal_attn_workspace_bytes(w.B, w.H, w.lq, w.kv_len, w.q_pos0,
