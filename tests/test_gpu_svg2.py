@@ -400,3 +400,40 @@ def test_rollout_with_svg2_through_a_full_ring(p):
     with pytest.raises(NotImplementedError):
         q = normal((B, L // 2, H, D), 900).to(dev())
         ro.denoise(6, q, q, q, torch.empty_like(q), torch.empty_like(q), tok_off=L // 2)
+
+
+def test_720p_window_pipeline_sampled():
+    # the 720P window: 40 heads, 10800 queries (40 clusters) against a full
+    # ring of 7 slots of 10800 keys (64 clusters each, 448 candidates),
+    # clustered inputs; selections checked for validity on two heads, the
+    # attention on sampled rows of three
+    from workloads import WIN720, clustered_qk
+
+    w = WIN720
+    Cq, Ck, p, L, n_vis = 40, 64, 0.9, w.chunk_tokens, w.cap // w.chunk_tokens
+    q, kc = clustered_qk(w, n_qc=Cq, n_kc=Ck)
+    q, kc = q.to(dev()), kc.to(dev())
+    vc = normal((w.B, w.H, w.cap, w.D), 95).to(dev())
+    r = _pipeline(q, kc, vc, L, n_vis, Cq, Ck, 2, p, splits=2)
+    assert torch.isfinite(r["out"].float()).all()
+    dens = float(r["llen"].double().mean()) / (n_vis * L)
+    print(f"  720P mean list density {dens:.3f}")
+    for h in (0, 39):
+        _check_selection(r, 0, h, n_vis, Ck, L, p, 1.0 / np.sqrt(w.D))
+        _check_slots(r, 0, h, L)
+    rng = np.random.default_rng(7)
+    q64, got = f64(q), f64(r["out"])
+    for h in (3, 20, 38):
+        qperm, qoff = r["qperm"][0, h].cpu().numpy(), r["qoff"][0, h].cpu().numpy()
+        k64, v64 = f64(kc[0, h]), f64(vc[0, h])
+        groups = []
+        for i in rng.choice(Cq, 3, replace=False):
+            rows = qperm[qoff[i]:qoff[i + 1]]
+            if len(rows) == 0:
+                continue
+            rows = rng.choice(rows, min(6, len(rows)), replace=False)
+            keys = r["lists"][0, h, i, :int(r["llen"][0, h, i])].cpu().numpy().astype(np.int64)
+            groups.append((rows, keys))
+        o_ref, _ = svg2.attn(q64[0, :, h], k64, v64, groups)
+        rows = np.concatenate([g[0] for g in groups])
+        assert_attn_close(got[0, rows, h], o_ref[rows], f"720P h{h}")
