@@ -437,3 +437,74 @@ def test_720p_window_pipeline_sampled():
         o_ref, _ = svg2.attn(q64[0, :, h], k64, v64, groups)
         rows = np.concatenate([g[0] for g in groups])
         assert_attn_close(got[0, rows, h], o_ref[rows], f"720P h{h}")
+
+
+# ------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("n,C,D", [(10, 16, 64), (1, 3, 128), (57, 1, 128), (200, 200, 64)])
+def test_kmeans_degenerate_sizes(n, C, D):
+    # more clusters than tokens (duplicate starting centroids: the lower index
+    # takes the ties, the rest stay empty and keep their centroid), a single
+    # token, a single cluster, one token per cluster
+    B, H = 1, 2
+    x = normal((B, H, n, D), 300 + n + C).to(dev())
+    cent, perm, off = _kmeans(x, C, 2)
+    x64 = f64(x)
+    for h in range(H):
+        p, o = perm[0, h].cpu().numpy(), off[0, h].cpu().numpy()
+        assert sorted(p.tolist()) == list(range(n)) and o[0] == 0 and o[-1] == n
+        assert (np.diff(o) >= 0).all()
+        for c in range(C):
+            m = p[o[c]:o[c + 1]]
+            assert (np.diff(m) > 0).all()
+            if len(m):
+                tol = (len(m) + 2) * EPS * np.abs(x64[0, h]).max()
+                assert (np.abs(f64(cent[0, h, c]) - x64[0, h][m].mean(0)) <= tol).all()
+        if C == 1:
+            np.testing.assert_allclose(f64(cent[0, h, 0]), x64[0, h].mean(0), atol=1e-5)
+
+
+def test_kmeans_largest_sizes():
+    # 16384 tokens, 256 clusters (the LDS-staged maximum of both kernels):
+    # one Lloyd step is valid against its known starting centroids
+    B, H, n, C, D = 1, 2, 16384, 256, 128
+    x = normal((B, H, n, D), 310).to(dev())
+    cent, perm, off = _kmeans(x, C, 1)
+    x64 = f64(x)
+    for h in range(H):
+        xs = x64[0, h]
+        c0 = xs[[c * n // C for c in range(C)]]
+        p, o = perm[0, h].cpu().numpy(), off[0, h].cpu().numpy()
+        assert sorted(p.tolist()) == list(range(n))
+        assign = np.empty(n, dtype=np.int64)
+        for c in range(C):
+            assert (np.diff(p[o[c]:o[c + 1]]) > 0).all()
+            assign[p[o[c]:o[c + 1]]] = c
+        e = (c0 ** 2).sum(1)[None, :] - 2.0 * xs @ c0.T
+        bound = 4 * (D + 2) * EPS * (np.abs(xs) @ np.abs(c0).T + (c0 ** 2).sum(1)[None, :])
+        assert (e[np.arange(n), assign] <= e.min(1) + bound.max(1)).all()
+
+
+@pytest.mark.parametrize("Cq,Ck,n_vis,p", [(1, 256, 4, 0.9), (5, 8, 3, 1e-6), (3, 64, 2, 0.999)])
+def test_plan_extremes(Cq, Ck, n_vis, p):
+    # one query cluster with 1024 candidates (the maximum), a p so small that
+    # one key cluster is kept per query cluster, and a p just below 1
+    B, H, L, D = 1, 2, 320, 64
+    Lq = 200
+    q = normal((B, Lq, H, D), 320).to(dev())
+    kc = normal((B, H, n_vis * L, D), 321).to(dev())
+    vc = normal((B, H, n_vis * L, D), 322).to(dev())
+    r = _pipeline(q, kc, vc, L, n_vis, Cq, Ck, 2, p)
+    for h in range(H):
+        _check_selection(r, 0, h, n_vis, Ck, L, p, 1.0 / np.sqrt(D))
+        _check_slots(r, 0, h, Lq)
+        if p < 1e-3:
+            assert ((r["sel"][0, h] >= 0).sum(-1).cpu() <= 1).all()
+    q64, k64, v64, got = f64(q), f64(kc), f64(vc), f64(r["out"])
+    for h in range(H):
+        qperm, qoff = r["qperm"][0, h].cpu().numpy(), r["qoff"][0, h].cpu().numpy()
+        groups = [(qperm[qoff[i]:qoff[i + 1]],
+                   r["lists"][0, h, i, :int(r["llen"][0, h, i])].cpu().numpy().astype(np.int64))
+                  for i in range(Cq) if qoff[i + 1] > qoff[i]]
+        o_ref, _ = svg2.attn(q64[0, :, h], k64[0, h], v64[0, h], groups)
+        assert_attn_close(got[0, :, h], o_ref, f"plan extremes h{h}")
