@@ -311,6 +311,17 @@ def time_svg2(crattn, w, q, kc, vc, out, lse, Cq=20, Ck=64, iters=2, p=0.9, spli
     t = {"keys": burst_ms(key_call, 5, 10)[2], "queries": burst_ms(query_call, 5, 10)[2],
          "plan": burst_ms(plan_call, 5, 10)[2], "attn": burst_ms(attn_call, 5, 10)[2],
          "call": burst_ms(whole_call, 5, 10)[2], "keys_cold": burst_ms(cold_call, 3, 5)[1]}
+    # the same call captured once in a HIP graph and replayed (its ~15
+    # launches then cost no host-side launch time)
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        whole_call(0)
+    for i in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    t["call_graph"] = burst_ms(lambda i: graph.replay(), 5, 10)[2]
+    del graph
     key_call(0)  # leave the own slot's clusters warm, as before the timed calls
     plan_call(0)
     torch.cuda.synchronize()
@@ -350,7 +361,8 @@ def svg2_extras(crattn, w, dev, dense_attn_ms, dense_flops, Cq=20, Ck=64, iters=
             "kmeans_own_keys_cold_3it_us": round(t["keys_cold"] * 1e3, 1),
             "kmeans_queries_us": round(t["queries"] * 1e3, 1),
             "plan_us": round(t["plan"] * 1e3, 1), "attn_us": round(t["attn"] * 1e3, 1),
-            "call_us": round(t["call"] * 1e3, 1), "listed_flops": sfl,
+            "call_us": round(t["call"] * 1e3, 1),
+            "call_graph_replay_us": round(t["call_graph"] * 1e3, 1), "listed_flops": sfl,
             "attn_tflops": round(tf, 1),
             "call_speedup_vs_dense_attn": round(dense_attn_ms / t["call"], 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,

@@ -508,3 +508,66 @@ def test_plan_extremes(Cq, Ck, n_vis, p):
                   for i in range(Cq) if qoff[i + 1] > qoff[i]]
         o_ref, _ = svg2.attn(q64[0, :, h], k64[0, h], v64[0, h], groups)
         assert_attn_close(got[0, :, h], o_ref, f"plan extremes h{h}")
+
+
+def test_svg2_call_replays_from_a_hip_graph():
+    # the whole denoising call (k-means of the own slot's keys and of the
+    # queries on two streams, plan, attention) captured once and replayed:
+    # each replay, started from the same centroids as an eager call, gives
+    # the eager call's output bit for bit (no memset nodes: the kernels
+    # clear their own counters)
+    B, H, D, L, n_vis, Cq, Ck, p = 1, 2, 128, 320, 3, 4, 8, 0.6
+    q = normal((B, L, H, D), 330).to(dev())
+    kc = normal((B, H, n_vis * L, D), 331).to(dev())
+    vc = normal((B, H, n_vis * L, D), 332).to(dev())
+    r = _pipeline(q, kc, vc, L, n_vis, Cq, Ck, 2, p, splits=2)
+    kcent, kperm, koff = r["kcent"], r["kperm"], r["koff"]
+    qcent, qperm, qoff = r["qcent"], r["qperm"], r["qoff"]
+    own = n_vis - 1
+    ws_k = _ws(max(crattn.svg2_kmeans_workspace_bytes(B, H, L, Ck),
+                   crattn.svg2_kmeans_workspace_bytes(B, H, L, Cq)))
+    ws_q = _ws(crattn.svg2_kmeans_workspace_bytes(B, H, L, Cq))
+    ks = kc[:, :, own * L:(own + 1) * L]
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream(device=dev())
+
+    def call():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        crattn.svg2_kmeans(q.permute(0, 2, 1, 3), Cq, 1, False, qcent, qperm, qoff, ws_q,
+                           stream=side)
+        crattn.svg2_kmeans(ks, Ck, 1, False, kcent[:, :, own], kperm[:, :, own],
+                           koff[:, :, own], ws_k)
+        main.wait_stream(side)
+        crattn.svg2_plan(qcent, qoff, kcent, koff, kperm, n_vis, L, p, r["sel"], r["lists"],
+                         r["llen"], r["slots"])
+        crattn.svg2_attn(q, kc, vc, qperm, r["slots"], r["lists"], r["llen"], out, None, 2,
+                         r["wsa"])
+
+    state = [t.clone() for t in (kcent, qcent)]
+
+    def restore():
+        kcent.copy_(state[0])
+        qcent.copy_(state[1])
+
+    restore()
+    call()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        out.zero_()
+        restore()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep}"
+        # eager work between the replays
+        restore()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
