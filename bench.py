@@ -145,6 +145,31 @@ def time_attn_only(crattn, w, dev, reps=5):
     return e0.elapsed_time(e1) / reps
 
 
+def operand_sweep(crattn, w, dev, n=25):
+    """The step attention on N(0, 1) operands and on constant K and V (same
+    queries, same shapes, same kernel): per-launch ms of one burst of n
+    launches after n warm-up launches, in that order.  The instruction stream
+    is the same; on this chip the clock under matrix load depends on the
+    operand data, so the gap between the two is the data's cost in clock."""
+    import torch
+
+    from workloads import normal, prior_cache
+
+    q = normal((w.B, w.lq, w.H, w.D), 1000 * w.index).to(dev)
+    kc, vc = prior_cache(w)
+    kc, vc = kc.to(dev), vc.to(dev)
+    out = torch.empty_like(q)
+    res = {}
+    for name, (k_, v_) in (("normal", (kc, vc)),
+                           ("const_kv", (torch.full_like(kc, 0.5), torch.full_like(vc, 0.5)))):
+        def call(i, k_=k_, v_=v_):
+            crattn.chunk_causal_attn(q, k_, v_, w.kv_len, w.q_pos0, w.chunk_tokens, out, None,
+                                     None)
+        burst_ms(call, 1, n)
+        res[name] = round(burst_ms(call, 1, n)[0], 4)
+    return {"attn_ms_normal_operands": res["normal"], "attn_ms_const_kv": res["const_kv"]}
+
+
 def burst_ms(call, bursts, n):
     """Per-launch time (ms) of `bursts` bursts of n back-to-back calls, each
     burst between two events on the stream; sorted ascending."""
@@ -491,6 +516,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--operand-sweep", action="store_true",
+                    help="only the step attention on N(0,1) vs constant K/V (for a clock counter run)")
     ap.add_argument("--svg2-only", action="store_true",
                     help="only the semantic-permutation call (for profiling it)")
     args = ap.parse_args()
@@ -512,6 +539,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = STEP480
+    if args.operand_sweep:
+        print(json.dumps(operand_sweep(crattn, w, dev)))
+        return
     if args.svg2_only:
         fl = attn_flops(w.B, w.H, w.lq, w.kv_len, w.D)
         print(json.dumps({"svg2_480": svg2_extras(crattn, w, dev, float("nan"), fl)}))
@@ -575,6 +605,7 @@ def main():
 
     extras = {}
     if not args.no_extras:
+        extras["attn_operand_sweep"] = operand_sweep(crattn, w, dev)
         extras["sp480_attn_ms"] = round(time_attn_only(crattn, SP480, dev), 4)
         extras["sp480_attn_tflops"] = round(
             attn_flops(1, SP480.H, SP480.lq, SP480.kv_len, SP480.D)
