@@ -242,6 +242,54 @@ def test_step480_sampled_rows():
     assert bool((o32 <= vmax[:, :, None] + 1e-2).all() and (o32 >= vmin[:, :, None] - 1e-2).all())
 
 
+def test_step_replays_from_a_hip_graph():
+    # one denoising call of the SP-rank slice (RoPE/append into the cache,
+    # then the split-KV attention and its combine) captured once and
+    # replayed: every replay writes the eager call's output, lse and cache
+    # rows bit for bit, with eager calls between the replays and the
+    # workspace poisoned before each (the path records no memset nodes)
+    w = SP480
+    mt, mh, mw = w.table_extents()
+    tab = table(w.D, mt, mh, mw)
+    q, k, v = (t.to(dev()) for t in call_qkv(w, 0))
+    kc, vc = (t.to(dev()) for t in prior_cache(w))
+    q_out = torch.empty_like(q)
+    out = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.lq, dtype=torch.float32, device=dev())
+    wsb = crattn.chunk_causal_attn_workspace_bytes(w.B, w.H, w.lq, w.kv_len, w.q_pos0,
+                                                   w.chunk_tokens, w.D)
+    assert wsb > 0  # the split-KV combine is part of the captured call
+    ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev())
+
+    def call():
+        crattn.rope_apply_append(q, q_out, k, v, kc, vc, w.cache_pos, tab, mt, mh, mw, w.t0,
+                                 w.tok_off, w.grid_h, w.grid_w)
+        crattn.chunk_causal_attn(q_out, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens, out, lse, ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lse.clone(), kc.clone(), vc.clone())
+    rows = sample_rows(w.lq)
+    o_ref, _ = oracle_rows(q_out, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens, rows=rows)
+    assert_attn_close(f64(out[:, rows]), o_ref, "SP slice before capture (sampled rows)")
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        for t in (out, lse, q_out):
+            t.zero_()
+        ws.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("out", "lse", "k cache", "v cache"), (out, lse, kc, vc), ref):
+            assert torch.equal(got, want), f"replay {rep}: {name}"
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+
+
 def test_sp480_split_kv_and_unsplit():
     w = SP480
     (q, k, v, kc, vc), (q_out, kcd, vcd) = _step(w)
