@@ -278,3 +278,43 @@ def test_rollout_with_hsa_every_chunk():
     with pytest.raises(NotImplementedError):
         q = normal((B, L, H, D), 900).to(dev())
         ro.denoise(4, q, q, q, torch.empty_like(q), torch.empty_like(q))
+
+
+def test_hsa_call_replays_from_a_hip_graph():
+    # pooling, selection and the block-sparse attention captured once and
+    # replayed: every replay writes the eager call's pool, selection and
+    # output bit for bit, with eager calls between the replays
+    B, H, D, per_frame, F_c, chunks, Lq, kf, kb = 1, 2, 128, 100, 2, 5, 200, 3, 6
+    q, kc, vc, L, cap, q_pos0 = _inputs(B, H, D, per_frame, F_c, chunks, Lq, 0, 91)
+    pool = torch.empty(crattn.hsa_pool_bytes(B, H, cap, D, per_frame) // 4, dtype=torch.float32,
+                       device=dev())
+    sel = torch.empty(B, H, -(-Lq // 256), kb, dtype=torch.int32, device=dev())
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, Lq, dtype=torch.float32, device=dev())
+
+    def call():
+        crattn.hsa_pool_keys(kc, 0, cap, per_frame, pool)
+        crattn.hsa_select(q, pool, cap, per_frame, q_pos0, L, kf, kb, sel)
+        crattn.hsa_attn(q, kc, vc, q_pos0, L, per_frame, sel, out, lse)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (pool.clone(), sel.clone(), out.clone(), lse.clone())
+    assert (ref[1] >= 0).any()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        pool.fill_(float("nan"))
+        sel.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, want in zip(("pool", "sel", "out", "lse"), (pool, sel, out, lse), ref):
+            assert torch.equal(got, want), f"replay {rep}: {name}"
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[2])
