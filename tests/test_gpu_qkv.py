@@ -135,3 +135,42 @@ def test_large_token_counts_every_element(B, n, C):
     _check(f64(kc[:, :, pos:]).transpose(0, 2, 1, 3), ke, ak, k0, C, True, "K'")
     _check(f64(vc[:, :, pos:]).transpose(0, 2, 1, 3), ve, av, ve, C, False, "V")
     assert bool((kc[:, :, :pos] == 7.0).all()) and bool((vc[:, :, :pos] == -7.0).all())
+
+
+def test_projection_replays_from_a_hip_graph():
+    # the fused projection + rotation + append captured once and replayed:
+    # every replay writes the eager call's Q' and cache rows bit for bit,
+    # with eager calls between the replays
+    B, n, C, H, D, gh, gw, t0, cap, pos = 1, 600, 512, 2, 128, 10, 20, 4, 1400, 500
+    x, w = _inputs(B, n, C, H, D, 61)
+    xd, wd = x.to(dev()), w.to(dev())
+    mt, mh, mw = t0 + n // (gh * gw) + 2, gh, gw
+    tab = table(D, mt, mh, mw)
+    q = torch.empty(B, n, H, D, dtype=torch.bfloat16, device=dev())
+    kc = torch.zeros(B, H, cap, D, dtype=torch.bfloat16, device=dev())
+    vc = torch.zeros(B, H, cap, D, dtype=torch.bfloat16, device=dev())
+
+    def call():
+        crattn.qkv_rope_append(xd, wd, q, kc, vc, pos, tab, mt, mh, mw, t0, 0, gh, gw)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (q.clone(), kc.clone(), vc.clone())
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        for t in (q, kc, vc):
+            t.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q, ref[0]), f"replay {rep}: q"
+        assert torch.equal(kc[:, :, pos:pos + n], ref[1][:, :, pos:pos + n]), f"replay {rep}: k"
+        assert torch.equal(vc[:, :, pos:pos + n], ref[2][:, :, pos:pos + n]), f"replay {rep}: v"
+        # rows outside the appended range are not written
+        assert (kc[:, :, :pos] == 7.0).all() and (vc[:, :, pos + n:] == 7.0).all()
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(q, ref[0])
