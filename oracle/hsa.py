@@ -16,9 +16,15 @@ Readings of what the page leaves open (each is stated where it is used):
   order), the last block of a frame holding the remainder; a frame is
   ``per_frame`` tokens and frames are consecutive in the cache.
 * Query blocks are runs of ``bq`` consecutive query rows of the call.
-* History = the frames of the chunks before the query's chunk.  The query's
-  own chunk is always attended in full (attention inside a chunk is
-  bidirectional and dense); selection applies to history only.
+* History = the frames of the visible cache rows [0, kv_len) outside the
+  query's own chunk.  While a ring of chunk slots fills, the own chunk is
+  the last visible slot and the history is the chunks before it; once the
+  ring is full, every other slot is history, whatever its position in the
+  ring (attention does not depend on key order, "Sparse VideoGen2" §2.A).
+  The query's own chunk is always attended in full (attention inside a
+  chunk is bidirectional and dense); selection applies to history only.
+  Candidate frames are ranked in ascending frame order (ties go to the
+  lower frame).
 * Scores are plain dot products of the pooled vectors (a positive scale
   does not change a top-k).  Top-k keeps the k largest scores; equal scores
   are ordered by the lower index first.
@@ -80,14 +86,28 @@ def topk(scores: np.ndarray, k: int) -> np.ndarray:
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 
-def select(q: np.ndarray, k_frames: np.ndarray, k_blocks: np.ndarray, n_hist: int,
+def history_frames(kv_len: int, q_pos0: int, chunk_tokens: int, per_frame: int) -> np.ndarray:
+    """Frame ids of the history of a call whose row 0 sits at q_pos0: every
+    whole frame of the visible rows [0, kv_len) outside the own chunk
+    (chunk q_pos0 // chunk_tokens), ascending."""
+    if kv_len % per_frame or chunk_tokens % per_frame:
+        raise ValueError("kv_len and chunk_tokens must be whole frames")
+    own = q_pos0 // chunk_tokens
+    fc = chunk_tokens // per_frame
+    return np.array([f for f in range(kv_len // per_frame) if f // fc != own], dtype=np.int64)
+
+
+def select(q: np.ndarray, k_frames: np.ndarray, k_blocks: np.ndarray, hist,
            per_frame: int, kf: int, kb: int, bq: int = 256, bk: int = 64):
     """Two-level selection for every (b, h, query block).
 
     q: [B, Lq, H, D] rotated queries of the call; k_frames / k_blocks: pooled
-    keys (pool_keys); n_hist: number of history frames (frames 0..n_hist-1).
+    keys (pool_keys); hist: the history frame ids (history_frames), or an
+    int n meaning frames 0..n-1 (the own chunk after them).
     Returns sel [B, H, nqb, kb] int64: the chosen block ids ascending, padded
     with -1 when fewer than kb blocks exist in the chosen frames."""
+    hist = (np.arange(hist, dtype=np.int64) if np.isscalar(hist)
+            else np.asarray(hist, dtype=np.int64))
     nbf = blocks_per_frame(per_frame, bk)
     qp = pool_queries(q, bq)
     B, H, nqb, _ = qp.shape
@@ -95,10 +115,12 @@ def select(q: np.ndarray, k_frames: np.ndarray, k_blocks: np.ndarray, n_hist: in
     for b in range(B):
         for h in range(H):
             for i in range(nqb):
-                if n_hist == 0:
+                if len(hist) == 0:
                     continue
-                fs = k_frames[b, h, :n_hist] @ qp[b, h, i]
-                frames = topk(fs, kf)
+                # candidate c is history frame hist[c]: ranked in ascending
+                # frame order, so ties go to the lower frame
+                fs = k_frames[b, h, hist] @ qp[b, h, i]
+                frames = hist[topk(fs, kf)]
                 cand = np.concatenate([np.arange(f * nbf, (f + 1) * nbf) for f in frames])
                 bs = k_blocks[b, h, cand] @ qp[b, h, i]
                 chosen = cand[topk(bs, kb)]

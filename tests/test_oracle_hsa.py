@@ -74,12 +74,12 @@ def test_blocks_come_only_from_selected_frames():
     q = np.zeros((1, 16, 1, D))
     q[..., 0] = 1.0
     frames, blocks = hsa.pool_keys(k, per_frame, bk)
-    sel = hsa.select(q, frames, blocks, n_hist=2, per_frame=per_frame, kf=1, kb=1, bq=16, bk=bk)
+    sel = hsa.select(q, frames, blocks, hist=2, per_frame=per_frame, kf=1, kb=1, bq=16, bk=bk)
     assert list(sel[0, 0, 0]) == [2]    # block 0 of frame 1
     flat = hsa.topk(blocks[0, 0, :4] @ np.eye(D)[0], 1)
     assert list(flat) == [0]
     # with kf = 2 the strong block is reachable and wins
-    sel2 = hsa.select(q, frames, blocks, n_hist=2, per_frame=per_frame, kf=2, kb=1, bq=16, bk=bk)
+    sel2 = hsa.select(q, frames, blocks, hist=2, per_frame=per_frame, kf=2, kb=1, bq=16, bk=bk)
     assert list(sel2[0, 0, 0]) == [0]
 
 
@@ -89,11 +89,11 @@ def test_padding_when_the_frames_hold_fewer_blocks():
     k = rng.standard_normal((1, 2, 300, 8))
     q = rng.standard_normal((1, 40, 2, 8))
     frames, blocks = hsa.pool_keys(k, per_frame)
-    sel = hsa.select(q, frames, blocks, n_hist=2, per_frame=per_frame, kf=1, kb=5, bq=64)
+    sel = hsa.select(q, frames, blocks, hist=2, per_frame=per_frame, kf=1, kb=5, bq=64)
     assert sel.shape == (1, 2, 1, 5)
     assert (sel[..., :2] >= 0).all() and (sel[..., 2:] == -1).all()
     # no history: nothing selected
-    sel0 = hsa.select(q, frames, blocks, n_hist=0, per_frame=per_frame, kf=2, kb=3, bq=64)
+    sel0 = hsa.select(q, frames, blocks, hist=0, per_frame=per_frame, kf=2, kb=3, bq=64)
     assert (sel0 == -1).all()
 
 
@@ -165,3 +165,94 @@ def test_budget_is_constant_in_history_length():
         sel = hsa.select(q, frames, blocks, chunks - 1, per_frame, kf, kb, bq=64)
         keys = hsa.visible_keys(sel[0, 0, 0], cap - per_frame, cap, per_frame)
         assert per_frame < len(keys) <= per_frame + kb * 64
+
+
+# --------------------------------------------------------------------------- ring window
+
+
+def test_history_frames_of_a_filling_and_of_a_full_ring():
+    # 3 frames of 10 tokens per chunk; ring of 7 slots
+    per_frame, L = 10, 30
+    # filling: chunk 2 in slot 2 sees slots 0..2, history = frames 0..5
+    assert list(hsa.history_frames(3 * L, 2 * L, L, per_frame)) == list(range(6))
+    # chunk 0: no history
+    assert len(hsa.history_frames(L, 5, L, per_frame)) == 0
+    # full ring, own chunk in slot 3: every other slot's frames, ascending
+    want = list(range(0, 9)) + list(range(12, 21))
+    assert list(hsa.history_frames(7 * L, 3 * L + 7, L, per_frame)) == want
+    # the integer form is the filling case
+    rng = _rng(7)
+    k = rng.standard_normal((1, 1, 4 * L, 8))
+    q = rng.standard_normal((1, 20, 1, 8))
+    frames, blocks = hsa.pool_keys(k, per_frame, bk=4)
+    a = hsa.select(q, frames, blocks, 9, per_frame, kf=4, kb=5, bq=8, bk=4)
+    b = hsa.select(q, frames, blocks, hsa.history_frames(4 * L, 3 * L, L, per_frame), per_frame,
+                   kf=4, kb=5, bq=8, bk=4)
+    assert np.array_equal(a, b)
+
+
+def _rotate_slots(x, r, L, axis):
+    """Move the content of ring slot i to slot (i + r) mod W along `axis`."""
+    return np.roll(x, r * L, axis=axis)
+
+
+@pytest.mark.parametrize("own,r", [(2, 1), (0, 3), (4, 2), (1, 4)])
+def test_ring_rotation_moves_the_selection_with_the_slots(own, r):
+    # "Sparse VideoGen2" §2.A: attention does not depend on where a key sits.
+    # Rotating the ring's slots (and the own slot with them) must rotate the
+    # chosen blocks with their frames and leave every output unchanged.
+    rng = _rng(10 + own)
+    W, F_c, gh, gw, D, H = 5, 2, 4, 5, 16, 2
+    per_frame = gh * gw
+    L = F_c * per_frame
+    cap = W * L
+    nbf = hsa.blocks_per_frame(per_frame, 8)
+    q = rng.standard_normal((1, 24, H, D))
+    k = rng.standard_normal((1, H, cap, D))
+    v = rng.standard_normal((1, H, cap, D))
+
+    def run(k, v, own):
+        frames, blocks = hsa.pool_keys(k, per_frame, bk=8)
+        hist = hsa.history_frames(cap, own * L, L, per_frame)
+        assert len(hist) == (W - 1) * F_c
+        sel = hsa.select(q, frames, blocks, hist, per_frame, kf=3, kb=4, bq=8, bk=8)
+        o, lse = hsa.attn(q, k, v, sel, own * L, (own + 1) * L, per_frame, bq=8, bk=8)
+        return sel, o, lse
+
+    sel, o, lse = run(k, v, own)
+    sel_r, o_r, lse_r = run(_rotate_slots(k, r, L, 2), _rotate_slots(v, r, L, 2), (own + r) % W)
+
+    def move(blk):
+        f, j = divmod(int(blk), nbf)
+        s, fi = divmod(f, F_c)
+        return (((s + r) % W) * F_c + fi) * nbf + j
+
+    for idx in np.ndindex(sel.shape[:3]):
+        assert sorted(move(b) for b in sel[idx] if b >= 0) == [b for b in sel_r[idx] if b >= 0]
+    # the own slot is never a candidate
+    assert not any((b // nbf) // F_c == own for b in sel.ravel() if b >= 0)
+    np.testing.assert_allclose(o_r, o, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(lse_r, lse, atol=1e-12)
+
+
+@pytest.mark.parametrize("own", [0, 2, 4])
+def test_full_ring_selecting_everything_is_dense_attention(own):
+    # own chunk anywhere in a full ring, every history block chosen: the
+    # dense attention over every slot (the dense oracle sees every key when
+    # the query sits in the last chunk of a full cache)
+    rng = _rng(20 + own)
+    W, F_c, per_frame, D, H, Lq, q_off = 5, 2, 36, 16, 2, 50, 11
+    L = F_c * per_frame
+    cap = W * L
+    q = rng.standard_normal((1, Lq, H, D))
+    k = rng.standard_normal((1, H, cap, D))
+    v = rng.standard_normal((1, H, cap, D))
+    frames, blocks = hsa.pool_keys(k, per_frame)
+    hist = hsa.history_frames(cap, own * L + q_off, L, per_frame)
+    nbf = hsa.blocks_per_frame(per_frame)
+    sel = hsa.select(q, frames, blocks, hist, per_frame, kf=len(hist), kb=len(hist) * nbf, bq=16)
+    assert (sel >= 0).all()
+    o, lse = hsa.attn(q, k, v, sel, own * L, (own + 1) * L, per_frame, bq=16)
+    o_d, lse_d = oracle.attn(q, k, v, cap, (W - 1) * L + q_off, L)
+    np.testing.assert_allclose(o, o_d, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(lse, lse_d, atol=1e-12)
