@@ -106,11 +106,11 @@ def load():
     lib.hsa_pool_bytes.restype = ctypes.c_size_t
     lib.hsa_pool_keys.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _i32, _i32, _i32, _vp]
     lib.hsa_pool_keys.restype = _i32
-    lib.hsa_select.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _i32, _i32, _vp, _i32, _i32,
-                               _i32, _i64, _vp]
+    lib.hsa_select.argtypes = [_vp, _vp, _i64, _i64, _i32, _i64, _i64, _i32, _i32, _vp, _i32,
+                               _i32, _i32, _i64, _vp]
     lib.hsa_select.restype = _i32
-    lib.hsa_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp, _i32,
-                             _i32, _i32, _i64, ctypes.c_float, _vp]
+    lib.hsa_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _i32, _vp, _vp,
+                             _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
     lib.hsa_attn.restype = _i32
     lib.svg2_kmeans_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
     lib.svg2_kmeans_workspace_bytes.restype = ctypes.c_size_t
@@ -306,24 +306,28 @@ def hsa_pool_keys(k_cache: torch.Tensor, row0: int, nrows: int, per_frame: int,
     return pool
 
 
-def hsa_select(q: torch.Tensor, pool: torch.Tensor, cap: int, per_frame: int, q_pos0: int,
-               chunk_tokens: int, kf: int, kb: int, sel: torch.Tensor, stream=None) -> torch.Tensor:
-    """q: [B, Lq, H, D] bf16 (rotated); sel: int32 [B, H, ceil(Lq/256), kb]."""
+def hsa_select(q: torch.Tensor, pool: torch.Tensor, cap: int, kv_len: int, per_frame: int,
+               q_pos0: int, chunk_tokens: int, kf: int, kb: int, sel: torch.Tensor,
+               stream=None) -> torch.Tensor:
+    """q: [B, Lq, H, D] bf16 (rotated); sel: int32 [B, H, ceil(Lq/256), kb].
+    History = the frames of rows [0, kv_len) outside the own chunk
+    (q_pos0 // chunk_tokens)."""
     B, Lq, H, D = q.shape
     if q.dtype != torch.bfloat16 or pool.dtype != torch.float32:
         raise ValueError("q must be bf16 and pool float32")
     nqb = -(-Lq // HSA_QBLOCK)
     if sel.dtype != torch.int32 or tuple(sel.shape) != (B, H, nqb, kb):
         raise ValueError(f"sel must be int32 [{B}, {H}, {nqb}, {kb}]")
-    _raise(load().hsa_select(_ptr(q), _ptr(pool), cap, per_frame, q_pos0, chunk_tokens, kf, kb,
-                             _ptr(sel), B, H, D, Lq, _stream(stream)))
+    _raise(load().hsa_select(_ptr(q), _ptr(pool), cap, kv_len, per_frame, q_pos0, chunk_tokens,
+                             kf, kb, _ptr(sel), B, H, D, Lq, _stream(stream)))
     return sel
 
 
-def hsa_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, q_pos0: int,
-             chunk_tokens: int, per_frame: int, sel: torch.Tensor, out: torch.Tensor,
+def hsa_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len: int,
+             q_pos0: int, chunk_tokens: int, per_frame: int, sel: torch.Tensor, out: torch.Tensor,
              lse: torch.Tensor | None = None, scale: float = 0.0, stream=None) -> torch.Tensor:
-    """Attention over the own chunk plus the selected blocks of sel."""
+    """Attention over the own chunk plus the selected history blocks of sel
+    (history: the frames of rows [0, kv_len) outside the own chunk)."""
     B, Lq, H, D = q.shape
     cap = k_cache.shape[2]
     if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
@@ -338,9 +342,9 @@ def hsa_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, q_po
     nqb = -(-Lq // HSA_QBLOCK)
     if sel.dtype != torch.int32 or sel.dim() != 4 or tuple(sel.shape[:3]) != (B, H, nqb):
         raise ValueError(f"sel must be int32 [{B}, {H}, {nqb}, kb]")
-    _raise(load().hsa_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, q_pos0, chunk_tokens,
-                           per_frame, _ptr(sel), sel.shape[3], _ptr(out), _ptr(lse), B, H, D, Lq,
-                           float(scale), _stream(stream)))
+    _raise(load().hsa_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, kv_len, q_pos0,
+                           chunk_tokens, per_frame, _ptr(sel), sel.shape[3], _ptr(out), _ptr(lse),
+                           B, H, D, Lq, float(scale), _stream(stream)))
     return out
 
 

@@ -110,6 +110,9 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v, 
   if (grid_h > max_h || grid_w > max_w)
     return fail(CRATTN_EINVAL, "rope_apply_append: grid %dx%d exceeds the table (%dx%d)", grid_h,
                 grid_w, max_h, max_w);
+  // the kernels decode positions with a 32-bit frame size
+  if ((int64_t)grid_h * grid_w >= (int64_t(1) << 31))
+    return fail(CRATTN_EINVAL, "rope_apply_append: grid_h * grid_w must be below 2^31");
   const int64_t per_frame = (int64_t)grid_h * grid_w;
   if (tok_off > kMaxElems || n > kMaxElems)
     return fail(CRATTN_EINVAL, "rope_apply_append: token range too large");
@@ -182,6 +185,9 @@ int qkv_rope_append(const void *x, const void *w, void *q_out, void *k_cache, vo
   if (grid_h > max_h || grid_w > max_w)
     return fail(CRATTN_EINVAL, "qkv_rope_append: grid %dx%d exceeds the table (%dx%d)", grid_h,
                 grid_w, max_h, max_w);
+  // the kernels decode positions with a 32-bit frame size
+  if ((int64_t)grid_h * grid_w >= (int64_t(1) << 31))
+    return fail(CRATTN_EINVAL, "qkv_rope_append: grid_h * grid_w must be below 2^31");
   if (tok_off > kMaxElems || n > kMaxElems)
     return fail(CRATTN_EINVAL, "qkv_rope_append: token range too large");
   const int64_t last_t = t0 + (tok_off + n - 1) / ((int64_t)grid_h * grid_w);
@@ -299,15 +305,22 @@ int attn_call(const char *who, const QRope *rq, const Sparse *sp, const void *q,
                   who, sp->per_frame);
     if (q_pos0 % chunk_tokens + Lq > chunk_tokens)
       return fail(CRATTN_EINVAL, "%s: the query rows must lie in one chunk", who);
+    if (kv_len % sp->per_frame != 0)
+      return fail(CRATTN_EINVAL, "%s: kv_len must be whole frames of %d tokens", who,
+                  sp->per_frame);
     const int nbf = (sp->per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK;
-    const int64_t hist_blocks = q_pos0 / chunk_tokens * (chunk_tokens / sp->per_frame) * nbf;
-    if (hist_blocks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
+    const int64_t vis_blocks = kv_len / sp->per_frame * nbf;
+    const int64_t own_b0 = q_pos0 / chunk_tokens * (chunk_tokens / sp->per_frame) * nbf;
+    const int64_t own_b1 = own_b0 + chunk_tokens / sp->per_frame * nbf;
+    if (vis_blocks >= (int64_t(1) << 31) || cap >= (int64_t(1) << 31))
       return fail(CRATTN_EINVAL, "%s: history too long for 32-bit block ids", who);
     a.sel = sp->sel;
     a.sel_kb = sp->kb;
     a.sel_nbf = nbf;
     a.sel_per_frame = sp->per_frame;
-    a.sel_n_hist_blocks = (int)hist_blocks;
+    a.sel_vis_blocks = (int)vis_blocks;
+    a.sel_own_b0 = (int)own_b0;
+    a.sel_own_b1 = (int)own_b1;
   }
   if (rq != nullptr) {
     if (rq->table == nullptr || !aligned16(rq->table))
@@ -320,6 +333,8 @@ int attn_call(const char *who, const QRope *rq, const Sparse *sp, const void *q,
     if (rq->grid_h > rq->max_h || rq->grid_w > rq->max_w)
       return fail(CRATTN_EINVAL, "%s: grid %dx%d exceeds the table (%dx%d)", who, rq->grid_h,
                   rq->grid_w, rq->max_h, rq->max_w);
+    if ((int64_t)rq->grid_h * rq->grid_w >= (int64_t(1) << 31))
+      return fail(CRATTN_EINVAL, "%s: grid_h * grid_w must be below 2^31", who);
     const int64_t per_frame = (int64_t)rq->grid_h * rq->grid_w;
     if (chunk_tokens % per_frame != 0)
       return fail(CRATTN_EINVAL, "%s: chunk_tokens %lld is not a whole number of %dx%d frames",
@@ -441,9 +456,9 @@ int hsa_pool_keys(const void *k_cache, int64_t cap, int64_t row0, int64_t nrows,
                     "hsa_pool_keys launch");
 }
 
-int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int64_t q_pos0,
-               int64_t chunk_tokens, int kf, int kb, int32_t *sel, int B, int H, int D,
-               int64_t Lq, void *stream) {
+int hsa_select(const void *q, const void *pool, int64_t cap, int64_t kv_len, int per_frame,
+               int64_t q_pos0, int64_t chunk_tokens, int kf, int kb, int32_t *sel, int B, int H,
+               int D, int64_t Lq, void *stream) {
   if (q == nullptr || pool == nullptr || sel == nullptr)
     return fail(CRATTN_EINVAL, "hsa_select: q, pool and sel are required");
   if (!aligned16(q) || !aligned16(pool) || !aligned16(sel))
@@ -458,13 +473,15 @@ int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int6
   if (q_pos0 > kMaxElems || Lq > kMaxElems || q_pos0 % chunk_tokens + Lq > chunk_tokens)
     return fail(CRATTN_EINVAL, "hsa_select: the query rows must lie in one chunk");
   const int64_t q_chunk = q_pos0 / chunk_tokens;
-  if ((q_chunk + 1) * chunk_tokens > cap)
-    return fail(CRATTN_EINVAL, "hsa_select: the query chunk ends past cap");
+  if (kv_len > cap || kv_len % per_frame != 0 || (q_chunk + 1) * chunk_tokens > kv_len)
+    return fail(CRATTN_EINVAL, "hsa_select: kv_len %lld must be whole frames, at most cap and "
+                               "past the query chunk's end", (long long)kv_len);
   if (kf < 1 || kf > CRATTN_HSA_MAX_KF || kb < 1 || kb > CRATTN_HSA_MAX_KB)
     return fail(CRATTN_EINVAL, "hsa_select: kf in [1, %d] and kb in [1, %d] required",
                 CRATTN_HSA_MAX_KF, CRATTN_HSA_MAX_KB);
   const int64_t nbf = (per_frame + CRATTN_HSA_KBLOCK - 1) / CRATTN_HSA_KBLOCK;
-  const int64_t n_hist = q_chunk * (chunk_tokens / per_frame);
+  const int64_t fc = chunk_tokens / per_frame;
+  const int64_t n_hist = kv_len / per_frame - fc;
   if (n_hist > CRATTN_HSA_MAX_CAND || std::min<int64_t>(kf, n_hist) * nbf > CRATTN_HSA_MAX_CAND)
     return fail(CRATTN_EINVAL, "hsa_select: %lld history frames, %lld block candidates: at most "
                                "%d each", (long long)n_hist,
@@ -483,6 +500,8 @@ int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int6
   a.sel = sel;
   a.Lq = Lq;
   a.n_hist = (int)n_hist;
+  a.own_f0 = (int)(q_chunk * fc);
+  a.fc = (int)fc;
   a.kf = kf;
   a.kb = kb;
   a.n_qblocks = (int)n_qblocks;
@@ -492,13 +511,10 @@ int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int6
                     "hsa_select launch");
 }
 
-int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap, int64_t q_pos0,
-             int64_t chunk_tokens, int per_frame, const int32_t *sel, int kb, void *out,
-             float *lse, int B, int H, int D, int64_t Lq, float scale, void *stream) {
+int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap, int64_t kv_len,
+             int64_t q_pos0, int64_t chunk_tokens, int per_frame, const int32_t *sel, int kb,
+             void *out, float *lse, int B, int H, int D, int64_t Lq, float scale, void *stream) {
   const Sparse sp{sel, kb, per_frame};
-  if (chunk_tokens < 1 || q_pos0 < 0 || q_pos0 > kMaxElems)
-    return fail(CRATTN_EINVAL, "hsa_attn: chunk_tokens >= 1 and q_pos0 >= 0 required");
-  const int64_t kv_len = (q_pos0 / chunk_tokens + 1) * chunk_tokens;
   return attn_call("hsa_attn", nullptr, &sp, q, k_cache, v_cache, cap, kv_len, q_pos0,
                    chunk_tokens, out, lse, nullptr, 0, B, H, D, Lq, scale, stream);
 }

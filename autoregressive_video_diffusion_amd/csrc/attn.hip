@@ -70,9 +70,10 @@ struct AttnKArgs {
   const float2 *table;
   TabGeom tg;
   uint32_t per_frame, gw, t0, tok_off;
-  // block-sparse instance: per (b, h, query tile) kb selected key blocks
+  // block-sparse instance: per (b, h, query tile) kb selected key blocks;
+  // history blocks are ids in [0, vis_blocks) outside [own_b0, own_b1)
   const int32_t *sel;
-  int kb, nbf, blk_frame, n_hist_blocks;
+  int kb, nbf, blk_frame, vis_blocks, own_b0, own_b1;
   // gather instance: query tiles of query clusters and their key lists
   const int32_t *q_perm;    // [B][H][Lq]
   const int32_t *gslots;    // [B][H][n_tiles][4]
@@ -251,6 +252,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   [[maybe_unused]] const int32_t *g_list = nullptr;
   [[maybe_unused]] const int32_t *g_qperm = nullptr;
   if constexpr (GATHER) {
+    static_assert(BM == CRATTN_SVG2_QTILE, "a query tile of the plan is one workgroup's rows");
     // an empty (or out of range) slot runs with no rows and no keys
     // (loads inside the persistent loop are not known to be uniform: the
     // values are made wave-uniform explicitly)
@@ -301,36 +303,45 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
 
   // ---- block-sparse key list: the tiles of the own chunk, then the
   // selected history blocks as (first row, end row), compacted in list
-  // order.  Ids outside [0, n_hist_blocks) are dropped, so nothing outside
-  // the history is ever read and no tile is empty. ----
+  // order.  Ids that are not history blocks (negative, past the visible
+  // frames, or in the own chunk) are dropped, so nothing outside the own
+  // chunk and the history is ever read and no tile is empty.  The ids are
+  // taken a workgroup's width at a time. ----
   [[maybe_unused]] int own0 = 0, n_own = 0;
   [[maybe_unused]] int2 *sp_tiles = nullptr;
   if constexpr (SPARSE) {
+    static_assert(BM == CRATTN_HSA_QBLOCK, "one selection row per query tile");
+    static_assert(kBN == CRATTN_HSA_KBLOCK, "a selected block is one key tile");
     __shared__ int2 sp_buf[kMaxSelBlocks];
     __shared__ int sp_count[NW];
     sp_tiles = sp_buf;
     own0 = (int)(q_chunk * a.L);
     n_own = (limit - own0 + kBN - 1) / kBN;
     const int32_t *sl = a.sel + (((int64_t)b * a.H + h) * a.n_tiles + tile) * a.kb;
-    const int id = tid < a.kb ? sl[tid] : -1;
-    const bool v = id >= 0 && id < a.n_hist_blocks;
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(v);
-    const int before = __builtin_popcountll(bal & ((uint64_t(1) << lane) - 1));
-    if (lane == 0) sp_count[wave] = __builtin_popcountll(bal);
-    __syncthreads();
-    int off = 0, tot = 0;
+    int base = 0;
+    for (int i0 = 0; i0 < a.kb; i0 += NW * 64) {
+      const int i = i0 + tid;
+      const int id = i < a.kb ? sl[i] : -1;
+      const bool v = id >= 0 && id < a.vis_blocks && (id < a.own_b0 || id >= a.own_b1);
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(v);
+      const int before = __builtin_popcountll(bal & ((uint64_t(1) << lane) - 1));
+      if (lane == 0) sp_count[wave] = __builtin_popcountll(bal);
+      __syncthreads();
+      int off = base, tot = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      off += w < wave ? sp_count[w] : 0;
-      tot += sp_count[w];
+      for (int w = 0; w < NW; ++w) {
+        off += w < wave ? sp_count[w] : 0;
+        tot += sp_count[w];
+      }
+      if (v) {
+        const int f = id / a.nbf, j = id - f * a.nbf;
+        const int start = f * a.blk_frame + j * kBN;
+        sp_buf[off + before] = make_int2(start, start + min(kBN, a.blk_frame - j * kBN));
+      }
+      base += tot;
+      __syncthreads();
     }
-    if (v) {
-      const int f = id / a.nbf, j = id - f * a.nbf;
-      const int start = f * a.blk_frame + j * kBN;
-      sp_buf[off + before] = make_int2(start, start + min(kBN, a.blk_frame - j * kBN));
-    }
-    __syncthreads();
-    nkt = n_own + tot;
+    nkt = n_own + base;
   }
   // first key row and end of the visible range of tile kt (the visible
   // rows of a tile are [key0, min(key0 + kBN, lim)))
@@ -988,17 +999,6 @@ __global__ void __launch_bounds__(1024) gather_order_kernel(AttnKArgs a, int n_e
   }
 }
 
-int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n < 1)
-      n = 256;
-  }
-  return n;
-}
 
 template <int D, int NW, int QB, int MINB, bool ROPE, bool SPARSE, bool GATHER = false>
 hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
@@ -1096,7 +1096,9 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.kb = a.sel_kb;
   k.nbf = a.sel_nbf;
   k.blk_frame = a.sel_per_frame;
-  k.n_hist_blocks = a.sel_n_hist_blocks;
+  k.vis_blocks = a.sel_vis_blocks;
+  k.own_b0 = a.sel_own_b0;
+  k.own_b1 = a.sel_own_b1;
   k.q_perm = a.q_perm;
   k.gslots = a.gslots;
   k.lists = a.lists;
@@ -1121,7 +1123,7 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
       k.ws_o = reinterpret_cast<float *>(ws + 256 + order_bytes);
       k.ws_lse = reinterpret_cast<float *>(ws + 256 + order_bytes + o_bytes);
     }
-    const int64_t grid = std::min<int64_t>(p.grid, cu_count());
+    const int64_t grid = std::min<int64_t>(p.grid, device_cu_count());
     hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(1024), 0, s, k, (int)n_entries,
                        (unsigned long long)grid);
     e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, grid, s)

@@ -17,6 +17,17 @@ inline RopeSplit rope_split(int D) {
   return RopeSplit{D - 2 * hw, hw, hw};
 }
 
+// Compute units of the current device, asked at each call: the library
+// keeps no state between calls (a cache would also go stale on another
+// device).  256 if the runtime cannot tell.
+inline int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  return n;
+}
+
 struct RopeTableArgs {
   float2 *table;
   int dt, dh, dw;
@@ -74,9 +85,11 @@ struct AttnArgs {
   int max_t, max_h, max_w;
   int64_t t0, tok_off;
   int grid_h, grid_w;
-  // block-sparse attention (hsa_attn): selected block ids per query tile
+  // block-sparse attention (hsa_attn): selected block ids per query tile;
+  // ids in [0, sel_vis_blocks) outside the own chunk's [sel_own_b0,
+  // sel_own_b1) are history blocks, any other id is skipped
   const int32_t *sel;
-  int sel_kb, sel_nbf, sel_per_frame, sel_n_hist_blocks;
+  int sel_kb, sel_nbf, sel_per_frame, sel_vis_blocks, sel_own_b0, sel_own_b1;
   // cluster-sparse attention (svg2_attn): query tiles of query clusters,
   // each with an explicit list of key rows
   const int32_t *q_perm;    // [B][H][Lq] query row of each reordered position
@@ -105,7 +118,9 @@ struct HsaSelectArgs {
   const float *blocks;
   int32_t *sel;          // [B][H][n_qblocks][kb]
   int64_t Lq;
-  int nf, nbf, n_hist;   // history = frames [0, n_hist)
+  // history = the visible frames [0, n_vis) except the own chunk's
+  // [own_f0, own_f0 + fc): candidate c is frame c, or c + fc from own_f0 on
+  int nf, nbf, n_hist, own_f0, fc;
   int kf, kb, n_qblocks;
   int B, H;
 };

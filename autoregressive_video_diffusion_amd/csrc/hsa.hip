@@ -132,13 +132,16 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
       }
 #pragma unroll
       for (int m = TPI / 2; m >= 1; m >>= 1) s += __shfl_xor(s, m, TPI);
-      if (sub == 0) score[base] = s;
+      // a NaN score (NaN or infinite pooled inputs) ranks below every
+      // number, so the comparisons below stay a total order
+      if (sub == 0) score[base] = __builtin_isnan(s) ? -INFINITY : s;
     }
   };
   // rank of item i among n scores: how many are larger, or equal with a
-  // lower index (the order of a stable descending sort).  Scores are read
+  // lower index (the order of a stable descending sort; no score is NaN, so
+  // the ranks of the n items are 0 .. n-1, each once).  Scores are read
   // four at a time; the caller pads score[n .. n+3] with -inf, which never
-  // ranks above a finite score.
+  // ranks above an item (a -inf item has the lower index).
   auto rank = [&](int i, int n) {
     const float si = score[i];
     int k = 0;
@@ -179,13 +182,20 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
     for (int e = tid; e < a.kb; e += 256) out[e] = -1;
     return;
   }
-  // 2. frame scores and the kf best frames, kept in ascending order
+  // 2. frame scores and the kf best frames, kept in ascending order.
+  // Candidate c is history frame c below the own chunk and c + fc above it
+  // (in a ring, the own chunk's slot may sit anywhere).
+  auto frame_of = [&](int c) { return c < a.own_f0 ? c : c + a.fc; };
   const float *fm = a.frames + (int64_t)bh * a.nf * D;
-  scores(n_hist, [&](int f) { return fm + (int64_t)f * D; });
+  scores(n_hist, [&](int c) { return fm + (int64_t)frame_of(c) * D; });
   if (tid < 4) score[n_hist + tid] = -INFINITY;
   __syncthreads();
-  compact(n_hist, [&](int f) { return rank(f, n_hist) < a.kf; },
-          [&](int f, int pos) { frames_kept[pos] = f; });
+  // (pos < kf always holds with a total order; the test keeps a write
+  // inside the array whatever the scores)
+  compact(n_hist, [&](int c) { return rank(c, n_hist) < a.kf; },
+          [&](int c, int pos) {
+            if (pos < a.kf) frames_kept[pos] = frame_of(c);
+          });
   const int n_frames = min(a.kf, n_hist);
   const int n_cand = n_frames * a.nbf;
   // 3. block scores of every block of the kept frames; candidate c is block
@@ -198,7 +208,9 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
   __syncthreads();
   // 4. the kept blocks in ascending id order, then -1
   compact(n_cand, [&](int cnd) { return rank(cnd, n_cand) < a.kb; },
-          [&](int cnd, int pos) { out[pos] = frames_kept[cnd / a.nbf] * a.nbf + cnd % a.nbf; });
+          [&](int cnd, int pos) {
+            if (pos < a.kb) out[pos] = frames_kept[cnd / a.nbf] * a.nbf + cnd % a.nbf;
+          });
   for (int e = min(a.kb, n_cand) + tid; e < a.kb; e += 256) out[e] = -1;
 }
 

@@ -337,19 +337,6 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
   }
 }
 
-// compute units of the current device (cached per device)
-int cu_count() {
-  static int cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
 
 }  // namespace
 
@@ -382,7 +369,7 @@ hipError_t launch_qkv_rope(const QkvArgs &q, hipStream_t s) {
   // token-tile width: the fewest tile-rounds over the chip's CUs, weighted
   // by the tile's width; ties go to the wider tile
   const int n_ft = (a.F - a.f_begin + 255) / 256;
-  const int n_cu = cu_count();
+  const int n_cu = device_cu_count();
   int best_tn = 4;
   int64_t best_cost = -1;
   for (int tn = 4; tn >= 2; --tn) {

@@ -46,8 +46,9 @@ class ChunkRollout:
                  svg2: tuple[int, int, float] | None = None, svg2_iters: int = 2,
                  svg2_splits: int = 2):
         """hsa = (kf, kb) switches the denoising attention to HSA with kf
-        frames and kb blocks kept per query block (chunks 0 .. window-1: the
-        selection's history is the slots before the chunk's own).
+        frames and kb blocks kept per query block; the selection's history is
+        every visible slot but the chunk's own (the slots before it while the
+        ring fills, all other slots once it is full).
 
         svg2 = (Cq, Ck, p) switches it to the semantic-permutation attention:
         Cq query clusters, Ck key clusters per chunk slot, top-p threshold p;
@@ -162,9 +163,6 @@ class ChunkRollout:
     def denoise(self, c: int, q, k, v, q_out, out, lse=None, tok_off: int = 0):
         """One denoising step of chunk c: rotate Q/K, write the (noisy) K/V into
         the chunk's slot, attend.  q, k, v, q_out, out: [B, n, H, D]."""
-        if self.hsa is not None and c >= self.window:
-            raise NotImplementedError("HSA in a full ring window: the selection's history is "
-                                      "the slots before the chunk's own")
         if self.svg2 is not None and (tok_off != 0 or q.shape[1] != self.L):
             raise NotImplementedError("semantic-permutation attention covers whole chunks")
         self._rope(c, q, q_out, k, v, tok_off)
@@ -175,11 +173,14 @@ class ChunkRollout:
             chunk_causal_attn(q_out, self.k_cache, self.v_cache, kv_len, q0 + tok_off, self.L,
                               out, lse, self.workspace)
             return out
+        # HSA: the own chunk is the chunk's actual slot (the dense call's
+        # "last slot" convention would put it elsewhere in a full ring)
         n = q_out.shape[1]
         sel = self.sel[:, :, :-(-n // HSA_QBLOCK)].contiguous() if n != self.L else self.sel
-        hsa_select(q_out, self.pool, self.cap, self.per_frame, q0 + tok_off, self.L,
+        own = self.slot(c) * self.L + tok_off
+        hsa_select(q_out, self.pool, self.cap, kv_len, self.per_frame, own, self.L,
                    self.hsa[0], self.hsa[1], sel)
-        hsa_attn(q_out, self.k_cache, self.v_cache, q0 + tok_off, self.L, self.per_frame, sel,
+        hsa_attn(q_out, self.k_cache, self.v_cache, kv_len, own, self.L, self.per_frame, sel,
                  out, lse)
         return out
 

@@ -233,10 +233,10 @@ def time_hsa(crattn, w, b, kf=6, kb=32):
         crattn.hsa_pool_keys(b.kc, own0, L, per_frame, pool)
 
     def select_call(i):
-        crattn.hsa_select(b.q_out, pool, w.cap, per_frame, w.q_pos0, L, kf, kb, sel)
+        crattn.hsa_select(b.q_out, pool, w.cap, w.kv_len, per_frame, w.q_pos0, L, kf, kb, sel)
 
     def attn_call(i):
-        crattn.hsa_attn(b.q_out, b.kc, b.vc, w.q_pos0, L, per_frame, sel, b.out, b.lse)
+        crattn.hsa_attn(b.q_out, b.kc, b.vc, w.kv_len, w.q_pos0, L, per_frame, sel, b.out, b.lse)
 
     for f in (pool_call, select_call, attn_call):
         for i in range(3):

@@ -145,8 +145,9 @@ int rope_precompute(float *table, int head_dim, int max_t, int max_h, int max_w,
  * set, a misaligned pointer, n < 1, B < 1, H < 1, D not a multiple of 8 in
  * [8, CRATTN_MAX_HEAD_DIM], cap < 1, cache_pos < 0, cache_pos + n > cap,
  * t0 < 0, tok_off < 0, grid_h < 1, grid_w < 1, a position outside the table
- * (t0 + last frame >= max_t, grid_h > max_h, grid_w > max_w), an unknown
- * dtype, or sizes whose element counts overflow 2^40; EHIP.
+ * (t0 + last frame >= max_t, grid_h > max_h, grid_w > max_w), a frame of
+ * grid_h * grid_w >= 2^31 tokens, an unknown dtype, or sizes whose element
+ * counts overflow 2^40; EHIP.
  */
 int rope_apply_append(const void *q, void *q_out, const void *k, const void *v,
                       void *k_cache, void *v_cache, int64_t cap, int64_t cache_pos,
@@ -175,7 +176,7 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v,
  * fp32 with the table's fp32 cos/sin, round-to-nearest-even bf16 stores.
  *
  * Errors: EINVAL for NULL x/w/caches/table, a misaligned pointer, B, H, n or
- * C < 1, the cache-range and position errors of rope_apply_append, B*n or
+ * C < 1, the cache-range, position and grid errors of rope_apply_append, B*n or
  * 3*H*D >= 2^31, or a cache over 2^40 elements; ENOTSUP for D other than 64
  * or 128, or C not a multiple of 64 or above 65536; EHIP.
  */
@@ -259,9 +260,10 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache,
  * sequence bit for bit; the attention arithmetic is chunk_causal_attn's.
  *
  * Errors: those of chunk_causal_attn, and EINVAL for a NULL or misaligned
- * table, table extents outside [1, 2^20], t0 < 0, a grid below 1 or beyond
- * the table, chunk_tokens not a whole number of frames, query rows that
- * leave their chunk, or a time index t0 + last frame >= max_t.
+ * table, table extents outside [1, 2^20], t0 < 0, a grid below 1, beyond
+ * the table or of grid_h * grid_w >= 2^31 tokens, chunk_tokens not a whole
+ * number of frames, query rows that leave their chunk, or a time index
+ * t0 + last frame >= max_t.
  */
 int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max_h, int max_w,
                            int64_t t0, int grid_h, int grid_w, const void *k_cache,
@@ -282,8 +284,14 @@ int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max
  * order (row r is in frame r / per_frame).  Key block j of frame f covers
  * rows f*per_frame + 64 j .. min(+64, (f+1)*per_frame); its global id is
  * f * nbf + j with nbf = ceil(per_frame / 64).  Query block i of a call is
- * rows 256 i .. min(256 i + 256, Lq).  History = the frames before the
- * query's chunk; the own chunk is always attended in full.
+ * rows 256 i .. min(256 i + 256, Lq).  The own chunk is chunk
+ * c = q_pos0 / chunk_tokens (rows c*chunk_tokens .. (c+1)*chunk_tokens) and
+ * is always attended in full.  History = every frame of the visible rows
+ * [0, kv_len) outside the own chunk.  While a ring of chunk slots fills,
+ * kv_len = (c+1)*chunk_tokens and the history is the chunks before the own
+ * one; in a full ring, kv_len = cap and the own chunk is the current slot,
+ * wherever it sits, so every other slot is history (attention does not
+ * depend on key order ["Sparse VideoGen2" §2.A]).
  *
  * Pooled keys ("pool"): device float [B][H][nf][D] frame means followed by
  * [B][H][nf * nbf][D] block means, nf = cap / per_frame;
@@ -309,24 +317,28 @@ int hsa_pool_keys(const void *k_cache, int64_t cap, int64_t row0, int64_t nrows,
  *   q        device bf16 [B][Lq][H][D]: the rotated queries of the call (all
  *            rows in one chunk: (q_pos0 mod chunk_tokens) + Lq <= chunk_tokens).
  *   pool     pooled keys of the history (hsa_pool_keys).
+ *   kv_len   visible rows: whole frames, past the own chunk's end, <= cap.
  *   kf, kb   frames and blocks kept (1 <= kf <= 64, 1 <= kb <= 512; at most
- *            4096 block candidates: min(kf, history frames) * nbf).
+ *            4096 history frames and 4096 block candidates:
+ *            min(kf, history frames) * nbf).
  *   sel      device int32 [B][H][ceil(Lq/256)][kb]: the kept block ids in
  *            ascending order, then -1 for the places left when the kept
  *            frames hold fewer than kb blocks (all -1 with no history).
  *
  * Arithmetic: the query block's mean and the dot products with the pooled
  * keys in fp32; the k largest scores are kept, equal scores by the lower
- * index first.
+ * frame / block id first.  A NaN score (from non-finite queries or keys)
+ * ranks below every number; sel then still holds at most kb valid ids.
  *
  * Errors: EINVAL for NULL or misaligned pointers, B, H, Lq < 1, q_pos0 < 0,
  * chunk_tokens or per_frame < 1, chunk_tokens or cap not whole frames, query
- * rows that leave their chunk, a query chunk that ends past cap, kf or kb
- * outside the limits, too many candidates; ENOTSUP for D not 64 or 128; EHIP.
+ * rows that leave their chunk, kv_len not whole frames, above cap or before
+ * the query chunk's end, kf or kb outside the limits, too many candidates;
+ * ENOTSUP for D not 64 or 128; EHIP.
  */
-int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int64_t q_pos0,
-               int64_t chunk_tokens, int kf, int kb, int32_t *sel, int B, int H, int D,
-               int64_t Lq, void *stream);
+int hsa_select(const void *q, const void *pool, int64_t cap, int64_t kv_len, int per_frame,
+               int64_t q_pos0, int64_t chunk_tokens, int kf, int kb, int32_t *sel, int B, int H,
+               int D, int64_t Lq, void *stream);
 
 /*
  * Attention over the own chunk plus the selected blocks.
@@ -334,19 +346,22 @@ int hsa_select(const void *q, const void *pool, int64_t cap, int per_frame, int6
  *   q, k_cache, v_cache, out, lse, scale  as for chunk_causal_attn (q
  *            rotated; all rows in one chunk).  The own chunk is rows
  *            [c*chunk_tokens, (c+1)*chunk_tokens) with c = q_pos0 / chunk_tokens.
+ *   kv_len   visible rows, as for hsa_select.
  *   sel, kb  the selection (hsa_select's layout).  The ids of a row are used
- *            up to the end of the row; ids outside the history (negative or
- *            >= the history's block count) are skipped.
+ *            up to the end of the row; ids that are not history blocks
+ *            (negative, in frames at or past kv_len, or in the own chunk) are
+ *            skipped.  Each id should appear once: a repeated id attends its
+ *            block's keys once per appearance (hsa_select never repeats one).
  *
  * Arithmetic: chunk_causal_attn's, over the visible rows in list order (own
  * chunk first).  Selecting every history block gives the dense result up to
  * summation order.
  *
- * Errors: those of chunk_causal_attn (with kv_len = the own chunk's end),
- * and EINVAL for a NULL or misaligned sel, kb outside [1, 512], per_frame < 1,
- * chunk_tokens or cap not whole frames, query rows that leave their chunk.
+ * Errors: those of chunk_causal_attn, and EINVAL for a NULL or misaligned
+ * sel, kb outside [1, 512], per_frame < 1, chunk_tokens, cap or kv_len not
+ * whole frames, query rows that leave their chunk.
  */
-int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap,
+int hsa_attn(const void *q, const void *k_cache, const void *v_cache, int64_t cap, int64_t kv_len,
              int64_t q_pos0, int64_t chunk_tokens, int per_frame, const int32_t *sel, int kb,
              void *out, float *lse, int B, int H, int D, int64_t Lq, float scale, void *stream);
 

@@ -75,6 +75,8 @@ def _append(**kw):
     (dict(k=MIS), 1), (dict(D=60), 1), (dict(D=264), 1), (dict(n=0), 1), (dict(B=0), 1),
     (dict(pos=40, n=64, cap=100), 1), (dict(pos=-1), 1), (dict(t0=4), 1), (dict(gh=9), 1),
     (dict(gw=9), 1), (dict(off=1), 1), (dict(dt=7), 1), (dict(t0=-1), 1),
+    # a frame of 2^32 tokens would wrap the kernels' 32-bit frame size
+    (dict(gh=1 << 16, gw=1 << 16, mh=1 << 16, mw=1 << 16), 1),
 ])
 def test_rope_apply_append_rejects(kw, code):
     assert _append(**kw) == code
@@ -96,6 +98,7 @@ def _qkv(**kw):
     (dict(w=MIS), 1), (dict(q_out=MIS), 1), (dict(D=96), 2), (dict(C=100), 2), (dict(C=96), 2), (dict(C=0), 1),
     (dict(C=65568), 2), (dict(n=0), 1), (dict(B=0), 1), (dict(pos=40, n=64, cap=100), 1),
     (dict(t0=4), 1), (dict(gh=9), 1), (dict(off=1), 1), (dict(t0=-1), 1),
+    (dict(gh=1 << 16, gw=1 << 16, mh=1 << 16, mw=1 << 16), 1),
 ])
 def test_qkv_rope_append_rejects(kw, code):
     assert _qkv(**kw) == code
@@ -143,7 +146,7 @@ def _attn_rope(**kw):
     (dict(q=None), 1), (dict(kv=255), 1), (dict(D=96), 2), (dict(cap=1 << 25), 1),
     # table and geometry
     (dict(table=None), 1), (dict(table=MIS), 1), (dict(mt=0), 1), (dict(t0=-1), 1),
-    (dict(t0=4), 1), (dict(gh=9), 1), (dict(gw=0), 1),
+    (dict(t0=4), 1), (dict(gh=9), 1), (dict(gw=0), 1), (dict(gh=1 << 16, gw=1 << 16, mh=1 << 16, mw=1 << 16), 1),
     # chunk_tokens must be whole frames; rows must stay in their chunk
     (dict(L=96, cap=384, kv=384, pos0=288, Lq=96, mt=8), 1),
     (dict(pos0=128, Lq=100), 1),
@@ -188,19 +191,21 @@ def test_hsa_pool_keys_rejects(kw, code):
 
 
 def _select(**kw):
-    a = dict(q=FAKE, pool=FAKE, cap=256, pf=64, pos0=192, L=64, kf=2, kb=4, sel=FAKE, B=1, H=2,
-             D=64, Lq=64)
+    a = dict(q=FAKE, pool=FAKE, cap=256, kv=256, pf=64, pos0=192, L=64, kf=2, kb=4, sel=FAKE, B=1,
+             H=2, D=64, Lq=64)
     a.update(kw)
-    return _lib().hsa_select(a["q"], a["pool"], a["cap"], a["pf"], a["pos0"], a["L"], a["kf"],
-                             a["kb"], a["sel"], a["B"], a["H"], a["D"], a["Lq"], None)
+    return _lib().hsa_select(a["q"], a["pool"], a["cap"], a["kv"], a["pf"], a["pos0"], a["L"],
+                             a["kf"], a["kb"], a["sel"], a["B"], a["H"], a["D"], a["Lq"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(sel=MIS), 1), (dict(D=32), 2), (dict(kf=0), 1), (dict(kf=65), 1),
     (dict(kb=0), 1), (dict(kb=513), 1), (dict(pos0=200), 1), (dict(L=96), 1),
     (dict(pos0=256), 1), (dict(Lq=0), 1),
+    # kv_len above cap, not whole frames, or ending inside / before the own chunk
+    (dict(kv=320), 1), (dict(kv=250), 1), (dict(kv=192), 1), (dict(pos0=0, kv=32), 1),
     # 4097 history frames exceed the candidate limit
-    (dict(cap=64 * 4098, pos0=64 * 4097, kf=1), 1),
+    (dict(cap=64 * 4098, kv=64 * 4098, pos0=64 * 4097, kf=1), 1),
 ])
 def test_hsa_select_rejects(kw, code):
     assert _select(**kw) == code
@@ -208,17 +213,18 @@ def test_hsa_select_rejects(kw, code):
 
 
 def _hsa_attn(**kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, pos0=192, L=64, pf=64, sel=FAKE, kb=4, out=FAKE,
-             lse=None, B=1, H=2, D=64, Lq=64, scale=0.0)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, kv=256, pos0=192, L=64, pf=64, sel=FAKE, kb=4,
+             out=FAKE, lse=None, B=1, H=2, D=64, Lq=64, scale=0.0)
     a.update(kw)
-    return _lib().hsa_attn(a["q"], a["k"], a["v"], a["cap"], a["pos0"], a["L"], a["pf"], a["sel"],
-                           a["kb"], a["out"], a["lse"], a["B"], a["H"], a["D"], a["Lq"], a["scale"],
-                           None)
+    return _lib().hsa_attn(a["q"], a["k"], a["v"], a["cap"], a["kv"], a["pos0"], a["L"], a["pf"],
+                           a["sel"], a["kb"], a["out"], a["lse"], a["B"], a["H"], a["D"], a["Lq"],
+                           a["scale"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(sel=None), 1), (dict(sel=MIS), 1), (dict(kb=0), 1), (dict(kb=513), 1), (dict(pf=0), 1),
-    (dict(pf=48), 1), (dict(pos0=200), 1), (dict(D=96), 2), (dict(cap=200), 1), (dict(q=None), 1),
+    (dict(pf=48), 1), (dict(pos0=200), 1), (dict(D=96), 2), (dict(cap=200, kv=200), 1),
+    (dict(q=None), 1), (dict(kv=320), 1), (dict(kv=192), 1), (dict(kv=224, pf=32), 1),
 ])
 def test_hsa_attn_rejects(kw, code):
     assert _hsa_attn(**kw) == code

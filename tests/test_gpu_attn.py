@@ -216,15 +216,19 @@ def _step(w, call=0):
     return (q, k, v, kc, vc), (q_out, kcd, vcd)
 
 
-def test_step480_sampled_rows():
+def test_step480_every_row():
+    # the headline call (4680 queries x 32760 keys, 12 heads) in the launch
+    # configuration the benchmark times: every row of every head against the
+    # oracle fed the GPU's own rotated queries and cache (~10 s of host time)
     w = STEP480
     (q, k, v, kc, vc), (q_out, kcd, vcd) = _step(w)
     out, lse = run_attn(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens)
+    o_ref, lse_ref = oracle_rows(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens)
+    assert_attn_close(f64(out), o_ref, "480P unit (every row)")
+    np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
+    del o_ref, lse_ref
     rows = sample_rows(w.lq)
-    o_ref, lse_ref = oracle_rows(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens, rows=rows)
-    assert_attn_close(f64(out[:, rows]), o_ref, "480P unit (sampled rows)")
-    np.testing.assert_allclose(f64(lse[:, :, rows]), lse_ref, atol=2e-3)
-    # end to end for the same rows: the oracle's own rotation of this chunk
+    # end to end for sampled rows: the oracle's own rotation of this chunk
     q_full = oracle.round_bf16(oracle.rope(f64(q), w.t0, 0, w.grid_h, w.grid_w))
     k_e = f64(kc)
     k_e[:, :, w.cache_pos:] = oracle.round_bf16(
@@ -291,18 +295,19 @@ def test_step_replays_from_a_hip_graph():
 
 
 def test_sp480_split_kv_and_unsplit():
+    # one sequence-parallel rank's slice: every row of every head, split-KV
+    # (as timed) and unsplit
     w = SP480
     (q, k, v, kc, vc), (q_out, kcd, vcd) = _step(w)
     assert crattn.chunk_causal_attn_workspace_bytes(w.B, w.H, w.lq, w.kv_len, w.q_pos0,
                                                     w.chunk_tokens, w.D) > 0
     out, lse = run_attn(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens)
     out1, lse1 = run_attn(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens, use_ws=False)
-    rows = sample_rows(w.lq, n_random=60)
-    o_ref, lse_ref = oracle_rows(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens, rows=rows)
-    assert_attn_close(f64(out[:, rows]), o_ref, "sp rank split-KV")
-    assert_attn_close(f64(out1[:, rows]), o_ref, "sp rank unsplit")
-    np.testing.assert_allclose(f64(lse[:, :, rows]), lse_ref, atol=2e-3)
-    np.testing.assert_allclose(f64(lse1[:, :, rows]), lse_ref, atol=2e-3)
+    o_ref, lse_ref = oracle_rows(q_out, kcd, vcd, w.kv_len, w.q_pos0, w.chunk_tokens)
+    assert_attn_close(f64(out), o_ref, "sp rank split-KV (every row)")
+    assert_attn_close(f64(out1), o_ref, "sp rank unsplit (every row)")
+    np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
+    np.testing.assert_allclose(f64(lse1), lse_ref, atol=2e-3)
 
 
 def test_sp_slice_equals_rows_of_whole_chunk():
@@ -380,14 +385,13 @@ def test_rollout480_seven_chunks():
         for j in range(4):
             q, k, v = call_qkv(w, c * 5 + j)
             ro.denoise(c, q.to(dev()), k.to(dev()), v.to(dev()), q_out, out)
-            if j == 3 and c in (0, 3, 6):
+            if j == 3:
+                # every chunk's last denoising call: all 12 heads, sampled rows
                 kv_len, q0 = ro.visible(c)
                 assert kv_len == (c + 1) * n and q0 == c * n
                 rows = sample_rows(n, n_random=8, seed=c)
-                o_ref, _ = oracle_rows(q_out, ro.k_cache, ro.v_cache, kv_len, q0, n, rows=rows,
-                                       heads=[0, 5, 11])
-                assert_attn_close(f64(out[:, rows][:, :, [0, 5, 11]]), o_ref,
-                                  f"rollout chunk {c} step {j}")
+                o_ref, _ = oracle_rows(q_out, ro.k_cache, ro.v_cache, kv_len, q0, n, rows=rows)
+                assert_attn_close(f64(out[:, rows]), o_ref, f"rollout chunk {c} step {j}")
         _, k, v = call_qkv(w, c * 5 + 4)
         ro.update(c, k.to(dev()), v.to(dev()))
         clean.append((k, v))
