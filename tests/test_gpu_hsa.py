@@ -400,7 +400,7 @@ def test_select_with_nan_and_inf_scores_stays_in_bounds():
     # a NaN query block and an infinite pooled frame: the selection still
     # writes at most kb valid, ascending history ids per row and nothing past
     # its rows (the output buffer has a guard tail)
-    B, H, D, per_frame, F_c, chunks, Lq, kf, kb = 1, 2, 128, 100, 2, 5, 600, 3, 5
+    B, H, D, per_frame, F_c, chunks, Lq, kf, kb = 1, 2, 128, 400, 2, 5, 600, 3, 5
     q, kc, vc, L, cap, q_pos0 = _inputs(B, H, D, per_frame, F_c, chunks, Lq, 0, 401, own=1)
     q[:, 256:300] = float("nan")               # query block 1 has NaN rows
     pool, _, _ = _pool(kc, per_frame)
