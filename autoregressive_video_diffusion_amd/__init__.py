@@ -40,8 +40,8 @@ import torch
 __all__ = [
     "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
     "rope_apply_append", "qkv_rope_append", "chunk_causal_attn_workspace_bytes",
-    "chunk_causal_attn", "chunk_causal_attn_rope", "hsa_pool_bytes", "hsa_pool_keys",
-    "hsa_select", "hsa_attn", "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots",
+    "chunk_causal_attn", "chunk_causal_attn_noalloc", "chunk_causal_attn_rope", "hsa_pool_bytes",
+    "hsa_pool_keys", "hsa_select", "hsa_attn", "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots",
     "svg2_plan", "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error", "EXPORTS",
     "HSA_QBLOCK", "HSA_KBLOCK", "SVG2_QTILE",
 ]
@@ -54,7 +54,8 @@ CRATTN_F32, CRATTN_BF16 = 0, 1
 
 # Every symbol include/crattn.h declares.
 EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append", "qkv_rope_append",
-           "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "chunk_causal_attn_rope",
+           "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "chunk_causal_attn_noalloc",
+           "chunk_causal_attn_rope",
            "hsa_pool_bytes", "hsa_pool_keys", "hsa_select", "hsa_attn",
            "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots", "svg2_plan",
            "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error")
@@ -98,6 +99,9 @@ def load():
     lib.chunk_causal_attn.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
                                       ctypes.c_size_t, _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
     lib.chunk_causal_attn.restype = _i32
+    lib.chunk_causal_attn_noalloc.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp,
+                                              _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
+    lib.chunk_causal_attn_noalloc.restype = _i32
     lib.chunk_causal_attn_rope.argtypes = [_vp, _vp, _i32, _i32, _i32, _i64, _i32, _i32, _vp, _vp,
                                            _i64, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_size_t,
                                            _i32, _i32, _i32, _i64, ctypes.c_float, _vp]
@@ -254,6 +258,29 @@ def chunk_causal_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _raise(load().chunk_causal_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, kv_len, q_pos0,
                                     chunk_tokens, _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                     B, H, D, Lq, float(scale), _stream(stream)))
+    return out
+
+
+def chunk_causal_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              kv_len: int, q_pos0: int, chunk_tokens: int, out: torch.Tensor,
+                              lse: torch.Tensor | None = None, scale: float = 0.0,
+                              stream=None) -> torch.Tensor:
+    """chunk_causal_attn with no workspace argument: split partials go to the
+    library's fixed per-device scratch (calls on one device must not overlap)."""
+    B, Lq, H, D = q.shape
+    cap = k_cache.shape[2]
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise ValueError("q and out must be bfloat16")
+    if tuple(out.shape) != (B, Lq, H, D):
+        raise ValueError("out must have q's shape")
+    for t in (k_cache, v_cache):
+        if tuple(t.shape) != (B, H, cap, D) or t.dtype != torch.bfloat16:
+            raise ValueError("caches must be bf16 [B, H, cap, D]")
+    if lse is not None and (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [B, H, Lq]")
+    _raise(load().chunk_causal_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), cap, kv_len,
+                                            q_pos0, chunk_tokens, _ptr(out), _ptr(lse), B, H, D,
+                                            Lq, float(scale), _stream(stream)))
     return out
 
 

@@ -37,6 +37,7 @@ int hip_status(hipError_t e, const char *what) {
 }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+static_assert(crattn::kAttnScratchBytes == CRATTN_NOALLOC_SCRATCH_BYTES, "scratch size");
 constexpr int kMaxExtent = 1 << 20;
 
 }  // namespace
@@ -394,6 +395,29 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache, i
                       float scale, void *stream) {
   return attn_call("chunk_causal_attn", nullptr, nullptr, q, k_cache, v_cache, cap, kv_len, q_pos0,
                    chunk_tokens, out, lse, workspace, ws_bytes, B, H, D, Lq, scale, stream);
+}
+
+int chunk_causal_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              int64_t cap, int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens,
+                              void *out, float *lse, int B, int H, int D, int64_t Lq, float scale,
+                              void *stream) {
+  const char *who = "chunk_causal_attn_noalloc";
+  // the workspace this shape needs (0 when the key range is not split); the
+  // rest of the validation is chunk_causal_attn's, run below before any launch
+  const int st = attn_shape_check(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, cap, who);
+  if (st != CRATTN_OK) return st;
+  const size_t need = crattn::attn_plan(B, H, Lq, kv_len, q_pos0, chunk_tokens, D, true).ws_bytes;
+  if (need > crattn::kAttnScratchBytes)
+    return fail(CRATTN_EINVAL, "%s: the call needs %zu bytes of scratch, the library holds %zu",
+                who, need, crattn::kAttnScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) {
+    hipError_t e = hipSuccess;
+    ws = crattn::attn_scratch(&e);
+    if (ws == nullptr) return hip_status(e, "chunk_causal_attn_noalloc scratch");
+  }
+  return attn_call(who, nullptr, nullptr, q, k_cache, v_cache, cap, kv_len, q_pos0, chunk_tokens,
+                   out, lse, ws, need, B, H, D, Lq, scale, stream);
 }
 
 int chunk_causal_attn_rope(const void *q, const float *table, int max_t, int max_h, int max_w,

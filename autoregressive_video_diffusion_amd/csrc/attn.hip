@@ -39,6 +39,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace crattn {
@@ -1008,6 +1009,35 @@ hipError_t launch_fwd(const AttnKArgs &k, int64_t grid, hipStream_t s) {
 }
 
 }  // namespace
+
+// Fixed scratch for the split-KV partials of chunk_causal_attn_noalloc.  In
+// host code `scratch` is only a stand-in for the device array: its device
+// address comes from hipGetSymbolAddress, once per device (each device holds
+// its own copy), and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[kAttnScratchBytes];
+
+void *attn_scratch(hipError_t *err) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void *> ptr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  void *p = ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptr[dev].store(p, std::memory_order_release);  // the same address in every thread
+  }
+  *err = hipSuccess;
+  return p;
+}
 
 AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
                    int64_t chunk_tokens, int D, bool allow_split) {

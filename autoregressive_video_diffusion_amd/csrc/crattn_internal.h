@@ -184,6 +184,13 @@ AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
 hipError_t launch_rope_table(const RopeTableArgs &a, hipStream_t s);
 hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
+
+// The library's fixed device scratch for callers that cannot allocate
+// (chunk_causal_attn_noalloc): kAttnScratchBytes on every device the library
+// runs on, held until the process ends.  attn_scratch returns its address on
+// the current device (looked up once per device), or null with *err set.
+constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+void *attn_scratch(hipError_t *err);
 hipError_t launch_qkv_rope(const QkvArgs &a, hipStream_t s);
 hipError_t launch_hsa_pool(const HsaPoolArgs &a, int D, hipStream_t s);
 hipError_t launch_hsa_select(const HsaSelectArgs &a, int D, hipStream_t s);

@@ -238,6 +238,30 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache,
                       int B, int H, int D, int64_t Lq, float scale, void *stream);
 
 /*
+ * chunk_causal_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation with the same arguments minus the
+ * workspace.  When the call's shape splits the key range, the split partials
+ * go to a scratch array the library holds on each device it runs on:
+ * 32 MiB (CRATTN_NOALLOC_SCRATCH_BYTES), kept until the process ends, its
+ * address looked up once per device.  The call allocates nothing.
+ *
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents (nothing in it has to start at zero): calls that
+ * overlap on one device (two streams, or two threads) race and must be
+ * ordered by the caller.
+ *
+ * Errors: those of chunk_causal_attn, and EINVAL when the shape needs more
+ * than CRATTN_NOALLOC_SCRATCH_BYTES of partials
+ * (chunk_causal_attn_workspace_bytes of the same shape tells how much).
+ */
+#define CRATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int chunk_causal_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                              int64_t cap, int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens,
+                              void *out, float *lse, int B, int H, int D, int64_t Lq, float scale,
+                              void *stream);
+
+/*
  * Chunk-causal flash attention with the queries' Causal-RoPE applied on
  * load [CRSP §2.B-§2.C; WF]: the same computation as rope_apply_append
  * followed by chunk_causal_attn on the rotated queries, without writing Q'

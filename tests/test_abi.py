@@ -129,6 +129,34 @@ def test_chunk_causal_attn_rejects(kw, code):
     assert crattn.crattn_last_error() != ""
 
 
+def _attn_noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cap=256, kv=256, pos0=192, L=64, out=FAKE, lse=None, B=1,
+             H=2, D=64, Lq=64, scale=0.0)
+    a.update(kw)
+    return _lib().chunk_causal_attn_noalloc(a["q"], a["k"], a["v"], a["cap"], a["kv"],
+                                            a["pos0"], a["L"], a["out"], a["lse"], a["B"],
+                                            a["H"], a["D"], a["Lq"], a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(v=MIS), 1), (dict(kv=255), 1), (dict(D=96), 2), (dict(Lq=0), 1),
+    (dict(scale=-1.0), 1), (dict(cap=1 << 25), 1),
+    # 4 heads x 4096 queries against 65536 keys split 4 ways: 33.8 MB of
+    # partials, above the library's 32 MiB scratch
+    (dict(cap=65536, kv=65536, pos0=61440, L=4096, Lq=4096, H=4, D=128), 1),
+])
+def test_chunk_causal_attn_noalloc_rejects(kw, code):
+    assert _attn_noalloc(**kw) == code
+    assert crattn.crattn_last_error() != ""
+
+
+def test_noalloc_scratch_covers_the_sp_rank_slice():
+    # the SP-rank slice's split partials fit the fixed scratch
+    need = crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680, 128)
+    assert 0 < need <= 32 << 20
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 4, 4096, 65536, 61440, 4096, 128) > 32 << 20
+
+
 def _attn_rope(**kw):
     # tiny geometry: 64-token chunks of one 8x8 frame, the last chunk at t0 3
     a = dict(q=FAKE, table=FAKE, mt=4, mh=8, mw=8, t0=3, gh=8, gw=8, k=FAKE, v=FAKE, cap=256,
