@@ -35,6 +35,7 @@
 #include "crattn_internal.h"
 #include "rope_common.h"
 #include "../../include/crattn.h"
+#include "attn_loop.inc"
 
 #include <math.h>
 
@@ -894,6 +895,277 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Dense chunk-causal attention, head_dim 128, with the key loop written in
+// CDNA4 assembly (attn_loop.inc, generated by gen_attn_loop.py).
+//
+// A workgroup of 4 wavefronts (one per SIMD) owns 256 query rows of one
+// (batch, head), each wavefront 64 rows as two 32-query blocks, so each K or
+// V fragment read from LDS feeds two matrix products.  With 64 query rows a
+// wavefront needs O (128 fp32 registers) and Q (64) beside the scores: O and
+// Q stay in the accumulation registers, where the matrix cores read and
+// write them directly, and the loop's registers are fixed by hand (the
+// compiler's own allocation of this shape spills).  The loop follows the
+// same arithmetic as attn_fwd_kernel (online softmax in base 2 with a lazily
+// raised maximum, P rounded to bf16, O in fp32) except that the row sums
+// add the bf16-rounded probabilities, the values the P.V product uses.
+//
+// This function does what the compiler is good at: it decodes the work
+// item, loads (and for ROPE rotates) the queries, computes the lane's copy
+// offsets and LDS fragment addresses, runs the loop, then normalises and
+// stores.
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x32_t __attribute__((ext_vector_type(32)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+#define CRT_D(p, t) \
+  p #t "0", p #t "1", p #t "2", p #t "3", p #t "4", p #t "5", p #t "6", p #t "7", p #t "8", p #t "9"
+
+template <bool ROPE>
+__global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
+  constexpr int D = 128, kBN = 64, BM = 256;
+  constexpr int DK = D / 16, DB = D / 32;
+  constexpr int KP = Pitch<D>::K, VP = Pitch<D>::V;
+  constexpr int K_CELLS = kBN * KP, V_CELLS = kBN * VP;
+  constexpr int STAGE_CELLS = K_CELLS + V_CELLS;
+  constexpr int STAGE_BYTES = STAGE_CELLS * 16;
+  static_assert(STAGE_BYTES == 37888 && K_CELLS * 16 == 17408, "layout the loop assumes");
+  __shared__ uint4 lds_ring[4 * STAGE_CELLS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- work item: (b, h, query tile, key split), XCD-grouped ----
+  int64_t item;
+  {
+    const int64_t G = gridDim.x;
+    const int64_t xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
+    const int64_t q = G / kXcds, r = G % kXcds;
+    item = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  }
+  const int split = (int)(item % a.splits);
+  int64_t bid = item / a.splits;
+  const int64_t tile = bid % a.n_tiles;
+  bid /= a.n_tiles;
+  const int h = (int)(bid % a.H);
+  const int b = (int)(bid / a.H);
+  int64_t seg, t_in, seg_row0, seg_rows;
+  if (tile < a.tiles0) {
+    seg = 0;
+    t_in = tile;
+    seg_row0 = 0;
+    seg_rows = a.seg0_rows;
+  } else {
+    const int64_t u = tile - a.tiles0;
+    if (u < a.n_full * a.tiles_full) {
+      const int64_t s = u / a.tiles_full;
+      t_in = u - s * a.tiles_full;
+      seg = 1 + s;
+      seg_row0 = a.seg0_rows + s * a.L;
+      seg_rows = a.L;
+    } else {
+      t_in = u - a.n_full * a.tiles_full;
+      seg = 1 + a.n_full;
+      seg_row0 = a.seg0_rows + a.n_full * a.L;
+      seg_rows = a.last_rows;
+    }
+  }
+  const int64_t row0 = seg_row0 + t_in * BM;
+  const int64_t nrows = min((int64_t)BM, seg_rows - t_in * BM);
+  const int64_t q_chunk = a.q_pos0 / a.L + seg;
+  const int limit = (int)min(a.kv_len, (q_chunk + 1) * a.L);
+  const int nkt = (limit + kBN - 1) / kBN;
+  const int kt_begin = __builtin_amdgcn_readfirstlane(split * nkt / a.splits);
+  const int kt_end = __builtin_amdgcn_readfirstlane((split + 1) * nkt / a.splits);
+  const int last = kt_end - 1;
+  const int rem = __builtin_amdgcn_readfirstlane(min(kBN, limit - last * kBN));
+
+  // ---- this wavefront's 64 queries as B operands (Q in registers) ----
+  const int64_t wrow0 = row0 + (int64_t)wave * 64;
+  bf16x8_t qf[2][DK];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t row = wrow0 + qb * 32 + l32;
+    const bool ok = row < row0 + nrows;
+    const uint16_t *qp = a.q + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (ok) x = *reinterpret_cast<const uint4 *>(qp + ks * 16);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
+    }
+    if constexpr (ROPE) {
+      constexpr int HT = (D - 4 * (D / 6)) / 2;
+      constexpr int HH = D / 6;
+      const Pos p = decode_pos(a.tok_off + (uint32_t)min(row, a.Lq - 1), a.per_frame, a.gw, a.t0);
+      const float2 *ax[3] = {a.table + p.t * HT + 4 * hf,
+                             a.table + a.tg.base_h + p.h * HH - HT + 4 * hf,
+                             a.table + a.tg.base_w + p.w * HH - HT - HH + 4 * hf};
+      auto axis = [](int q) { return q < HT ? 0 : q < HT + HH ? 1 : 2; };
+      float2 cs[DK][4];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q0 = ks * 8 + e;
+          const int a0 = axis(q0), a1 = axis(q0 + 4);
+          const float2 *ptr = a0 == a1 ? ax[a0] : (hf ? ax[a1] : ax[a0]);
+          cs[ks][e] = ptr[q0];
+        }
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
+        uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float2 r = rotate_pair(__uint_as_float(wv[e] << 16),
+                                       __uint_as_float(wv[e] & 0xffff0000u), cs[ks][e]);
+          wv[e] = pack_bf16(r.x, r.y);
+        }
+        qf[qb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+      }
+    }
+  }
+  f32x32_t qa[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) {
+      const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
+      qa[qb][4 * ks + 0] = __uint_as_float(x.x);
+      qa[qb][4 * ks + 1] = __uint_as_float(x.y);
+      qa[qb][4 * ks + 2] = __uint_as_float(x.z);
+      qa[qb][4 * ks + 3] = __uint_as_float(x.w);
+    }
+
+  // ---- the lane's copy offsets: slot n of the tile (K: instructions
+  // wave + 4n, and for n = 4 instruction 16 on wave 0, a repeat of slot 3
+  // elsewhere; V: wave + 4n), full rows and rows clamped to the last valid
+  // key of the final tile ----
+  u32x8_t dma_a, dmal_a;
+  u32x2_t dma_b, dmal_b;
+  {
+    uint32_t off[10], offl[10];
+#pragma unroll
+    for (int n = 0; n < 10; ++n) {
+      const bool kside = n < 5;
+      const int j = kside ? (n < 4 ? wave + 4 * n : (wave == 0 ? 16 : wave + 12)) : wave + 4 * (n - 5);
+      const int pitch = kside ? KP : VP;
+      const int cell = j * 64 + lane;
+      const int row = cell / pitch, c = cell - row * pitch;
+      const uint32_t col = (uint32_t)(c < D / 8 ? c * 16 : 0);
+      off[n] = (uint32_t)row * (D * 2) + col;
+      offl[n] = (uint32_t)min(row, rem - 1) * (D * 2) + col;
+    }
+    for (int n = 0; n < 8; ++n) {
+      dma_a[n] = off[n];
+      dmal_a[n] = offl[n];
+    }
+    dma_b[0] = off[8];
+    dma_b[1] = off[9];
+    dmal_b[0] = offl[8];
+    dmal_b[1] = offl[9];
+  }
+  // ---- LDS addresses: ring base, per-lane fragment bases per stage ----
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const uint32_t ring = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(lds_ring));
+  u32x8_t bases;
+  {
+    const uint32_t kb0 = ring + (uint32_t)((k_row_perm(l32) * KP + hf) * 16);
+    const int vj = lane & 15;
+    const int v_dim = (l32 >> 4) * 16 + 4 * (vj & 3);
+    const uint32_t vb0 =
+        ring + K_CELLS * 16 + (uint32_t)((8 * hf + (vj >> 2)) * VP * 16 + v_dim * 2);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bases[s] = kb0 + s * STAGE_BYTES;
+      bases[4 + s] = vb0 + s * STAGE_BYTES;
+    }
+  }
+  const uint32_t kh8 = 8u * (uint32_t)hf;
+  const int64_t head_off = ((int64_t)b * a.H + h) * a.cap * D;
+  const uint16_t *kh = a.k + head_off;
+  const uint16_t *vh = a.v + head_off;
+  const uint32_t wb = ring + (uint32_t)wave * 1024u;
+  const uint32_t k5 = (uint32_t)((wave == 0 ? 16 : wave + 12) - wave) * 1024u;
+  const float sc = a.scale_log2;
+
+  f32x32_t o[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int r = 0; r < 32; ++r) o[g][r] = 0.f;
+  f32x2_t m2 = {-INFINITY, -INFINITY};
+  f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
+  int t = kt_begin;
+  if (kt_begin < kt_end) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile(CRATTN_ATTN_LOOP_ASM
+                 : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
+                   "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
+                   "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t)
+                 : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
+                   "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
+                   "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
+                   "{s71}"(sc), "{s72}"(wb), "{s73}"(k5)
+                 : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
+                   CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5), CRT_D("v", 6),
+                   CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9), CRT_D("v", 10), CRT_D("v", 11),
+                   CRT_D("v", 12), CRT_D("v", 13), CRT_D("v", 14), CRT_D("v", 15),
+                   CRT_D("v", 16), CRT_D("v", 17), CRT_D("v", 18), "v190", "v191", "v198",
+                   "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "s74", "s75",
+                   "s76", "s77", "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86",
+                   "s87", "m0", "vcc", "scc", "memory");
+#pragma clang diagnostic pop
+  }
+
+  // ---- epilogue: normalise and store (rows of this wave's two blocks) ----
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = half_swap_sum(l4[2 * qb] + l4[2 * qb + 1]);
+    const float m_run = m2[qb];
+    const int64_t row = wrow0 + qb * 32 + l32;
+    if (row >= row0 + nrows) continue;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const float lse2 = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
+    if (a.splits == 1) {
+      uint16_t *op = a.out + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int base = qb * 16 + i4 * 4;
+          uint2 w;
+          w.x = pack_bf16(o[db][base + 0] * inv, o[db][base + 1] * inv);
+          w.y = pack_bf16(o[db][base + 2] * inv, o[db][base + 3] * inv);
+          *reinterpret_cast<uint2 *>(op + db * 32 + i4 * 8) = w;
+        }
+      if (hf == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Lq + row] = lse2 * kLn2;
+    } else {
+      const int64_t prow = (((int64_t)split * a.B + b) * a.H + h) * a.Lq + row;
+      float *op = a.ws_o + prow * D + hf * 4;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int base = qb * 16 + i4 * 4;
+          *reinterpret_cast<float4 *>(op + db * 32 + i4 * 8) =
+              make_float4(o[db][base + 0] * inv, o[db][base + 1] * inv, o[db][base + 2] * inv,
+                          o[db][base + 3] * inv);
+        }
+      if (hf == 0) a.ws_lse[prow] = lse2;
+    }
+  }
+}
+#undef CRT_D
+
 struct CombineArgs {
   const float *ws_o;
   const float *ws_lse;
@@ -1159,9 +1431,16 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
     e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, grid, s)
                    : launch_fwd<64, 8, 1, 1, false, false, true>(k, grid, s);
   } else if (a.D == 128) {
-    e = a.sel != nullptr ? launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s)
-        : a.rope         ? launch_fwd<128, 8, 1, 1, true, false>(k, p.grid, s)
-                         : launch_fwd<128, 8, 1, 1, false, false>(k, p.grid, s);
+    if (a.sel != nullptr) {
+      e = launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s);
+    } else {
+      // dense: the kernel with the hand-scheduled key loop
+      if (a.rope)
+        hipLaunchKernelGGL(attn_fwd64_kernel<true>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+      else
+        hipLaunchKernelGGL(attn_fwd64_kernel<false>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+      e = hipGetLastError();
+    }
   } else {
     e = a.sel != nullptr ? launch_fwd<64, 8, 1, 1, false, true>(k, p.grid, s)
         : a.rope         ? launch_fwd<64, 8, 1, 1, true, false>(k, p.grid, s)
