@@ -2,7 +2,9 @@
 
     python -m autoregressive_video_diffusion_amd.build [--jobs N]
 
-Each source is compiled to an object in parallel, then linked into
+The assembly of the dense attention's key loop is generated first
+(csrc/gen_attn_loop.py -> csrc/attn_loop.inc).  Each source is compiled to an
+object in parallel, then linked into
 ``autoregressive_video_diffusion_amd/libcrattn.so``.  Packed-fp32 VALU
 instructions are disabled for all device code.
 """
@@ -13,13 +15,14 @@ import concurrent.futures as cf
 import os
 import shutil
 import subprocess
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libcrattn.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "rope.hip", "attn.hip", "qkv.hip", "hsa.hip", "svg2.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "rope.hip", "attn.hip", "qkv.hip", "hsa.hip", "svg2.hip"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
@@ -42,7 +45,14 @@ def _compile(src: str) -> str:
     return obj
 
 
+def generate() -> None:
+    """Regenerate the assembly of the attention key loop (attn_loop.inc)."""
+    subprocess.run([sys.executable, os.path.join(CSRC, "gen_attn_loop.py"), "--out",
+                    os.path.join(CSRC, "attn_loop.inc")], check=True)
+
+
 def build(jobs: int | None = None) -> str:
+    generate()
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(jobs) as ex:

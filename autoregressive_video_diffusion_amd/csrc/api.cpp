@@ -101,8 +101,8 @@ int rope_apply_append(const void *q, void *q_out, const void *k, const void *v, 
     return fail(CRATTN_EINVAL, "rope_apply_append: B=%d H=%d n=%lld must be >= 1", B, H,
                 (long long)n);
   if (cap < 1 || cache_pos < 0 || cache_pos > cap || n > cap - cache_pos)
-    return fail(CRATTN_EINVAL, "rope_apply_append: rows [%lld, %lld) outside the cache (cap %lld)",
-                (long long)cache_pos, (long long)(cache_pos + n), (long long)cap);
+    return fail(CRATTN_EINVAL, "rope_apply_append: %lld rows from row %lld leave the cache (cap %lld)",
+                (long long)n, (long long)cache_pos, (long long)cap);
   if (t0 < 0 || tok_off < 0 || grid_h < 1 || grid_w < 1)
     return fail(CRATTN_EINVAL, "rope_apply_append: t0, tok_off >= 0 and grid >= 1 required");
   if (max_t < 1 || max_h < 1 || max_w < 1 || max_t > kMaxExtent || max_h > kMaxExtent ||
@@ -176,8 +176,8 @@ int qkv_rope_append(const void *x, const void *w, void *q_out, void *k_cache, vo
     return fail(CRATTN_ENOTSUP, "qkv_rope_append: C=%d must be a multiple of 64, at most 65536",
                 C);
   if (cap < 1 || cache_pos < 0 || cache_pos > cap || n > cap - cache_pos)
-    return fail(CRATTN_EINVAL, "qkv_rope_append: rows [%lld, %lld) outside the cache (cap %lld)",
-                (long long)cache_pos, (long long)(cache_pos + n), (long long)cap);
+    return fail(CRATTN_EINVAL, "qkv_rope_append: %lld rows from row %lld leave the cache (cap %lld)",
+                (long long)n, (long long)cache_pos, (long long)cap);
   if (t0 < 0 || tok_off < 0 || grid_h < 1 || grid_w < 1)
     return fail(CRATTN_EINVAL, "qkv_rope_append: t0, tok_off >= 0 and grid >= 1 required");
   if (max_t < 1 || max_h < 1 || max_w < 1 || max_t > kMaxExtent || max_h > kMaxExtent ||
@@ -454,8 +454,8 @@ int hsa_pool_keys(const void *k_cache, int64_t cap, int64_t row0, int64_t nrows,
                                "frames required");
   if (row0 < 0 || nrows < 1 || row0 % per_frame != 0 || nrows % per_frame != 0 ||
       nrows > cap - row0)
-    return fail(CRATTN_EINVAL, "hsa_pool_keys: rows [%lld, %lld) must be whole frames inside "
-                               "[0, %lld)", (long long)row0, (long long)(row0 + nrows),
+    return fail(CRATTN_EINVAL, "hsa_pool_keys: %lld rows from row %lld must be whole frames "
+                               "inside [0, %lld)", (long long)nrows, (long long)row0,
                 (long long)cap);
   if (hsa_pool_bytes(B, H, cap, D, per_frame) == 0 || (double)B * H * (double)cap * D > (double)kMaxElems)
     return fail(CRATTN_EINVAL, "hsa_pool_keys: sizes too large");

@@ -65,7 +65,7 @@ struct AttnKArgs {
   float *ws_lse;  // [splits][B][H][Lq]      base-2 log-sum-exp
   int B, H;
   int64_t Lq, cap, kv_len, q_pos0, L;
-  float scale_log2;
+  float scale_log2, inv_scale_log2;
   int64_t seg0_rows, tiles0, tiles_full, n_full, last_rows, n_tiles;
   int splits;
   // Causal-RoPE of the queries on load (the rotating instance only)
@@ -1095,6 +1095,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
   const uint32_t wb = ring + (uint32_t)wave * 1024u;
   const uint32_t k5 = (uint32_t)((wave == 0 ? 16 : wave + 12) - wave) * 1024u;
   const float sc = a.scale_log2;
+  const float inv_sc = a.inv_scale_log2;
 
   f32x32_t o[4];
 #pragma unroll
@@ -1114,13 +1115,14 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
                  : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
                    "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
                    "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
-                   "{s71}"(sc), "{s72}"(wb), "{s73}"(k5)
+                   "{s71}"(sc), "{s72}"(wb), "{s73}"(k5), "{s88}"(inv_sc)
                  : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
                    CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5), CRT_D("v", 6),
                    CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9), CRT_D("v", 10), CRT_D("v", 11),
                    CRT_D("v", 12), CRT_D("v", 13), CRT_D("v", 14), CRT_D("v", 15),
                    CRT_D("v", 16), CRT_D("v", 17), CRT_D("v", 18), "v190", "v191", "v198",
-                   "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "s74", "s75",
+                   "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v236", "v237",
+                   "s74", "s75",
                    "s76", "s77", "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86",
                    "s87", "m0", "vcc", "scc", "memory");
 #pragma clang diagnostic pop
@@ -1208,16 +1210,6 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   wv.y = pack_bf16(acc.z * inv, acc.w * inv);
   *reinterpret_cast<uint2 *>(a.out + (((int64_t)b * a.Lq + row) * a.H + h) * a.D + c4 * 4) = wv;
   if (c4 == 0 && a.lse != nullptr) a.lse[r] = (mx + __log2f(wsum)) * kLn2;
-}
-
-// Launch shapes: waves per workgroup, 32-query blocks per wave, minimum
-// resident workgroups per compute unit.
-struct FwdShape {
-  int waves, qb, bn;
-};
-FwdShape fwd_shape(int D) {
-  (void)D;
-  return FwdShape{8, 1, 64};
 }
 
 // Work order of the gather instance: the (b, h, slot) entries with rows,
@@ -1311,47 +1303,6 @@ void *attn_scratch(hipError_t *err) {
   return p;
 }
 
-AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
-                   int64_t chunk_tokens, int D, bool allow_split) {
-  AttnPlan p{};
-  p.d = D;
-  const FwdShape fs = fwd_shape(D);
-  p.bm = fs.waves * fs.qb * 32;
-  p.bn = fs.bn;
-  const int64_t L = chunk_tokens;
-  const int64_t c0 = q_pos0 / L;
-  p.seg0_rows = std::min(Lq, (c0 + 1) * L - q_pos0);
-  p.tiles0 = (p.seg0_rows + p.bm - 1) / p.bm;
-  const int64_t rest = Lq - p.seg0_rows;
-  p.n_full = rest / L;
-  p.last_rows = rest - p.n_full * L;
-  p.tiles_full = (L + p.bm - 1) / p.bm;
-  p.n_tiles = p.tiles0 + p.n_full * p.tiles_full + (p.last_rows + p.bm - 1) / p.bm;
-  const int64_t units = (int64_t)B * H * p.n_tiles;
-  // Fewest key tiles any query tile has (the first segment sees the least).
-  const int64_t min_keys = std::min(kv_len, (c0 + 1) * L);
-  const int64_t min_ktiles = (min_keys + p.bn - 1) / p.bn;
-  constexpr int64_t kSlots = 256;  // one workgroup per compute unit of an MI355X
-  p.splits = 1;
-  // Split the key range only when the query tiles alone leave most of the
-  // chip idle: partials cost (D + 1) * 4 bytes per row and split of traffic.
-  if (allow_split && units * 2 <= kSlots) {
-    double best = (double)units / (double)(((units + kSlots - 1) / kSlots) * kSlots);
-    for (int s = 2; s <= 16; ++s) {
-      if (min_ktiles / s < 8) break;
-      const int64_t u = units * s;
-      const double eff = (double)u / (double)(((u + kSlots - 1) / kSlots) * kSlots);
-      if (eff > best + 0.05) {
-        best = eff;
-        p.splits = s;
-      }
-    }
-  }
-  p.grid = units * p.splits;
-  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0;
-  return p;
-}
-
 hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   AttnKArgs k;
   k.q = static_cast<const uint16_t *>(a.q);
@@ -1368,6 +1319,7 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.L = a.chunk_tokens;
   const float scale = a.scale > 0.f ? a.scale : 1.0f / sqrtf((float)a.D);
   k.scale_log2 = scale * 1.44269504088896340736f;
+  k.inv_scale_log2 = 1.0f / k.scale_log2;
   k.seg0_rows = p.seg0_rows;
   k.tiles0 = p.tiles0;
   k.tiles_full = p.tiles_full;

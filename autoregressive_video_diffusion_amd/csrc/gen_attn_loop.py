@@ -68,6 +68,7 @@ def VF(g):
 
 
 VM = (192, 193)                  # running max per query block (base-2 units)
+VTH = (236, 237)                 # rescale threshold per block: (m + 8) / c, in raw scores
 VL = ((194, 195), (196, 197))    # row-sum chains per query block
 VT = tuple(range(198, 206))      # temporaries
 VONES = 206                      # bf16 (1, 1)
@@ -87,7 +88,7 @@ def Q(qb, ks):
 
 
 # scalar registers (inputs first, then scratch)
-sKH, sVH, sT, sLAST, sREM, sC, sWB, sK5 = 64, 66, 68, 69, 70, 71, 72, 73
+sKH, sVH, sT, sLAST, sREM, sC, sWB, sK5, sIC = 64, 66, 68, 69, 70, 71, 72, 73, 88
 sTILE, sT3, sKA, sVA, sSB, sN0, sN1, sTMP = 74, 75, 76, 78, 80, 82, 84, 86
 SCRATCH_S = tuple(range(74, 88))
 
@@ -247,45 +248,77 @@ def exp_group(buf, qb, c, half):
     return out
 
 
-def max_ops(buf, qb, tmp):
+MAX_CHAINS = 4      # independent max3 chains per query block (1 or 4)
+EXP_PAIRS = True    # interleave the exponential groups two by two
+EXP_WEAVE = False   # within a pair, put a non-exponential instruction after each v_exp
+MERGE_WAITS = False # fold an lgkmcnt wait into the one before it when possible
+ABLATE = ()         # timing probes only: work left out of the main steps
+
+
+def max_ops(buf, qb, tmp, chain_tmps=()):
     """Row maximum of S(buf)[*][qb] over this lane's 32 keys, then over the
-    partner lane (l ^ 32), scaled to base-2 units: result in v[tmp]."""
+    partner lane (l ^ 32), in raw score units: result in v[tmp] (v[tmp+1]
+    is clobbered).  With MAX_CHAINS = 4 the 32 values are reduced in four
+    independent chains (temporaries v[tmp], v[tmp+1] and chain_tmps) joined
+    at the end, so consecutive max3 do not wait on each other."""
     vals = [S(buf, kb, qb) + r for kb in range(2) for r in range(16)]
     m = f"v{tmp}"
-    out = [valu(f"v_max3_f32 {m}, {vr(vals[0])}, {vr(vals[1])}, {vr(vals[2])}", (m,),
-                tuple(f"v{x}" for x in vals[:3]))]
-    i = 3
-    while i < len(vals):
-        if i + 1 < len(vals):
-            out.append(valu(f"v_max3_f32 {m}, {m}, {vr(vals[i])}, {vr(vals[i + 1])}", (m,),
-                            (m, f"v{vals[i]}", f"v{vals[i + 1]}")))
-            i += 2
-        else:
-            out.append(valu(f"v_max_f32 {m}, {m}, {vr(vals[i])}", (m,), (m, f"v{vals[i]}")))
-            i += 1
+
+    def chain(dst, vs):
+        out = [valu(f"v_max3_f32 {dst}, {vr(vs[0])}, {vr(vs[1])}, {vr(vs[2])}", (dst,),
+                    tuple(f"v{x}" for x in vs[:3]))]
+        i = 3
+        while i < len(vs):
+            if i + 1 < len(vs):
+                out.append(valu(f"v_max3_f32 {dst}, {dst}, {vr(vs[i])}, {vr(vs[i + 1])}", (dst,),
+                                (dst, f"v{vs[i]}", f"v{vs[i + 1]}")))
+                i += 2
+            else:
+                out.append(valu(f"v_max_f32 {dst}, {dst}, {vr(vs[i])}", (dst,),
+                                (dst, f"v{vs[i]}")))
+                i += 1
+        return out
+
+    if MAX_CHAINS == 1 or not chain_tmps:
+        out = chain(m, vals)
+    else:
+        dsts = [m, f"v{tmp + 1}"] + [f"v{x}" for x in chain_tmps]
+        parts = [chain(d, vals[8 * i:8 * i + 8]) for i, d in enumerate(dsts)]
+        out = [ins for grp in zip(*parts) for ins in grp]          # round-robin
+        out.append(valu(f"v_max3_f32 {m}, {dsts[0]}, {dsts[1]}, {dsts[2]}", (m,),
+                        tuple(dsts[:3])))
+        out.append(valu(f"v_max_f32 {m}, {m}, {dsts[3]}", (m,), (m, dsts[3])))
     t2 = f"v{tmp + 1}"
     out.append(valu(f"v_mov_b32 {t2}, {m}", (t2,), (m,)))
     out.append(valu(f"v_permlane32_swap_b32 {m}, {t2}", (m, t2), (m, t2), "perm"))
     out.append(valu(f"v_max_f32 {m}, {m}, {t2}", (m,), (m, t2)))
-    out.append(valu(f"v_mul_f32 {m}, {sr(sC)}, {m}", (m,), (m,)))
     return out
 
 
+def threshold(qb):
+    """VTH[qb] = (m + 8) / c: a raw score above it would give p > 2^8."""
+    t = VTH[qb]
+    return [valu(f"v_add_f32 {vr(t)}, 0x41000000, {vr(VM[qb])}", (f"v{t}",), (f"v{VM[qb]}",)),
+            valu(f"v_mul_f32 {vr(t)}, {sr(sIC)}, {vr(t)}", (f"v{t}",), (f"v{t}",))]
+
+
 def rescale_block(cur_buf, tag):
-    """Raise the running max where a lane's new candidate exceeds it by more
-    than 2^8 and rescale that row's sums and O (rare: early tiles).  The
-    candidates are in VT[0] (qb 0) and VT[2] (qb 1), the per-lane decisions in
+    """Raise the running max where a lane's new maximum exceeds it by more
+    than 2^8 and rescale that row's sums and O (rare: early tiles).  The raw
+    maxima are in VT[0] (qb 0) and VT[2] (qb 1), the per-lane decisions in
     sN0 / sN1.  S(cur_buf) is free here and serves as the buffer for O."""
     out = [label(f"{tag}")]
     for qb in range(2):
         mc, need = VT[2 * qb], (sN0, sN1)[qb]
         mn, al = VT[4 + 2 * qb], VT[5 + 2 * qb]
-        out += [valu(f"v_cndmask_b32_e64 {vr(mn)}, {vr(VM[qb])}, {vr(mc)}, {sr(need, 2)}",
+        out += [valu(f"v_mul_f32 {vr(mc)}, {sr(sC)}, {vr(mc)}", (f"v{mc}",), (f"v{mc}",)),
+                valu(f"v_cndmask_b32_e64 {vr(mn)}, {vr(VM[qb])}, {vr(mc)}, {sr(need, 2)}",
                      (f"v{mn}",), (f"v{VM[qb]}", f"v{mc}")),
                 valu(f"v_sub_f32 {vr(al)}, {vr(VM[qb])}, {vr(mn)}", (f"v{al}",),
                      (f"v{VM[qb]}", f"v{mn}")),
                 valu(f"v_exp_f32 {vr(al)}, {vr(al)}", (f"v{al}",), (f"v{al}",), "trans"),
                 valu(f"v_mov_b32 {vr(VM[qb])}, {vr(mn)}", (f"v{VM[qb]}",), (f"v{mn}",))]
+        out += threshold(qb)
         for ch in range(2):
             lr = VL[qb][ch]
             out.append(valu(f"v_mul_f32 {vr(lr)}, {vr(lr)}, {vr(al)}", (f"v{lr}",),
@@ -358,14 +391,37 @@ def pv_mfmas():
     return out
 
 
+def exp_chunk(cur, c):
+    """The exponentials of chunk c of S(cur), both query blocks: 4 groups of
+    12 instructions; with EXP_PAIRS two groups are merged stage by stage
+    (fma, exp, cvt, dot2), doubling the distance between each instruction
+    and the one that reads its result."""
+    groups = [exp_group(cur, qb, c, half) for qb in range(2) for half in range(2)]
+    if not EXP_PAIRS:
+        return [i for g in groups for i in g]
+    out = []
+    for a, b in ((groups[0], groups[1]), (groups[2], groups[3])):
+        if EXP_WEAVE:
+            # fma a | exp a with fma b | exp b with cvt/dot2 a | cvt/dot2 b
+            out += a[0:4]
+            for k in range(4):
+                out += [a[4 + k], b[k]]
+            x = a[8:12]
+            for k in range(4):
+                out += [b[4 + k], x[k]]
+            out += b[8:12]
+        else:
+            for lo, hi in ((0, 4), (4, 8), (8, 10), (10, 12)):
+                out += a[lo:hi] + b[lo:hi]
+    return out
+
+
 def exp_items(cur, lo, hi):
     """The exponentials of S(cur), chunk by chunk (chunk c is read by the PV
     products base + 8c + qb), spread over gaps [lo, hi)."""
     instrs = []
     for c in range(4):
-        for qb in range(2):
-            for half in range(2):
-                instrs += exp_group(cur, qb, c, half)
+        instrs += exp_chunk(cur, c)
     return spread(instrs, lo, hi)
 
 
@@ -375,17 +431,19 @@ def exp_items_due(cur):
     c - 1."""
     out = []
     for c in range(4):
-        instrs = []
-        for qb in range(2):
-            for half in range(2):
-                instrs += exp_group(cur, qb, c, half)
+        instrs = exp_chunk(cur, c)
         out += [(0, i) for i in instrs] if c == 0 else spread(instrs, 8 * c - 8, 8 * c - 1)
     return out
 
 
+KR_AHEAD = 2.5      # gaps between a K fragment's read and its first product
+VR_AHEAD = 3.0      # the same for V^T fragments (ring of 4: at most 6)
+
+
 def k_read_items(stage, frags):
-    """K fragment f feeds QK products 2f and 2f+1: read it two products ahead."""
-    return [(2 * f - 2.5, ins) for f in frags for ins in k_read(f, stage)]
+    """K fragment f feeds QK products 2f and 2f+1; its ring slot was last read
+    by product 2f - 7, so it can be read up to six products ahead."""
+    return [(2 * f - KR_AHEAD, ins) for f in frags for ins in k_read(f, stage)]
 
 
 def v_read_items(stage, base):
@@ -394,8 +452,23 @@ def v_read_items(stage, base):
     out = []
     for g in range(16):
         for j, ins in enumerate(v_read(g, stage)):
-            out.append((base + 2 * g - 3 + 0.1 * j, ins))
+            out.append((base + 2 * g - VR_AHEAD + 0.1 * j, ins))
     return out
+
+
+def _ablate(items):
+    """Drop classes of work from a step's items (timing probes: the results
+    are wrong, every access stays where it was)."""
+    def drop(i):
+        t = i.text
+        return (("exp" in ABLATE and (t.startswith("v_fma_f32") or t.startswith("v_exp_f32") or
+                                      t.startswith("v_cvt_pk") or t.startswith("v_dot2"))) or
+                ("max" in ABLATE and (t.startswith("v_max") or "permlane" in t or
+                                      (t.startswith("v_mov_b32") and i.kind == "valu"))) or
+                ("lds" in ABLATE and i.kind == "lds") or
+                ("dma" in ABLATE and (i.kind == "vmem" or t.startswith("s_add_u32 m0"))) or
+                ("barrier" in ABLATE and (i.kind == "barrier" or t.startswith("s_waitcnt vmcnt"))))
+    return [(t, i) for t, i in items if not drop(i)]
 
 
 def step(phi):
@@ -421,7 +494,9 @@ def step(phi):
     items += exp_items(cur, 0, 54)
     items += v_read_items(vst, 32)
     # row maximum of S(t+1) (its last products are 28..31)
-    mx = max_ops(nxt, 0, VT[0]) + max_ops(nxt, 1, VT[2])
+    m0 = max_ops(nxt, 0, VT[0], (VT[4], VT[5]))
+    m1 = max_ops(nxt, 1, VT[2], (VT[6], VT[7]))
+    mx = [i for pair in zip(m0, m1) for i in pair]   # the two blocks interleaved
     items += spread(mx, 34, 63)
     # before the last two products: tile t+2 has landed and every wave is
     # past its reads of tile t's V; then tile t+2's first K fragments
@@ -430,14 +505,16 @@ def step(phi):
               (62.7, Ins("s_barrier", "barrier"))]
     nkst = (phi + 2) % NS
     items += [(62.8 + 0.01 * f, ins) for f in range(4) for ins in k_read(f, nkst)]
+    if ABLATE:
+        items = _ablate(items)
+        if "mfma" in ABLATE:
+            mf = mf[:1]
     body = place(mf, items, head)
     tail = []
     for qb in range(2):
-        mc, t = VT[2 * qb], VT[4 + qb]
-        tail += [valu(f"v_add_f32 {vr(t)}, 0x41000000, {vr(VM[qb])}", (f"v{t}",),
-                      (f"v{VM[qb]}",)),
-                 valu(f"v_cmp_gt_f32_e64 {sr((sN0, sN1)[qb], 2)}, {vr(mc)}, {vr(t)}",
-                      (f"s{(sN0, sN1)[qb]}",), (f"v{mc}", f"v{t}"))]
+        mc = VT[2 * qb]
+        tail.append(valu(f"v_cmp_gt_f32_e64 {sr((sN0, sN1)[qb], 2)}, {vr(mc)}, {vr(VTH[qb])}",
+                         (f"s{(sN0, sN1)[qb]}",), (f"v{mc}", f"v{VTH[qb]}")))
     tail += [salu(f"s_or_b64 {sr(sTMP, 2)}, {sr(sN0, 2)}, {sr(sN1, 2)}"),
              branch(f"s_cbranch_scc1 crt_resc{phi}", f"crt_resc{phi}"),
              label(f"crt_rescr{phi}"),
@@ -497,8 +574,9 @@ def prologue():
     out = place(qk_mfmas(0), k_read_items(0, range(16)), out)
     for qb in range(2):
         out += max_ops(0, qb, VT[2 * qb])
-        out.append(valu(f"v_mov_b32 {vr(VM[qb])}, {vr(VT[2 * qb])}", (f"v{VM[qb]}",),
+        out.append(valu(f"v_mul_f32 {vr(VM[qb])}, {sr(sC)}, {vr(VT[2 * qb])}", (f"v{VM[qb]}",),
                         (f"v{VT[2 * qb]}",)))
+        out += threshold(qb)
     # tile t+1 has landed and is visible: its first K fragments
     out += [Ins("s_waitcnt vmcnt(10)", "wait"), Ins("s_barrier", "barrier")]
     for f in range(4):
@@ -524,7 +602,8 @@ def program():
     main, cold = [], []
     for phi in range(NS):
         b, c = step(phi)
-        check_p_ready(b)
+        if "exp" not in ABLATE:
+            check_p_ready(b)
         main += b
         cold += c
     lasts = []
@@ -683,6 +762,34 @@ def fix(prog):
     raise RuntimeError("hazard fixing did not converge")
 
 
+def merge_waits(prog, window=12):
+    """Fold an s_waitcnt lgkmcnt(n2) into an earlier lgkmcnt(n1) of the same
+    straight-line run when at most `window` instructions lie between them:
+    with k LDS reads issued in between, lgkmcnt(min(n1, n2 - k)) at the first
+    point already guarantees the second (reads complete in order)."""
+    out = list(prog)
+    i = 0
+    while i < len(out):
+        a = out[i]
+        if a.kind == "wait" and a.text.startswith("s_waitcnt lgkmcnt("):
+            n1 = int(a.text.split("(")[1].split(")")[0])
+            k = 0
+            for j in range(i + 1, min(len(out), i + 1 + window)):
+                b = out[j]
+                if b.kind in ("label", "branch", "barrier"):
+                    break
+                if b.kind == "lds":
+                    k += 1
+                if b.kind == "wait" and b.text.startswith("s_waitcnt lgkmcnt("):
+                    n2 = int(b.text.split("(")[1].split(")")[0])
+                    if n2 - k >= 0:
+                        out[i] = Ins(f"s_waitcnt lgkmcnt({min(n1, n2 - k)})", "wait")
+                        del out[j]
+                    break
+        i += 1
+    return out
+
+
 def stats(prog):
     import collections
     c = collections.Counter(i.kind for i in prog)
@@ -731,8 +838,33 @@ def main():
     ap.add_argument("--out", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                   "attn_loop.inc"))
     ap.add_argument("--report", action="store_true")
+    ap.add_argument("--kr-ahead", type=float, default=None, help="K fragment read distance")
+    ap.add_argument("--vr-ahead", type=float, default=None, help="V fragment read distance")
+    ap.add_argument("--max-chains", type=int, default=None, choices=(1, 4))
+    ap.add_argument("--exp-pairs", type=int, default=None, choices=(0, 1))
+    ap.add_argument("--exp-weave", type=int, default=None, choices=(0, 1))
+    ap.add_argument("--merge-waits", type=int, default=None, choices=(0, 1))
+    ap.add_argument("--ablate", default="", help="timing probe: comma list of exp, max, lds, "
+                    "dma, barrier, mfma left out of the main steps")
     args = ap.parse_args()
+    global KR_AHEAD, VR_AHEAD, MAX_CHAINS, EXP_PAIRS, EXP_WEAVE, MERGE_WAITS, ABLATE
+    if args.ablate:
+        ABLATE = tuple(args.ablate.split(","))
+    if args.exp_weave is not None:
+        EXP_WEAVE = bool(args.exp_weave)
+    if args.merge_waits is not None:
+        MERGE_WAITS = bool(args.merge_waits)
+    if args.max_chains is not None:
+        MAX_CHAINS = args.max_chains
+    if args.exp_pairs is not None:
+        EXP_PAIRS = bool(args.exp_pairs)
+    if args.kr_ahead is not None:
+        KR_AHEAD = args.kr_ahead
+    if args.vr_ahead is not None:
+        VR_AHEAD = args.vr_ahead
     prog = fix(program())
+    if MERGE_WAITS:
+        prog = fix(merge_waits(prog))
     lines = render(prog)
     text = ("// Generated by gen_attn_loop.py; do not edit.  The key loop of the dense\n"
             "// chunk-causal attention kernel (head_dim 128) in CDNA4 assembly: one\n"

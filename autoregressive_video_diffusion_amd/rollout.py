@@ -124,7 +124,9 @@ class ChunkRollout:
         return chunk_causal_attn_workspace_bytes(self.B, self.H, lq or self.L, kv_len,
                                                  q0 + tok_off, self.L, self.D)
 
-    def _rope(self, c, q, q_out, k, v, tok_off):
+    def rope_append(self, c: int, q, q_out, k, v, tok_off: int = 0):
+        """Rotate Q (if given) and K of chunk c, write Q' and append K', V to
+        the chunk's slot (one rope_apply_append call)."""
         rope_apply_append(q, q_out, k, v, self.k_cache, self.v_cache,
                           self.slot(c) * self.L + tok_off, self.table, self.max_t, self.grid_h,
                           self.grid_w, self.t0(c), tok_off, self.grid_h, self.grid_w)
@@ -165,7 +167,12 @@ class ChunkRollout:
         the chunk's slot, attend.  q, k, v, q_out, out: [B, n, H, D]."""
         if self.svg2 is not None and (tok_off != 0 or q.shape[1] != self.L):
             raise NotImplementedError("semantic-permutation attention covers whole chunks")
-        self._rope(c, q, q_out, k, v, tok_off)
+        self.rope_append(c, q, q_out, k, v, tok_off)
+        return self.attend(c, q_out, out, lse, tok_off)
+
+    def attend(self, c: int, q_out, out, lse=None, tok_off: int = 0):
+        """The attention of a denoising step of chunk c on its rotated
+        queries q_out (dense, HSA or semantic-permutation)."""
         kv_len, q0 = self.visible(c)
         if self.svg2 is not None:
             return self._svg2_attend(c, q_out, out, lse)
@@ -187,7 +194,7 @@ class ChunkRollout:
     def update(self, c: int, k, v, tok_off: int = 0):
         """Cache update of chunk c: rotate the clean K and store it with V
         (and, with HSA, pool the chunk's keys once the whole chunk is in)."""
-        self._rope(c, None, None, k, v, tok_off)
+        self.rope_append(c, None, None, k, v, tok_off)
         if self.hsa is not None and tok_off + k.shape[1] == self.L:
             hsa_pool_keys(self.k_cache, self.slot(c) * self.L, self.L, self.per_frame, self.pool)
         if self.svg2 is not None and tok_off + k.shape[1] == self.L:

@@ -8,8 +8,12 @@ The cos/sin table is built once before timing, as the method prescribes
 (precomputed contiguous tables).
 
 Inputs are synthetic N(0, 1) bf16 (seeded), resident in HBM before timing.
-Several complete buffer sets (inputs, outputs and KV cache, ~1.1 GB in all)
-are used round-robin, so no step finds its data in the 256 MB Infinity Cache.
+Eight complete buffer sets (inputs, outputs and KV cache, 273 MB each) are
+used round-robin: between two uses of one set the others move ~600 MB through
+HBM (the RoPE/append bursts alone, 86 MB per launch, move 7 x 86 MB), more
+than the 256 MB Infinity Cache, so no launch finds its data there.  Before
+the warm-up steps 64 untimed steps let the clock settle (it ramps over the
+first ~30 ms of matrix work); the line records both counts.
 
 Prints ONE JSON line.  Per-kernel times come from HIP events recorded on the
 stream the library launches on (torch's current stream).
@@ -87,6 +91,9 @@ def read_traffic(kernel="attn"):
         return None
 
 
+_PRIOR = {}
+
+
 class StepBuffers:
     def __init__(self, w, dev, seed_base):
         import torch
@@ -95,7 +102,9 @@ class StepBuffers:
 
         q, k, v = call_qkv(w, seed_base)
         self.q, self.k, self.v = q.to(dev), k.to(dev), v.to(dev)
-        kc, vc = prior_cache(w)
+        if w.name not in _PRIOR:   # the same prior cache contents in every set
+            _PRIOR[w.name] = prior_cache(w)
+        kc, vc = _PRIOR[w.name]
         self.kc, self.vc = kc.to(dev), vc.to(dev)
         self.q_out = torch.empty_like(self.q)
         self.out = torch.empty_like(self.q)
@@ -458,6 +467,257 @@ def rollout_ms(crattn, dev, reps=2, hsa=None):
     return (time.perf_counter() - t) * 1e3 / reps
 
 
+def hsa_win720(crattn, dev, dense_ms, kf=6, kb=32):
+    """HSA on the 720P window (t0 81, own chunk in slot 6 of the 7-slot
+    ring): key pooling of the ring, selection (kf of 18 history frames, kb
+    blocks per 256-row query block) and the sparse attention; FLOPs over the
+    keys each query block attends."""
+    import torch
+
+    from workloads import WIN720 as w, normal, prior_cache
+
+    per_frame, L, cap = w.grid_h * w.grid_w, w.chunk_tokens, w.cap
+    q = normal((w.B, w.lq, w.H, w.D), 720).to(dev)
+    kc, vc = (x.to(dev) for x in prior_cache(w))
+    out = torch.empty_like(q)
+    pool = torch.empty(crattn.hsa_pool_bytes(w.B, w.H, cap, w.D, per_frame) // 4,
+                       dtype=torch.float32, device=dev)
+    crattn.hsa_pool_keys(kc, 0, cap, per_frame, pool)
+    nqb = -(-w.lq // crattn.HSA_QBLOCK)
+    sel = torch.empty(w.B, w.H, nqb, kb, dtype=torch.int32, device=dev)
+    own = w.slot * L
+
+    def select_call(i):
+        crattn.hsa_select(q, pool, cap, cap, per_frame, own, L, kf, kb, sel)
+
+    def attn_call(i):
+        crattn.hsa_attn(q, kc, vc, cap, own, L, per_frame, sel, out)
+
+    def pool_call(i):
+        crattn.hsa_pool_keys(kc, own, L, per_frame, pool)
+
+    for f in (pool_call, select_call, attn_call):
+        f(0)
+        f(1)
+    torch.cuda.synchronize()
+    pool_ms = burst_ms(pool_call, 3, 5)[1]
+    sel_ms = burst_ms(select_call, 3, 5)[1]
+    attn_ms = burst_ms(attn_call, 3, 3)[1]
+    s_ = sel.cpu()
+    nbf = -(-per_frame // crattn.HSA_KBLOCK)
+    fl = 0
+    for i in range(nqb):
+        rows = min(crattn.HSA_QBLOCK, w.lq - i * crattn.HSA_QBLOCK)
+        for h in range(w.H):
+            ids = [int(x) for x in s_[0, h, i] if int(x) >= 0]
+            keys = L + sum(min(crattn.HSA_KBLOCK, per_frame - (x % nbf) * crattn.HSA_KBLOCK)
+                           for x in ids)
+            fl += 4 * rows * keys * w.D
+    tf = fl / (attn_ms * 1e-3) / 1e12
+    del q, kc, vc, out, pool
+    torch.cuda.empty_cache()
+    return {"kf": kf, "kb": kb, "pool_chunk_us": round(pool_ms * 1e3, 2),
+            "select_us": round(sel_ms * 1e3, 2), "attn_ms": round(attn_ms, 4),
+            "visible_flops": fl, "speedup_vs_dense_attn": round(dense_ms / attn_ms, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+
+
+def rollout_breakdown(crattn, dev):
+    """The 480P rollout (7 chunks x (4 denoising calls + 1 cache update)),
+    every call bracketed by events: per chunk the mean RoPE/append and
+    attention time of its denoising calls and the cache-update time, with
+    their rates against the rooflines, and the totals."""
+    import torch
+
+    from autoregressive_video_diffusion_amd.rollout import ChunkRollout
+    from workloads import ROLLOUT480 as w
+
+    ro = ChunkRollout(w.B, w.H, w.D, w.frames, w.grid_h, w.grid_w, window=7, max_chunks=7,
+                      device=dev)
+    n = w.chunk_tokens
+    g = torch.Generator(device="cpu").manual_seed(2024)
+    qkv = [tuple(torch.randn(w.B, n, w.H, w.D, generator=g).to(torch.bfloat16).to(dev)
+                 for _ in range(3)) for _ in range(5)]
+    q_out = torch.empty_like(qkv[0][0])
+    out = torch.empty_like(q_out)
+
+    def once(ev=None):
+        for c in range(7):
+            for j in range(4):
+                q, k, v = qkv[j]
+                if ev is not None:
+                    ev[c][j][0].record()
+                ro.rope_append(c, q, q_out, k, v)
+                if ev is not None:
+                    ev[c][j][1].record()
+                ro.attend(c, q_out, out)
+                if ev is not None:
+                    ev[c][j][2].record()
+            if ev is not None:
+                ev[c][4][0].record()
+            ro.update(c, qkv[4][1], qkv[4][2])
+            if ev is not None:
+                ev[c][4][1].record()
+
+    once()
+    torch.cuda.synchronize()
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [[[mk() for _ in range(3)] for _ in range(5)] for _ in range(7)]
+    t0 = time.perf_counter()
+    once(ev)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    rb, ub = rope_bytes(w.B, n, w.H, w.D), rope_bytes(w.B, n, w.H, w.D, with_q=False)
+    chunks, tot_a, tot_r, tot_u, tot_fl = [], 0.0, 0.0, 0.0, 0
+    for c in range(7):
+        a = [ev[c][j][1].elapsed_time(ev[c][j][2]) for j in range(4)]
+        r = [ev[c][j][0].elapsed_time(ev[c][j][1]) for j in range(4)]
+        u = ev[c][4][0].elapsed_time(ev[c][4][1])
+        fl = attn_flops(w.B, w.H, n, (c + 1) * n, w.D)
+        am = sum(a) / 4
+        chunks.append({"chunk": c, "keys": (c + 1) * n, "attn_ms": round(am, 4),
+                       "attn_tflops": round(fl / (am * 1e-3) / 1e12, 1),
+                       "rope_append_us": round(sum(r) / 4 * 1e3, 2),
+                       "cache_update_us": round(u * 1e3, 2)})
+        tot_a += sum(a)
+        tot_r += sum(r)
+        tot_u += u
+        tot_fl += 4 * fl
+    a_tf = tot_fl / (tot_a * 1e-3) / 1e12
+    r_gbs = (28 * rb + 7 * ub) / ((tot_r + tot_u) * 1e-3) / 1e9
+    return {"calls": "7 chunks x (4 x (RoPE/append + attention) + cache update)",
+            "wall_ms": round(wall, 3), "attn_ms_total": round(tot_a, 3),
+            "rope_append_ms_total": round(tot_r + tot_u, 4), "per_chunk": chunks,
+            "attn_roofline": {"bound": "mfma", "achieved": round(a_tf, 1),
+                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(a_tf / PEAK_BF16_TFLOPS, 4), "flops": tot_fl},
+            "rope_roofline": {"bound": "hbm", "achieved": round(r_gbs, 1), "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": round(r_gbs / PEAK_HBM_GBS, 4),
+                              "bytes": 28 * rb + 7 * ub}}
+
+
+def rope_append_rate(crattn, w, dev, sets=1, bursts=5, burst=10):
+    """RoPE/append of one denoising call of workload w over `sets` buffer
+    sets used round-robin: per-launch µs of the median burst, GB/s and the
+    fraction of HBM peak (algorithmic bytes, 6 tensors)."""
+    import torch
+
+    from workloads import call_qkv
+
+    mt, mh, mw = w.table_extents()
+    table = torch.empty(crattn.rope_table_bytes(w.D, mt, mh, mw) // 4, dtype=torch.float32,
+                        device=dev)
+    crattn.rope_precompute(table, w.D, mt, mh, mw, w.theta)
+    bufs = []
+    for i in range(sets):
+        q, k, v = (x.to(dev) for x in call_qkv(w, i))
+        kc = torch.empty(w.B, w.H, w.cap, w.D, dtype=torch.bfloat16, device=dev)
+        bufs.append((q, k, v, torch.empty_like(q), kc, torch.empty_like(kc)))
+
+    def call(i):
+        q, k, v, qo, kc, vc = bufs[i % sets]
+        crattn.rope_apply_append(q, qo, k, v, kc, vc, w.cache_pos, table, mt, mh, mw, w.t0,
+                                 w.tok_off, w.grid_h, w.grid_w)
+
+    for i in range(2 * sets + 2):
+        call(i)
+    torch.cuda.synchronize()
+    ms = burst_ms(call, bursts, max(burst, sets))[bursts // 2]
+    b = rope_bytes(w.B, w.lq, w.H, w.D)
+    gbs = b / (ms * 1e-3) / 1e9
+    del bufs
+    torch.cuda.empty_cache()
+    return {"us": round(ms * 1e3, 2), "bytes_per_launch": b, "buffer_sets": sets,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
+
+
+def sample_rows(lq, per_frame, stride=16):
+    """Every stride-th query row plus the first and last row of every frame."""
+    import numpy as np
+
+    rows = set(range(0, lq, stride))
+    for f0 in range(0, lq, per_frame):
+        rows |= {f0, min(lq, f0 + per_frame) - 1}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_extras():
+    """Host timings of the oracle on the other workloads: the SP-rank slice
+    whole; the 480P rollout and the 720P window on a 1/16 row sample (every
+    16th row plus the first and last row of every frame, all heads), scaled
+    to all rows and labelled extrapolated."""
+    import numpy as np
+
+    import oracle
+    from workloads import ROLLOUT480, SP480, WIN720
+
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(11)
+    res = {}
+
+    def kv(w, cap):
+        # data values do not change the oracle's cost: a random block tiled
+        blk = rng.standard_normal((w.B, w.H, 4096, w.D))
+        reps = -(-cap // 4096)
+        k = np.ascontiguousarray(np.tile(blk, (1, 1, reps, 1))[:, :, :cap])
+        return k, k * 0.5
+
+    w = SP480
+    q = rng.standard_normal((w.B, w.lq, w.H, w.D))
+    k, v = kv(w, w.cap)
+    t = time.perf_counter()
+    oracle.attn(q, k, v, w.kv_len, w.q_pos0, w.chunk_tokens, threads=threads)
+    dt = time.perf_counter() - t
+    fl = attn_flops(w.B, w.H, w.lq, w.kv_len, w.D)
+    res["sp480"] = {"s": round(dt, 2), "tflops": round(fl / dt / 1e12, 6), "rows": "all"}
+
+    w = ROLLOUT480
+    per_frame = w.grid_h * w.grid_w
+    rows = sample_rows(w.lq, per_frame)
+    q = rng.standard_normal((w.B, w.lq, w.H, w.D))
+    k, v = kv(w, w.cap)
+    dt, fl = 0.0, 0
+    for c in range(7):
+        t = time.perf_counter()
+        oracle.attn(q, k, v, (c + 1) * w.lq, c * w.lq, w.chunk_tokens, rows=rows,
+                    threads=threads)
+        dt += time.perf_counter() - t
+        fl += attn_flops(w.B, w.H, len(rows), (c + 1) * w.lq, w.D)
+    scale = 4 * w.lq / len(rows)      # all rows, 4 denoising calls per chunk
+    res["rollout480"] = {"s_extrapolated": round(dt * scale, 2),
+                         "tflops": round(fl / dt / 1e12, 6),
+                         "sample": f"{len(rows)} of {w.lq} rows, one call per chunk "
+                                   f"({dt:.1f} s), scaled x{scale:.1f}"}
+    del k, v
+
+    w = WIN720
+    rows = sample_rows(w.lq, w.grid_h * w.grid_w)
+    q = rng.standard_normal((w.B, w.lq, w.H, w.D))
+    k, v = kv(w, w.cap)
+    t = time.perf_counter()
+    oracle.attn(q, k, v, w.kv_len, w.q_pos0, w.chunk_tokens, rows=rows, threads=threads)
+    dt = time.perf_counter() - t
+    fl = attn_flops(w.B, w.H, len(rows), w.kv_len, w.D)
+    res["win720"] = {"s_extrapolated": round(dt * w.lq / len(rows), 2),
+                     "tflops": round(fl / dt / 1e12, 6),
+                     "sample": f"{len(rows)} of {w.lq} rows ({dt:.1f} s), scaled "
+                               f"x{w.lq / len(rows):.1f}"}
+    res["threads"] = threads
+    return res
+
+
 def cpu_baseline(w, stride=1):
     """The oracle on the host cores: attention of every `stride`-th query row
     of the 480P chunk (all 12 heads, all 32760 keys), fp64.  The default is
@@ -483,7 +743,7 @@ def cpu_baseline(w, stride=1):
     oracle.rope(x, w.t0, w.tok_off, w.grid_h, w.grid_w)
     dt_rope = time.perf_counter() - t
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": (f"attention of {len(rows)} of {w.lq} query rows (stride {stride}) x "
                        f"{w.H} heads vs {w.kv_len} keys, head_dim {w.D}, fp64, "
                        f"{dt:.1f} s on {threads} threads; RoPE of the chunk's Q and K "
@@ -512,7 +772,12 @@ def main():
     # the attention launches keep speeding up over the first ~30 ms of work
     # (clock ramp); 40 warmup steps (~40 ms) reach the steady state
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--sets", type=int, default=4, help="buffer sets used round-robin")
+    ap.add_argument("--sets", type=int, default=8,
+                    help="buffer sets used round-robin (8 x 273 MB: between two uses of a set "
+                         "the others move ~600 MB, more than the 256 MB Infinity Cache)")
+    ap.add_argument("--ramp-steps", type=int, default=64,
+                    help="untimed steps before the warm-up ones: the chip's clock ramps over "
+                         "its first ~30 ms of matrix work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -553,6 +818,9 @@ def main():
     ws = torch.empty(wsb // 4 + 4, dtype=torch.float32, device=dev) if wsb else None
     torch.cuda.synchronize()
 
+    for i in range(args.ramp_steps):
+        run_step(crattn, w, sets[i % len(sets)], table, ext, ws)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
         run_step(crattn, w, sets[i % len(sets)], table, ext, ws)
     torch.cuda.synchronize()
@@ -623,16 +891,22 @@ def main():
         extras["svg2_480"] = svg2_extras(crattn, w, dev, attn_ms, fl)
         plain_ms, fused_ms = fused_step_ms(crattn, w, sets, table, ext, ws)
         extras["step_plain_vs_fused_qrot_ms"] = [round(plain_ms, 4), round(fused_ms, 4)]
-        extras["rollout480_ms_total"] = round(rollout_ms(crattn, dev), 3)
+        extras["rollout480"] = rollout_breakdown(crattn, dev)
+        extras["rollout480_ms_total"] = extras["rollout480"]["wall_ms"]
         extras["rollout480_ms_per_chunk"] = round(extras["rollout480_ms_total"] / 7, 3)
         extras["rollout480_hsa_ms_total"] = round(rollout_ms(crattn, dev, hsa=(6, 32)), 3)
+        extras["sp480_rope_append"] = rope_append_rate(crattn, SP480, dev, sets=8, burst=40)
+        extras["sp480_rope_append"]["note"] = ("10.8 MB per launch: launch-bound, and its 8 "
+                                               "sets fit the Infinity Cache; reported, not judged")
         torch.cuda.empty_cache()
         del sets
         torch.cuda.empty_cache()
+        extras["win720_rope_append"] = rope_append_rate(crattn, WIN720, dev, sets=1)
         extras["win720_attn_ms"] = round(time_attn_only(crattn, WIN720, dev, reps=3), 3)
         extras["win720_attn_tflops"] = round(
             attn_flops(1, WIN720.H, WIN720.lq, WIN720.kv_len, WIN720.D)
             / (extras["win720_attn_ms"] * 1e-3) / 1e12, 1)
+        extras["win720_hsa"] = hsa_win720(crattn, dev, extras["win720_attn_ms"])
 
     rec = {
         "metric": METRIC,
@@ -649,7 +923,8 @@ def main():
         "data": "synthetic N(0,1) bf16, seeded; inputs resident in HBM",
         "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
                    "chunk": f"{w.frames}x{w.grid_h}x{w.grid_w}", "queries": w.lq,
-                   "keys": w.kv_len, "t0": w.t0, "buffer_sets": args.sets},
+                   "keys": w.kv_len, "t0": w.t0, "buffer_sets": args.sets,
+                   "clock_ramp_steps": args.ramp_steps},
         "ms_per_chunk": round(ms_per_step, 4),
         "attn_ms": round(attn_ms, 4),
         "attn_ms_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
@@ -680,6 +955,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
+        if not args.no_extras:
+            rec["cpu_baseline"]["other_workloads"] = oracle_extras()
     print(json.dumps(rec), flush=True)
 
 
