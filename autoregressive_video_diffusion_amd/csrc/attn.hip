@@ -84,6 +84,11 @@ struct AttnKArgs {
   int64_t list_cap;
   int cq;
   unsigned long long *work;  // next work item (set to the grid size before launch)
+  // balanced split of the dense head_dim-128 kernel: the workgroups' equal
+  // ranges of all key steps; ws_o / ws_lse hold two partial slots each
+  int stream;
+  int64_t steps_bh, total_steps;
+  unsigned *counters;  // per workgroup: parts of the tile it ends in that are done
   const int32_t *order;      // (b, h, slot) of the non-empty slots, costliest first
   const int32_t *n_real;     // their number
 };
@@ -923,9 +928,78 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 #define CRT_D(p, t) \
   p #t "0", p #t "1", p #t "2", p #t "3", p #t "4", p #t "5", p #t "6", p #t "7", p #t "8", p #t "9"
 
+// One query tile of the dense kernel: its rows and key range, and (balanced
+// split) where its key steps sit in the (batch, head, tile, key tile) order.
+struct FwdTile {
+  int b, h;
+  int64_t row0, nrows;  // query rows [row0, row0 + nrows) of (b, h)
+  int limit, nkt;       // visible keys and 64-key tiles
+  int64_t pos0;         // linear index of the tile's first key step
+};
+
+// Query rows of segment s (chunk q_pos0 / L + s) start at seg_row0 and
+// number seg_rows; its tiles see min(kv_len, (chunk + 1) L) keys.
+__device__ inline int64_t fwd_seg_tiles(const AttnKArgs &a, int64_t s) {
+  return s == 0 ? a.tiles0
+       : s <= a.n_full ? a.tiles_full
+                       : a.n_tiles - a.tiles0 - a.n_full * a.tiles_full;
+}
+__device__ inline int fwd_seg_nkt(const AttnKArgs &a, int64_t s) {
+  const int64_t limit = min(a.kv_len, (a.q_pos0 / a.L + s + 1) * a.L);
+  return (int)((limit + 63) / 64);
+}
+
+__device__ inline FwdTile fwd_tile_in(const AttnKArgs &a, int64_t bh, int64_t s, int64_t t_in) {
+  FwdTile t;
+  t.b = (int)(bh / a.H);
+  t.h = (int)(bh % a.H);
+  const int64_t seg_row0 = s == 0 ? 0 : a.seg0_rows + (s - 1) * a.L;
+  const int64_t seg_rows = s == 0 ? a.seg0_rows : s <= a.n_full ? a.L : a.last_rows;
+  t.row0 = seg_row0 + t_in * 256;
+  t.nrows = min((int64_t)256, seg_rows - t_in * 256);
+  t.limit = (int)min(a.kv_len, (a.q_pos0 / a.L + s + 1) * a.L);
+  t.nkt = (t.limit + 63) / 64;
+  t.pos0 = 0;
+  return t;
+}
+
+// Tile g (of B * H * n_tiles): the unsplit launch, one tile per workgroup.
+__device__ inline FwdTile fwd_tile(const AttnKArgs &a, int64_t g) {
+  const int64_t bh = g / a.n_tiles, tile = g % a.n_tiles;
+  int64_t s, t_in;
+  if (tile < a.tiles0) {
+    s = 0;
+    t_in = tile;
+  } else {
+    const int64_t u = tile - a.tiles0;
+    s = 1 + min(u / a.tiles_full, a.n_full);
+    t_in = u - (s - 1) * a.tiles_full;
+  }
+  return fwd_tile_in(a, bh, s, t_in);
+}
+
+// The tile holding linear key step x (balanced split).
+__device__ inline FwdTile fwd_locate(const AttnKArgs &a, int64_t x) {
+  const int64_t bh = x / a.steps_bh;
+  int64_t r = x - bh * a.steps_bh, base = bh * a.steps_bh;
+  const int64_t n_seg = 1 + a.n_full + (a.last_rows > 0 ? 1 : 0);
+  int64_t s = 0;
+  for (;; ++s) {
+    const int64_t cnt = fwd_seg_tiles(a, s) * fwd_seg_nkt(a, s);
+    if (r < cnt || s == n_seg - 1) break;
+    r -= cnt;
+    base += cnt;
+  }
+  const int nkt = fwd_seg_nkt(a, s);
+  const int64_t t_in = r / nkt;
+  FwdTile t = fwd_tile_in(a, bh, s, t_in);
+  t.pos0 = base + t_in * nkt;
+  return t;
+}
+
 template <bool ROPE>
 __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
-  constexpr int D = 128, kBN = 64, BM = 256;
+  constexpr int D = 128, kBN = 64;
   constexpr int DK = D / 16, DB = D / 32;
   constexpr int KP = Pitch<D>::K, VP = Pitch<D>::V;
   constexpr int K_CELLS = kBN * KP, V_CELLS = kBN * VP;
@@ -933,6 +1007,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
   constexpr int STAGE_BYTES = STAGE_CELLS * 16;
   static_assert(STAGE_BYTES == 37888 && K_CELLS * 16 == 17408, "layout the loop assumes");
   __shared__ uint4 lds_ring[4 * STAGE_CELLS];
+  __shared__ int sh_count;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -940,137 +1015,22 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
   const int hf = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- work item: (b, h, query tile, key split), XCD-grouped ----
-  int64_t item;
+  // ---- work: consecutive work indices on one XCD (they share K/V in its L2)
+  int64_t w;
   {
     const int64_t G = gridDim.x;
     const int64_t xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
     const int64_t q = G / kXcds, r = G % kXcds;
-    item = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    w = xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
   }
-  const int split = (int)(item % a.splits);
-  int64_t bid = item / a.splits;
-  const int64_t tile = bid % a.n_tiles;
-  bid /= a.n_tiles;
-  const int h = (int)(bid % a.H);
-  const int b = (int)(bid / a.H);
-  int64_t seg, t_in, seg_row0, seg_rows;
-  if (tile < a.tiles0) {
-    seg = 0;
-    t_in = tile;
-    seg_row0 = 0;
-    seg_rows = a.seg0_rows;
-  } else {
-    const int64_t u = tile - a.tiles0;
-    if (u < a.n_full * a.tiles_full) {
-      const int64_t s = u / a.tiles_full;
-      t_in = u - s * a.tiles_full;
-      seg = 1 + s;
-      seg_row0 = a.seg0_rows + s * a.L;
-      seg_rows = a.L;
-    } else {
-      t_in = u - a.n_full * a.tiles_full;
-      seg = 1 + a.n_full;
-      seg_row0 = a.seg0_rows + a.n_full * a.L;
-      seg_rows = a.last_rows;
-    }
-  }
-  const int64_t row0 = seg_row0 + t_in * BM;
-  const int64_t nrows = min((int64_t)BM, seg_rows - t_in * BM);
-  const int64_t q_chunk = a.q_pos0 / a.L + seg;
-  const int limit = (int)min(a.kv_len, (q_chunk + 1) * a.L);
-  const int nkt = (limit + kBN - 1) / kBN;
-  const int kt_begin = __builtin_amdgcn_readfirstlane(split * nkt / a.splits);
-  const int kt_end = __builtin_amdgcn_readfirstlane((split + 1) * nkt / a.splits);
-  const int last = kt_end - 1;
-  const int rem = __builtin_amdgcn_readfirstlane(min(kBN, limit - last * kBN));
+  // Balanced split: key steps [s_lo, s_hi) of the linear order.  Its tiles
+  // are taken last to first: the last one starts at key tile 0, as do the
+  // other workgroups' first tiles, so the workgroups of one head walk the
+  // keys nearly in step.
+  const int64_t G = gridDim.x, T = a.total_steps;
+  const int64_t s_lo = a.stream ? w * T / G : 0, s_hi = a.stream ? (w + 1) * T / G : 0;
+  auto part_of = [&](int64_t x) { return ((x + 1) * G - 1) / T; };  // workgroup holding step x
 
-  // ---- this wavefront's 64 queries as B operands (Q in registers) ----
-  const int64_t wrow0 = row0 + (int64_t)wave * 64;
-  bf16x8_t qf[2][DK];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int64_t row = wrow0 + qb * 32 + l32;
-    const bool ok = row < row0 + nrows;
-    const uint16_t *qp = a.q + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (ok) x = *reinterpret_cast<const uint4 *>(qp + ks * 16);
-      qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
-    }
-    if constexpr (ROPE) {
-      constexpr int HT = (D - 4 * (D / 6)) / 2;
-      constexpr int HH = D / 6;
-      const Pos p = decode_pos(a.tok_off + (uint32_t)min(row, a.Lq - 1), a.per_frame, a.gw, a.t0);
-      const float2 *ax[3] = {a.table + p.t * HT + 4 * hf,
-                             a.table + a.tg.base_h + p.h * HH - HT + 4 * hf,
-                             a.table + a.tg.base_w + p.w * HH - HT - HH + 4 * hf};
-      auto axis = [](int q) { return q < HT ? 0 : q < HT + HH ? 1 : 2; };
-      float2 cs[DK][4];
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q0 = ks * 8 + e;
-          const int a0 = axis(q0), a1 = axis(q0 + 4);
-          const float2 *ptr = a0 == a1 ? ax[a0] : (hf ? ax[a1] : ax[a0]);
-          cs[ks][e] = ptr[q0];
-        }
-#pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
-        uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float2 r = rotate_pair(__uint_as_float(wv[e] << 16),
-                                       __uint_as_float(wv[e] & 0xffff0000u), cs[ks][e]);
-          wv[e] = pack_bf16(r.x, r.y);
-        }
-        qf[qb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
-      }
-    }
-  }
-  f32x32_t qa[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks) {
-      const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
-      qa[qb][4 * ks + 0] = __uint_as_float(x.x);
-      qa[qb][4 * ks + 1] = __uint_as_float(x.y);
-      qa[qb][4 * ks + 2] = __uint_as_float(x.z);
-      qa[qb][4 * ks + 3] = __uint_as_float(x.w);
-    }
-
-  // ---- the lane's copy offsets: slot n of the tile (K: instructions
-  // wave + 4n, and for n = 4 instruction 16 on wave 0, a repeat of slot 3
-  // elsewhere; V: wave + 4n), full rows and rows clamped to the last valid
-  // key of the final tile ----
-  u32x8_t dma_a, dmal_a;
-  u32x2_t dma_b, dmal_b;
-  {
-    uint32_t off[10], offl[10];
-#pragma unroll
-    for (int n = 0; n < 10; ++n) {
-      const bool kside = n < 5;
-      const int j = kside ? (n < 4 ? wave + 4 * n : (wave == 0 ? 16 : wave + 12)) : wave + 4 * (n - 5);
-      const int pitch = kside ? KP : VP;
-      const int cell = j * 64 + lane;
-      const int row = cell / pitch, c = cell - row * pitch;
-      const uint32_t col = (uint32_t)(c < D / 8 ? c * 16 : 0);
-      off[n] = (uint32_t)row * (D * 2) + col;
-      offl[n] = (uint32_t)min(row, rem - 1) * (D * 2) + col;
-    }
-    for (int n = 0; n < 8; ++n) {
-      dma_a[n] = off[n];
-      dmal_a[n] = offl[n];
-    }
-    dma_b[0] = off[8];
-    dma_b[1] = off[9];
-    dmal_b[0] = offl[8];
-    dmal_b[1] = offl[9];
-  }
   // ---- LDS addresses: ring base, per-lane fragment bases per stage ----
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t ring = __builtin_amdgcn_readfirstlane(
@@ -1089,82 +1049,299 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     }
   }
   const uint32_t kh8 = 8u * (uint32_t)hf;
-  const int64_t head_off = ((int64_t)b * a.H + h) * a.cap * D;
-  const uint16_t *kh = a.k + head_off;
-  const uint16_t *vh = a.v + head_off;
   const uint32_t wb = ring + (uint32_t)wave * 1024u;
   const uint32_t k5 = (uint32_t)((wave == 0 ? 16 : wave + 12) - wave) * 1024u;
   const float sc = a.scale_log2;
   const float inv_sc = a.inv_scale_log2;
 
-  f32x32_t o[4];
+  int64_t x_end = s_hi;
+  for (bool first = true;; first = false) {
+    FwdTile ti;
+    int k0, k1;
+    if (!a.stream) {
+      if (!first) break;
+      ti = fwd_tile(a, w);
+      k0 = 0;
+      k1 = ti.nkt;
+    } else {
+      if (x_end <= s_lo) break;
+      ti = fwd_locate(a, x_end - 1);
+      k0 = (int)(max(s_lo, ti.pos0) - ti.pos0);
+      k1 = (int)(x_end - ti.pos0);
+      x_end = ti.pos0 + k0;
+    }
+    k0 = __builtin_amdgcn_readfirstlane(k0);
+    k1 = __builtin_amdgcn_readfirstlane(k1);
+    // every wavefront is done with the previous tile's LDS before this
+    // tile's copies start
+    if (!first) __syncthreads();
+    const int b = ti.b, h = ti.h;
+    const int64_t row0 = ti.row0, nrows = ti.nrows;
+    const int last = k1 - 1;
+    const int rem = __builtin_amdgcn_readfirstlane(min(kBN, ti.limit - last * kBN));
+
+    // ---- this wavefront's 64 queries as B operands (Q in registers) ----
+    const int64_t wrow0 = row0 + (int64_t)wave * 64;
+    bf16x8_t qf[2][DK];
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+    for (int qb = 0; qb < 2; ++qb) {
+      const int64_t row = wrow0 + qb * 32 + l32;
+      const bool ok = row < row0 + nrows;
+      const uint16_t *qp = a.q + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 8;
 #pragma unroll
-    for (int r = 0; r < 32; ++r) o[g][r] = 0.f;
-  f32x2_t m2 = {-INFINITY, -INFINITY};
-  f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
-  int t = kt_begin;
-  if (kt_begin < kt_end) {
+      for (int ks = 0; ks < DK; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (ok) x = *reinterpret_cast<const uint4 *>(qp + ks * 16);
+        qf[qb][ks] = __builtin_bit_cast(bf16x8_t, x);
+      }
+      if constexpr (ROPE) {
+        constexpr int HT = (D - 4 * (D / 6)) / 2;
+        constexpr int HH = D / 6;
+        const Pos p =
+            decode_pos(a.tok_off + (uint32_t)min(row, a.Lq - 1), a.per_frame, a.gw, a.t0);
+        const float2 *ax[3] = {a.table + p.t * HT + 4 * hf,
+                               a.table + a.tg.base_h + p.h * HH - HT + 4 * hf,
+                               a.table + a.tg.base_w + p.w * HH - HT - HH + 4 * hf};
+        auto axis = [](int q) { return q < HT ? 0 : q < HT + HH ? 1 : 2; };
+        float2 cs[DK][4];
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int q0 = ks * 8 + e;
+            const int a0 = axis(q0), a1 = axis(q0 + 4);
+            const float2 *ptr = a0 == a1 ? ax[a0] : (hf ? ax[a1] : ax[a0]);
+            cs[ks][e] = ptr[q0];
+          }
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
+          uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float2 r = rotate_pair(__uint_as_float(wv[e] << 16),
+                                         __uint_as_float(wv[e] & 0xffff0000u), cs[ks][e]);
+            wv[e] = pack_bf16(r.x, r.y);
+          }
+          qf[qb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(wv[0], wv[1], wv[2], wv[3]));
+        }
+      }
+    }
+    f32x32_t qa[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const uint4 x = __builtin_bit_cast(uint4, qf[qb][ks]);
+        qa[qb][4 * ks + 0] = __uint_as_float(x.x);
+        qa[qb][4 * ks + 1] = __uint_as_float(x.y);
+        qa[qb][4 * ks + 2] = __uint_as_float(x.z);
+        qa[qb][4 * ks + 3] = __uint_as_float(x.w);
+      }
+
+    // ---- the lane's copy offsets: slot n of the tile (K: instructions
+    // wave + 4n, and for n = 4 instruction 16 on wave 0, a repeat of slot 3
+    // elsewhere; V: wave + 4n), full rows and rows clamped to the last valid
+    // key of the final tile ----
+    u32x8_t dma_a, dmal_a;
+    u32x2_t dma_b, dmal_b;
+    {
+      uint32_t off[10], offl[10];
+#pragma unroll
+      for (int n = 0; n < 10; ++n) {
+        const bool kside = n < 5;
+        const int j =
+            kside ? (n < 4 ? wave + 4 * n : (wave == 0 ? 16 : wave + 12)) : wave + 4 * (n - 5);
+        const int pitch = kside ? KP : VP;
+        const int cell = j * 64 + lane;
+        const int row = cell / pitch, c = cell - row * pitch;
+        const uint32_t col = (uint32_t)(c < D / 8 ? c * 16 : 0);
+        off[n] = (uint32_t)row * (D * 2) + col;
+        offl[n] = (uint32_t)min(row, rem - 1) * (D * 2) + col;
+      }
+      for (int n = 0; n < 8; ++n) {
+        dma_a[n] = off[n];
+        dmal_a[n] = offl[n];
+      }
+      dma_b[0] = off[8];
+      dma_b[1] = off[9];
+      dmal_b[0] = offl[8];
+      dmal_b[1] = offl[9];
+    }
+    const int64_t head_off = ((int64_t)b * a.H + h) * a.cap * D;
+    const uint16_t *kh = a.k + head_off;
+    const uint16_t *vh = a.v + head_off;
+
+    f32x32_t o[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int r = 0; r < 32; ++r) o[g][r] = 0.f;
+    f32x2_t m2 = {-INFINITY, -INFINITY};
+    f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
+    int t = k0;
+    if (k0 < k1) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile(CRATTN_ATTN_LOOP_ASM
-                 : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
-                   "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
-                   "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t)
-                 : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
-                   "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
-                   "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
-                   "{s71}"(sc), "{s72}"(wb), "{s73}"(k5), "{s88}"(inv_sc)
-                 : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
-                   CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5), CRT_D("v", 6),
-                   CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9), CRT_D("v", 10), CRT_D("v", 11),
-                   CRT_D("v", 12), CRT_D("v", 13), CRT_D("v", 14), CRT_D("v", 15),
-                   CRT_D("v", 16), CRT_D("v", 17), CRT_D("v", 18), "v190", "v191", "v198",
-                   "v199", "v200", "v201", "v202", "v203", "v204", "v205", "v206", "v236", "v237",
-                   "s74", "s75",
-                   "s76", "s77", "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86",
-                   "s87", "m0", "vcc", "scc", "memory");
+      asm volatile(CRATTN_ATTN_LOOP_ASM
+                   : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
+                     "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
+                     "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t)
+                   : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
+                     "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
+                     "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
+                     "{s71}"(sc), "{s72}"(wb), "{s73}"(k5), "{s88}"(inv_sc)
+                   : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
+                     CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5),
+                     CRT_D("v", 6), CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9),
+                     CRT_D("v", 10), CRT_D("v", 11), CRT_D("v", 12), CRT_D("v", 13),
+                     CRT_D("v", 14), CRT_D("v", 15), CRT_D("v", 16), CRT_D("v", 17),
+                     CRT_D("v", 18), "v190", "v191", "v198", "v199", "v200", "v201", "v202",
+                     "v203", "v204", "v205", "v206", "v236", "v237", "s74", "s75", "s76", "s77",
+                     "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "m0",
+                     "vcc", "scc", "memory");
 #pragma clang diagnostic pop
-  }
+    }
 
-  // ---- epilogue: normalise and store (rows of this wave's two blocks) ----
+    // ---- this tile's rows: base-2 log-sum-exp and the normalised O ----
+    float lse2[2], inv[2];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float lt = half_swap_sum(l4[2 * qb] + l4[2 * qb + 1]);
-    const float m_run = m2[qb];
-    const int64_t row = wrow0 + qb * 32 + l32;
-    if (row >= row0 + nrows) continue;
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const float lse2 = lt > 0.f ? m_run + __log2f(lt) : -INFINITY;
-    if (a.splits == 1) {
+    for (int qb = 0; qb < 2; ++qb) {
+      const float lt = half_swap_sum(l4[2 * qb] + l4[2 * qb + 1]);
+      inv[qb] = lt > 0.f ? 1.0f / lt : 0.f;
+      lse2[qb] = lt > 0.f ? m2[qb] + __log2f(lt) : -INFINITY;
+    }
+    const int trow0 = wave * 64 + l32;  // tile row of (qb = 0); qb adds 32
+
+    bool merge = false;
+    int64_t part0 = 0, part1 = 0, a0 = 0;
+    if (k0 != 0 || k1 != ti.nkt) {
+      // A part of a tile cut between workgroups (balanced split only): the
+      // parts are those of workgroups part0 .. part1; a part writes its
+      // normalised O and log-sum-exp to its slot (slot 0 of a workgroup for
+      // the tile its range starts in, slot 1 for the tile it ends in) and
+      // counts itself done; the part that finds all others done merges them.
+      a0 = ti.pos0;
+      part0 = part_of(a0);
+      part1 = part_of(a0 + ti.nkt - 1);
+      const int n_parts = (int)(part1 - part0 + 1);
+      // Only wavefront 0 fences at device scope: the workgroup barriers order
+      // the other wavefronts' slot stores before its release and its acquire
+      // before their slot loads.  Slot writers release (L2 write-back) once;
+      // only the merging part acquires (L2 invalidate).
+      unsigned *cnt = a.counters + part0;
+      if (tid == 0)
+        sh_count = (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      merge = sh_count == n_parts - 1;
+      __syncthreads();
+      if (!merge) {
+        const int64_t slot = 2 * w + (s_lo >= a0 ? 0 : 1);
+        float *so = a.ws_o + slot * (256 * D);
+        float *sl = a.ws_lse + slot * 256;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const int r = trow0 + qb * 32;
+          if (r >= nrows) continue;
+          float *op = so + (int64_t)r * D + hf * 4;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int base = qb * 16 + i4 * 4;
+              *reinterpret_cast<float4 *>(op + db * 32 + i4 * 8) =
+                  make_float4(o[db][base + 0] * inv[qb], o[db][base + 1] * inv[qb],
+                              o[db][base + 2] * inv[qb], o[db][base + 3] * inv[qb]);
+            }
+          if (hf == 0) sl[r] = lse2[qb];
+        }
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          sh_count = (int)__hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        merge = sh_count == n_parts - 1;
+      }
+      if (!merge) continue;
+      if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+    }
+
+    // ---- final rows: this part alone, or merged with the tile's other
+    // parts (O = sum_p 2^(lse_p - lse) O_p, lse = log2 sum_p 2^lse_p).  The
+    // merge takes the parts in workgroup order with this part's normalised
+    // O rounded as its slot would hold it, so the result does not depend on
+    // which part finished last. ----
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r = trow0 + qb * 32;
+      if (r >= nrows) continue;
+      float scl = inv[qb], lse_f = lse2[qb];
+      if (merge) {
+        float mx = -INFINITY;
+        for (int64_t v = part0; v <= part1; ++v) {
+          const int64_t slot = 2 * v + (v * T / G >= a0 ? 0 : 1);
+          mx = fmaxf(mx, v == w ? lse2[qb] : a.ws_lse[slot * 256 + r]);
+        }
+        float acc[DB][16];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+        float wsum = 0.f;
+        for (int64_t v = part0; v <= part1; ++v) {
+          const int64_t slot = 2 * v + (v * T / G >= a0 ? 0 : 1);
+          const float lv = v == w ? lse2[qb] : a.ws_lse[slot * 256 + r];
+          const float wv = lv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lv - mx);
+          wsum += wv;
+          const float *op = a.ws_o + slot * (256 * D) + (int64_t)r * D + hf * 4;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+              const int base = qb * 16 + i4 * 4;
+              float4 x;
+              if (v == w)
+                x = make_float4(o[db][base + 0] * inv[qb], o[db][base + 1] * inv[qb],
+                                o[db][base + 2] * inv[qb], o[db][base + 3] * inv[qb]);
+              else
+                x = *reinterpret_cast<const float4 *>(op + db * 32 + i4 * 8);
+              acc[db][i4 * 4 + 0] = fmaf(wv, x.x, acc[db][i4 * 4 + 0]);
+              acc[db][i4 * 4 + 1] = fmaf(wv, x.y, acc[db][i4 * 4 + 1]);
+              acc[db][i4 * 4 + 2] = fmaf(wv, x.z, acc[db][i4 * 4 + 2]);
+              acc[db][i4 * 4 + 3] = fmaf(wv, x.w, acc[db][i4 * 4 + 3]);
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][qb * 16 + i] = acc[db][i];
+        scl = wsum > 0.f ? 1.0f / wsum : 0.f;
+        lse_f = wsum > 0.f ? mx + __log2f(wsum) : -INFINITY;
+      }
+      const int64_t row = row0 + r;
       uint16_t *op = a.out + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int base = qb * 16 + i4 * 4;
-          uint2 w;
-          w.x = pack_bf16(o[db][base + 0] * inv, o[db][base + 1] * inv);
-          w.y = pack_bf16(o[db][base + 2] * inv, o[db][base + 3] * inv);
-          *reinterpret_cast<uint2 *>(op + db * 32 + i4 * 8) = w;
+          uint2 u;
+          u.x = pack_bf16(o[db][base + 0] * scl, o[db][base + 1] * scl);
+          u.y = pack_bf16(o[db][base + 2] * scl, o[db][base + 3] * scl);
+          *reinterpret_cast<uint2 *>(op + db * 32 + i4 * 8) = u;
         }
-      if (hf == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Lq + row] = lse2 * kLn2;
-    } else {
-      const int64_t prow = (((int64_t)split * a.B + b) * a.H + h) * a.Lq + row;
-      float *op = a.ws_o + prow * D + hf * 4;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int base = qb * 16 + i4 * 4;
-          *reinterpret_cast<float4 *>(op + db * 32 + i4 * 8) =
-              make_float4(o[db][base + 0] * inv, o[db][base + 1] * inv, o[db][base + 2] * inv,
-                          o[db][base + 3] * inv);
-        }
-      if (hf == 0) a.ws_lse[prow] = lse2;
+      if (hf == 0 && a.lse != nullptr) a.lse[((int64_t)b * a.H + h) * a.Lq + row] = lse_f * kLn2;
     }
   }
+}
+
+// Clear the balanced split's completion counters before a launch.
+__global__ void attn_clear_counters_kernel(unsigned *c, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) c[i] = 0u;
 }
 #undef CRT_D
 
@@ -1362,6 +1539,9 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
   k.work = nullptr;
   k.order = nullptr;
   k.n_real = nullptr;
+  k.stream = 0;
+  k.steps_bh = k.total_steps = 0;
+  k.counters = nullptr;
   hipError_t e;
   if (a.gslots != nullptr) {
     // persistent: the workspace holds the work counter and the number of
@@ -1387,6 +1567,19 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
       e = launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s);
     } else {
       // dense: the kernel with the hand-scheduled key loop
+      if (p.stream) {
+        // workspace: counters, then the partial slots' O, then their lse
+        char *ws = static_cast<char *>(a.workspace);
+        const size_t n_slots = 2u * (size_t)p.grid;
+        k.stream = 1;
+        k.steps_bh = p.steps_bh;
+        k.total_steps = p.total_steps;
+        k.counters = reinterpret_cast<unsigned *>(ws);
+        k.ws_o = reinterpret_cast<float *>(ws + kStreamCounterBytes);
+        k.ws_lse = k.ws_o + n_slots * (size_t)kStreamRows * 128u;
+        hipLaunchKernelGGL(attn_clear_counters_kernel, dim3(1), dim3(256), 0, s, k.counters,
+                           (int)p.grid);
+      }
       if (a.rope)
         hipLaunchKernelGGL(attn_fwd64_kernel<true>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
       else

@@ -176,7 +176,21 @@ struct AttnPlan {
   int64_t tiles_full; // tiles of every full middle segment
   int64_t n_full;     // number of full middle segments
   int64_t last_rows;  // rows of the trailing partial segment (0 if none)
+  // balanced split (dense head_dim-128 kernel with a workspace): the key
+  // steps of all query tiles, in (batch, head, tile, key tile) order, cut
+  // into `grid` equal ranges, one per workgroup; a tile cut between ranges
+  // is merged by the last of its parts to finish
+  bool stream;
+  int64_t steps_bh;     // key steps of one (batch, head): sum over tiles
+  int64_t total_steps;  // B * H * steps_bh
 };
+
+// Workspace of the balanced split: per-range completion counters, then two
+// partial slots per workgroup (normalised O, fp32, then base-2 log-sum-exp)
+// of one 256-row query tile each.
+constexpr int kStreamRows = 256;
+constexpr size_t kStreamCounterBytes = 1024;  // 256 counters
+inline size_t stream_slot_floats(int D) { return (size_t)kStreamRows * (size_t)(D + 1); }
 
 AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
                    int64_t chunk_tokens, int D, bool allow_split);
@@ -189,7 +203,7 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s);
 // (chunk_causal_attn_noalloc): kAttnScratchBytes on every device the library
 // runs on, held until the process ends.  attn_scratch returns its address on
 // the current device (looked up once per device), or null with *err set.
-constexpr size_t kAttnScratchBytes = size_t(32) << 20;
+constexpr size_t kAttnScratchBytes = size_t(72) << 20;
 void *attn_scratch(hipError_t *err);
 hipError_t launch_qkv_rope(const QkvArgs &a, hipStream_t s);
 hipError_t launch_hsa_pool(const HsaPoolArgs &a, int D, hipStream_t s);

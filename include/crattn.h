@@ -255,7 +255,7 @@ int chunk_causal_attn(const void *q, const void *k_cache, const void *v_cache,
  * than CRATTN_NOALLOC_SCRATCH_BYTES of partials
  * (chunk_causal_attn_workspace_bytes of the same shape tells how much).
  */
-#define CRATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define CRATTN_NOALLOC_SCRATCH_BYTES (72u << 20)
 int chunk_causal_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
                               int64_t cap, int64_t kv_len, int64_t q_pos0, int64_t chunk_tokens,
                               void *out, float *lse, int B, int H, int D, int64_t Lq, float scale,

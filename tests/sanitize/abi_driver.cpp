@@ -59,7 +59,7 @@ int main() {
          CRATTN_EINVAL);
   EXPECT(rope_apply_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 0, T, 4, 8, 8, 1, 2, 64,
                            INT64_MAX, 3, INT64_MAX, 8, 8, CRATTN_BF16, nullptr) == CRATTN_EINVAL);
-  EXPECT(chunk_causal_attn_noalloc(FAKE, FAKE, FAKE, 65536, 65536, 61440, 4096, FAKE, nullptr, 1,
+  EXPECT(chunk_causal_attn_noalloc(FAKE, FAKE, FAKE, 65536, 65535, 61440, 4096, FAKE, nullptr, 1,
                                    4, 128, 4096, 0.f, nullptr) == CRATTN_EINVAL);
   EXPECT(hsa_select(FAKE, FAKE, 32760, 32761, 1560, 3 * 4680, 4680, 6, 32,
                     static_cast<int32_t *>(FAKE), 1, 12, 128, 4680, nullptr) == CRATTN_EINVAL);

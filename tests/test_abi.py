@@ -42,11 +42,22 @@ def test_rope_table_bytes():
 
 
 def test_workspace_bytes():
-    # 480P chunk: enough query tiles to fill the chip, no split
-    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32760, 28080, 4680, 128) == 0
-    # one sequence-parallel rank's 585 queries: split-KV partials (O fp32 + lse)
-    ws = crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680, 128)
-    assert ws > 0 and ws % (12 * 585 * 129 * 4) == 0
+    # head_dim 128: balanced split over G <= 256 workgroups, 1 KB of counters
+    # then two partial slots of 256 rows x (128 + 1) fp32 per workgroup
+    slot = 256 * 129 * 4
+    # 480P chunk: 12 x 19 tiles x 512 key steps over 256 workgroups
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32760, 28080, 4680, 128) == \
+        1024 + 2 * 256 * slot
+    # one sequence-parallel rank's 585 queries: 12 x 3 tiles x 512 steps, 256 workgroups
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680,
+                                                    128) == 1024 + 2 * 256 * slot
+    # one head, 3 tiles: at least 512 / 8 = 64 steps per workgroup -> 24
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 1, 585, 32760, 28080 + 2925, 4680,
+                                                    128) == 1024 + 2 * 24 * slot
+    # head_dim 64: split-KV partials (O fp32 + lse) when the tiles leave the chip idle
+    ws = crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680, 64)
+    assert ws > 0 and ws % (12 * 585 * 65 * 4) == 0
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32760, 28080, 4680, 64) == 0
     # invalid shapes
     assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32759, 28080, 4680, 128) == 0
     assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 0, 32760, 0, 4680, 128) == 0
@@ -141,20 +152,24 @@ def _attn_noalloc(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), 1), (dict(v=MIS), 1), (dict(kv=255), 1), (dict(D=96), 2), (dict(Lq=0), 1),
     (dict(scale=-1.0), 1), (dict(cap=1 << 25), 1),
-    # 4 heads x 4096 queries against 65536 keys split 4 ways: 33.8 MB of
-    # partials, above the library's 32 MiB scratch
-    (dict(cap=65536, kv=65536, pos0=61440, L=4096, Lq=4096, H=4, D=128), 1),
 ])
 def test_chunk_causal_attn_noalloc_rejects(kw, code):
     assert _attn_noalloc(**kw) == code
     assert crattn.crattn_last_error() != ""
 
 
-def test_noalloc_scratch_covers_the_sp_rank_slice():
-    # the SP-rank slice's split partials fit the fixed scratch
-    need = crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680, 128)
-    assert 0 < need <= 32 << 20
-    assert crattn.chunk_causal_attn_workspace_bytes(1, 4, 4096, 65536, 61440, 4096, 128) > 32 << 20
+def test_noalloc_scratch_covers_every_shape():
+    # head_dim 128 needs at most 1 KB + 512 slots (the balanced split's
+    # bound, whatever the shape); head_dim 64 splits only small launches
+    cap = 72 << 20
+    for args in [(1, 12, 585, 32760, 28080 + 2925, 4680), (1, 12, 4680, 32760, 28080, 4680),
+                 (1, 4, 4096, 65536, 61440, 4096), (2, 40, 10800, 64800, 54000, 10800),
+                 (1, 1, 64, 64, 0, 64), (1, 2, 300, 100000, 99900, 100)]:
+        for D in (64, 128):
+            need = crattn.chunk_causal_attn_workspace_bytes(*args, D)
+            assert 0 <= need <= cap, (args, D, need)
+    assert crattn.chunk_causal_attn_workspace_bytes(2, 40, 10800, 64800, 54000, 10800, 128) == \
+        1024 + 2 * 256 * 256 * 129 * 4
 
 
 def _attn_rope(**kw):

@@ -189,6 +189,27 @@ def test_stress_distributions(kind):
     assert_attn_close(f64(out), o_ref, kind)
 
 
+def test_balanced_split_many_parts_all_rows():
+    # one head of the SP slice: 3 query tiles of 512 key steps cut over 24
+    # workgroups of 64 steps, so every tile has 8 or 9 parts merged by the
+    # last to finish; every row against the oracle, and five reruns agree
+    # bit for bit whichever part finishes last
+    w = SP480
+    q = rand_bf16((1, w.lq, 1, w.D), 61)
+    kc = rand_bf16((1, 1, w.cap, w.D), 62)
+    vc = rand_bf16((1, 1, w.cap, w.D), 63)
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 1, w.lq, w.kv_len, w.q_pos0,
+                                                    w.chunk_tokens, w.D) == \
+        1024 + 2 * 24 * 256 * 129 * 4
+    out, lse = run_attn(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens)
+    o_ref, lse_ref = oracle_rows(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens)
+    assert_attn_close(f64(out), o_ref, "many parts")
+    np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
+    for _ in range(5):
+        o2, l2 = run_attn(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens)
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
 def test_deterministic_rerun():
     w = SP480
     q = rand_bf16((1, w.lq, w.H, w.D), 51)
