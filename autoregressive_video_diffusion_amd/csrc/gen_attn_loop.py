@@ -255,12 +255,23 @@ MERGE_WAITS = False # fold an lgkmcnt wait into the one before it when possible
 ABLATE = ()         # timing probes only: work left out of the main steps
 
 
-def max_ops(buf, qb, tmp, chain_tmps=()):
-    """Row maximum of S(buf)[*][qb] over this lane's 32 keys, then over the
-    partner lane (l ^ 32), in raw score units: result in v[tmp] (v[tmp+1]
-    is clobbered).  With MAX_CHAINS = 4 the 32 values are reduced in four
-    independent chains (temporaries v[tmp], v[tmp+1] and chain_tmps) joined
-    at the end, so consecutive max3 do not wait on each other."""
+def cross_max(tmp):
+    """v[tmp] = max of v[tmp] over the lane and its partner (l ^ 32), the
+    other half of the same query column (v[tmp+1] is clobbered)."""
+    m, t2 = f"v{tmp}", f"v{tmp + 1}"
+    return [valu(f"v_mov_b32 {t2}, {m}", (t2,), (m,)),
+            valu(f"v_permlane32_swap_b32 {m}, {t2}", (m, t2), (m, t2), "perm"),
+            valu(f"v_max_f32 {m}, {m}, {t2}", (m,), (m, t2))]
+
+
+def max_ops(buf, qb, tmp, chain_tmps=(), cross=True):
+    """Row maximum of S(buf)[*][qb] over this lane's 32 keys, then (cross)
+    over the partner lane (l ^ 32), in raw score units: result in v[tmp]
+    (v[tmp+1] is clobbered).  With MAX_CHAINS = 4 the 32 values are reduced
+    in four independent chains (temporaries v[tmp], v[tmp+1] and chain_tmps)
+    joined at the end, so consecutive max3 do not wait on each other.  The
+    main steps take the lane's own maximum only: whether to rescale is
+    decided per lane, and the rescale block itself takes the row's."""
     vals = [S(buf, kb, qb) + r for kb in range(2) for r in range(16)]
     m = f"v{tmp}"
 
@@ -288,10 +299,8 @@ def max_ops(buf, qb, tmp, chain_tmps=()):
         out.append(valu(f"v_max3_f32 {m}, {dsts[0]}, {dsts[1]}, {dsts[2]}", (m,),
                         tuple(dsts[:3])))
         out.append(valu(f"v_max_f32 {m}, {m}, {dsts[3]}", (m,), (m, dsts[3])))
-    t2 = f"v{tmp + 1}"
-    out.append(valu(f"v_mov_b32 {t2}, {m}", (t2,), (m,)))
-    out.append(valu(f"v_permlane32_swap_b32 {m}, {t2}", (m, t2), (m, t2), "perm"))
-    out.append(valu(f"v_max_f32 {m}, {m}, {t2}", (m,), (m, t2)))
+    if cross:
+        out += cross_max(tmp)
     return out
 
 
@@ -303,14 +312,19 @@ def threshold(qb):
 
 
 def rescale_block(cur_buf, tag):
-    """Raise the running max where a lane's new maximum exceeds it by more
-    than 2^8 and rescale that row's sums and O (rare: early tiles).  The raw
-    maxima are in VT[0] (qb 0) and VT[2] (qb 1), the per-lane decisions in
-    sN0 / sN1.  S(cur_buf) is free here and serves as the buffer for O."""
+    """Raise the running max where a row's new maximum exceeds it by more
+    than 2^8 and rescale that row's sums and O (rare: early tiles).  The
+    lanes' raw maxima are in VT[0] (qb 0) and VT[2] (qb 1); the row maxima
+    and the per-lane decisions (sN0 / sN1) are taken here, so both halves of
+    a row decide alike.  S(cur_buf) is free here and serves as the buffer
+    for O."""
     out = [label(f"{tag}")]
     for qb in range(2):
         mc, need = VT[2 * qb], (sN0, sN1)[qb]
         mn, al = VT[4 + 2 * qb], VT[5 + 2 * qb]
+        out += cross_max(mc)
+        out.append(valu(f"v_cmp_gt_f32_e64 {sr(need, 2)}, {vr(mc)}, {vr(VTH[qb])}",
+                        (f"s{need}",), (f"v{mc}", f"v{VTH[qb]}")))
         out += [valu(f"v_mul_f32 {vr(mc)}, {sr(sC)}, {vr(mc)}", (f"v{mc}",), (f"v{mc}",)),
                 valu(f"v_cndmask_b32_e64 {vr(mn)}, {vr(VM[qb])}, {vr(mc)}, {sr(need, 2)}",
                      (f"v{mn}",), (f"v{VM[qb]}", f"v{mc}")),
@@ -494,8 +508,8 @@ def step(phi):
     items += exp_items(cur, 0, 54)
     items += v_read_items(vst, 32)
     # row maximum of S(t+1) (its last products are 28..31)
-    m0 = max_ops(nxt, 0, VT[0], (VT[4], VT[5]))
-    m1 = max_ops(nxt, 1, VT[2], (VT[6], VT[7]))
+    m0 = max_ops(nxt, 0, VT[0], (VT[4], VT[5]), cross=False)
+    m1 = max_ops(nxt, 1, VT[2], (VT[6], VT[7]), cross=False)
     mx = [i for pair in zip(m0, m1) for i in pair]   # the two blocks interleaved
     items += spread(mx, 34, 63)
     # before the last two products: tile t+2 has landed and every wave is
