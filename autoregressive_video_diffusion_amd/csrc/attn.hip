@@ -1035,34 +1035,35 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
   typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t ring = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(lds_ring));
+  // LDS: a ring of 4 K stages, then a ring of 4 V stages
   u32x8_t bases;
   {
     const uint32_t kb0 = ring + (uint32_t)((k_row_perm(l32) * KP + hf) * 16);
     const int vj = lane & 15;
     const int v_dim = (l32 >> 4) * 16 + 4 * (vj & 3);
     const uint32_t vb0 =
-        ring + K_CELLS * 16 + (uint32_t)((8 * hf + (vj >> 2)) * VP * 16 + v_dim * 2);
+        ring + 4 * K_CELLS * 16 + (uint32_t)((8 * hf + (vj >> 2)) * VP * 16 + v_dim * 2);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bases[s] = kb0 + s * STAGE_BYTES;
-      bases[4 + s] = vb0 + s * STAGE_BYTES;
+      bases[s] = kb0 + s * K_CELLS * 16;
+      bases[4 + s] = vb0 + s * V_CELLS * 16;
     }
   }
   const uint32_t kh8 = 8u * (uint32_t)hf;
   const uint32_t wb = ring + (uint32_t)wave * 1024u;
   const uint32_t k5 = (uint32_t)((wave == 0 ? 16 : wave + 12) - wave) * 1024u;
   const float sc = a.scale_log2;
-  const float inv_sc = a.inv_scale_log2;
 
   int64_t x_end = s_hi;
   for (bool first = true;; first = false) {
     FwdTile ti;
     int k0, k1;
     if (!a.stream) {
+      // one tile per workgroup, or one of its uniform key splits
       if (!first) break;
-      ti = fwd_tile(a, w);
-      k0 = 0;
-      k1 = ti.nkt;
+      ti = fwd_tile(a, w / a.splits);
+      k0 = (int)(w % a.splits) * ti.nkt / a.splits;
+      k1 = (int)(w % a.splits + 1) * ti.nkt / a.splits;
     } else {
       if (x_end <= s_lo) break;
       ti = fwd_locate(a, x_end - 1);
@@ -1190,14 +1191,15 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
                    : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
                      "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
                      "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
-                     "{s71}"(sc), "{s72}"(wb), "{s73}"(k5), "{s88}"(inv_sc)
+                     "{s71}"(sc), "{s72}"(wb), "{s73}"(k5)
                    : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
                      CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5),
                      CRT_D("v", 6), CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9),
                      CRT_D("v", 10), CRT_D("v", 11), CRT_D("v", 12), CRT_D("v", 13),
                      CRT_D("v", 14), CRT_D("v", 15), CRT_D("v", 16), CRT_D("v", 17),
                      CRT_D("v", 18), "v190", "v191", "v198", "v199", "v200", "v201", "v202",
-                     "v203", "v204", "v205", "v206", "v236", "v237", "s74", "s75", "s76", "s77",
+                     "v203", "v204", "v205", "v206", "v236", "v237", "v238", "v239", "v240", "v241",
+                     "s74", "s75", "s76", "s77",
                      "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "m0",
                      "vcc", "scc", "memory");
 #pragma clang diagnostic pop
@@ -1212,6 +1214,30 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
       lse2[qb] = lt > 0.f ? m2[qb] + __log2f(lt) : -INFINITY;
     }
     const int trow0 = wave * 64 + l32;  // tile row of (qb = 0); qb adds 32
+
+    if (a.splits > 1) {
+      // uniform split: the partial (normalised O, base-2 log-sum-exp) of
+      // this key range, merged by attn_combine_kernel
+      const int64_t split = w % a.splits;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int r = trow0 + qb * 32;
+        if (r >= nrows) continue;
+        const int64_t prow = ((split * a.B + b) * a.H + h) * a.Lq + row0 + r;
+        float *op = a.ws_o + prow * D + hf * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int base = qb * 16 + i4 * 4;
+            *reinterpret_cast<float4 *>(op + db * 32 + i4 * 8) =
+                make_float4(o[db][base + 0] * inv[qb], o[db][base + 1] * inv[qb],
+                            o[db][base + 2] * inv[qb], o[db][base + 3] * inv[qb]);
+          }
+        if (hf == 0) a.ws_lse[prow] = lse2[qb];
+      }
+      continue;
+    }
 
     bool merge = false;
     int64_t part0 = 0, part1 = 0, a0 = 0;

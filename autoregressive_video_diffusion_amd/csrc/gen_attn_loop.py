@@ -15,13 +15,24 @@ Shape of the generated code (head_dim 128, 64-key tiles):
     wavefront owns 64 rows as two 32-query blocks (qb = 0, 1), so every K
     and V fragment read from LDS feeds two products;
   * O (4 x 32 dims x 2 blocks, fp32) and Q (bf16) live in accumulation
-    registers (a0..a191); scores, probabilities and fragments in v0..v235;
-  * K/V tiles are copied global -> LDS (global_load_lds_dwordx4) into a ring
-    of 4 stages, three tiles ahead, one barrier per tile;
-  * a step handles tile t: S(t+1) = K(t+1) Q^T (32 products) while the
-    exponentials of S(t) run, then O += P(t) V(t) (32 products) while the
-    row maximum of S(t+1) runs; the copy of tile t+3 is issued in between.
-    Four step variants (the ring stage and score buffer rotate) are unrolled.
+    registers (a0..a191); scores, probabilities and fragments in v0..v239;
+  * K and V tiles are copied global -> LDS (global_load_lds_dwordx4) into
+    two rings of 4 stages (K three tiles ahead, V two), one barrier per tile;
+  * a step handles tile t: O += P(t-1) V(t-1) (32 products), then
+    S(t+1) = K(t+1) Q^T (32 products), while the exponentials of S(t) run
+    beside both.  The product with V runs one tile behind the exponentials,
+    so a tile's probabilities are known whole before any of them is used.
+
+No row maximum is taken in the steps.  m starts at the first tile's exact
+row maximum and p = 2^(s*c - m) is computed with it; the row sums are kept
+in two alternating register sets (before and after each tile), and a step
+ends by testing whether any lane's sums passed 2^31.  Until one does, every
+p of the tile is below 2^31 and the fp32/bf16 arithmetic is as exact as with
+the true maximum (scaling by 2^k changes no relative rounding).  When one
+does (a row's scores rose far above m), a cold block takes the tile's row
+maximum from its raw scores (the exponentials write to temporaries, so S(t)
+is intact), raises m past it and past the mass already summed, rescales O
+and the sums, and recomputes the tile's p.
 
 Every MFMA is followed by a share of the other instructions; a scheduler
 places them under each group's deadline, and a checker then walks every
@@ -43,12 +54,12 @@ D = 128
 BN = 64
 KP, VP = D // 8 + 1, D // 8 + 4     # padded LDS row pitches in 16-byte cells
 K_CELLS, V_CELLS = BN * KP, BN * VP
-STAGE = (K_CELLS + V_CELLS) * 16     # bytes of one ring stage (K then V)
-V_LDS = K_CELLS * 16                 # V's offset inside a stage
+K_STAGE, V_STAGE = K_CELLS * 16, V_CELLS * 16   # 17408, 20480 bytes
 NS = 4
+V_RING = NS * K_STAGE                # V ring after the K ring: 69632
 NW = 4
-K_INSTR, V_INSTR = K_CELLS // 64, V_CELLS // 64   # 17 and 20 copies of 1 KB
 TILE_BYTES = BN * D * 2
+
 
 # ------------------------------------------------------------------ registers
 def S(buf, kb, qb):
@@ -68,9 +79,11 @@ def VF(g):
 
 
 VM = (192, 193)                  # running max per query block (base-2 units)
-VTH = (236, 237)                 # rescale threshold per block: (m + 8) / c, in raw scores
-VL = ((194, 195), (196, 197))    # row-sum chains per query block
-VT = tuple(range(198, 206))      # temporaries
+# row-sum chains [set][qb][chain]: a step adds its tile to the set of its
+# parity, starting from the other set (which keeps the sums before the tile)
+VL = (((194, 195), (196, 197)), ((236, 237), (238, 239)))
+VT = tuple(range(198, 206))      # exponential temporaries
+VA = (240, 241)                  # rescale factors (cold block only)
 VONES = 206                      # bf16 (1, 1)
 VKH8 = 207                       # 8 * (lane / 32)
 VDMA = tuple(range(208, 218))    # copy offsets: 5 K slots, 5 V slots
@@ -88,9 +101,9 @@ def Q(qb, ks):
 
 
 # scalar registers (inputs first, then scratch)
-sKH, sVH, sT, sLAST, sREM, sC, sWB, sK5, sIC = 64, 66, 68, 69, 70, 71, 72, 73, 88
-sTILE, sT3, sKA, sVA, sSB, sN0, sN1, sTMP = 74, 75, 76, 78, 80, 82, 84, 86
-SCRATCH_S = tuple(range(74, 88))
+sKH, sVH, sT, sLAST, sREM, sC, sWB, sK5 = 64, 66, 68, 69, 70, 71, 72, 73
+sTILE, sTV, sKA, sVA, sSB, sSBV, sN0, sT3, sTMP, sLIM = 74, 75, 76, 78, 80, 81, 82, 84, 85, 86
+SUM_LIMIT = 0x4F000000           # 2^31: a lane's row sum above it calls the rescale
 
 
 def vr(base, n=1):
@@ -188,90 +201,106 @@ def v_read(g, stage):
                     f"offset:{off + 4 * VP * 16}", vset(VF(g) + 2, 2))]
 
 
-def dma(n, tile_reg_k, tile_reg_v):
-    """Copy slot n (0..4 K, 5..9 V) of the tile whose global bases are in
-    sKA / sVA into the stage whose per-wave base is in sSB."""
+def dma(n):
+    """Copy slot n (0..4 K, 5..9 V) of the tiles whose global bases are in
+    sKA / sVA into the stages whose per-wave bases are in sSB / sSBV."""
     if n < 4:
         m0 = f"s_add_u32 m0, {sr(sSB)}, {4 * n * 1024}"
-        base = tile_reg_k
+        base = sKA
     elif n == 4:
         m0 = f"s_add_u32 m0, {sr(sSB)}, {sr(sK5)}"
-        base = tile_reg_k
+        base = sKA
     else:
-        m0 = f"s_add_u32 m0, {sr(sSB)}, {V_LDS + 4 * (n - 5) * 1024}"
-        base = tile_reg_v
+        m0 = f"s_add_u32 m0, {sr(sSBV)}, {4 * (n - 5) * 1024}"
+        base = sVA
     return [Ins(m0, "salu", ("m0",)),
             Ins(f"global_load_lds_dwordx4 {vr(VDMA[n])}, {sr(base, 2)}", "vmem", (),
                 (f"v{VDMA[n]}", "m0"))]
 
 
-def tile_bases(tile_sreg, stage):
-    """sKA/sVA = global bases of tile `tile_sreg`; sSB = stage base."""
+def dma_k():
+    return [i for n in range(5) for i in dma(n)]
+
+
+def dma_v():
+    return [i for n in range(5, 10) for i in dma(n)]
+
+
+def k_bases(tile_sreg, stage):
+    """sKA = global base of K tile `tile_sreg`; sSB = its stage's base."""
     return [salu(f"s_lshl_b32 {sr(sTMP)}, {sr(tile_sreg)}, {TILE_BYTES.bit_length() - 1}"),
             salu(f"s_add_u32 {sr(sKA)}, {sr(sKH)}, {sr(sTMP)}"),
             salu(f"s_addc_u32 {sr(sKA + 1)}, {sr(sKH + 1)}, 0"),
+            salu(f"s_add_u32 {sr(sSB)}, {sr(sWB)}, {stage * K_STAGE}")]
+
+
+def v_bases(tile_sreg, stage):
+    """sVA = global base of V tile `tile_sreg`; sSBV = its stage's base."""
+    return [salu(f"s_lshl_b32 {sr(sTMP)}, {sr(tile_sreg)}, {TILE_BYTES.bit_length() - 1}"),
             salu(f"s_add_u32 {sr(sVA)}, {sr(sVH)}, {sr(sTMP)}"),
             salu(f"s_addc_u32 {sr(sVA + 1)}, {sr(sVH + 1)}, 0"),
-            salu(f"s_add_u32 {sr(sSB)}, {sr(sWB)}, {stage * STAGE}")]
+            salu(f"s_add_u32 {sr(sSBV)}, {sr(sWB)}, {V_RING + stage * V_STAGE}")]
 
 
-def switch_to_last_offsets():
+def clamp_offsets(slots):
+    """Copy rows clamped to the last valid key (the final tile)."""
     return [valu(f"v_mov_b32 {vr(VDMA[i])}, {vr(VDMAL[i])}", (f"v{VDMA[i]}",),
-                 (f"v{VDMAL[i]}",)) for i in range(10)]
+                 (f"v{VDMAL[i]}",)) for i in slots]
 
 
-def exp_group(buf, qb, c, half):
-    """Exponentials of keys 8c' + 4*half .. +3 pairs: two packed pairs of
-    P[qb][c] (c = 2 kb + c').  Two pairs interleaved so that every v_exp
-    result has an instruction between it and its reader."""
+def tile_index(dst, ahead):
+    """dst = min(t + ahead, last); SCC = (dst == last)."""
+    return [salu(f"s_add_u32 {sr(sT3)}, {sr(sT)}, {ahead}"),
+            salu(f"s_min_u32 {sr(dst)}, {sr(sT3)}, {sr(sLAST)}"),
+            salu(f"s_cmp_eq_u32 {sr(dst)}, {sr(sLAST)}")]
+
+
+def exp_group(buf, qb, c, half, lset, tmp):
+    """Exponentials of keys 8c' + 4*half .. +3 pairs of chunk c (c = 2 kb +
+    c') for query block qb: p = 2^(s*c - m) in four temporaries (S stays
+    intact), two packed bf16 pairs of P[qb][c], and their row sums added to
+    chain set lset (the first chunk starts from the other set)."""
     kb, cp = c // 2, c % 2
     base = S(buf, kb, qb) + cp * 8
     out = []
-    pairs = [half * 2, half * 2 + 1]          # packed index inside the chunk (0..3)
-    regs = [(base + 2 * j, base + 2 * j + 1) for j in pairs]
-    for a, b in regs:
-        for r in (a, b):
-            out.append(valu(f"v_fma_f32 {vr(r)}, {vr(r)}, {sr(sC)}, -{vr(VM[qb])}",
-                            (f"v{r}",), (f"v{r}", f"v{VM[qb]}")))
-    for a, b in regs:
-        for r in (a, b):
-            out.append(valu(f"v_exp_f32 {vr(r)}, {vr(r)}", (f"v{r}",), (f"v{r}",), "trans"))
-    for j, (a, b) in zip(pairs, regs):
+    pairs = [half * 2, half * 2 + 1]
+    srcs = [base + 2 * j + e for j in pairs for e in range(2)]
+    for s_, t in zip(srcs, tmp):
+        out.append(valu(f"v_fma_f32 {vr(t)}, {vr(s_)}, {sr(sC)}, -{vr(VM[qb])}",
+                        (f"v{t}",), (f"v{s_}", f"v{VM[qb]}")))
+    for t in tmp:
+        out.append(valu(f"v_exp_f32 {vr(t)}, {vr(t)}", (f"v{t}",), (f"v{t}",), "trans"))
+    for k, j in enumerate(pairs):
         pr = P(qb, c) + j
+        a, b = tmp[2 * k], tmp[2 * k + 1]
         out.append(valu(f"v_cvt_pk_bf16_f32 {vr(pr)}, {vr(a)}, {vr(b)}", (f"v{pr}",),
                         (f"v{a}", f"v{b}")))
     for j in pairs:
         pr = P(qb, c) + j
-        lr = VL[qb][j % 2]
-        out.append(valu(f"v_dot2_f32_bf16 {vr(lr)}, {vr(pr)}, {vr(VONES)}, {vr(lr)}",
-                        (f"v{lr}",), (f"v{pr}", f"v{VONES}", f"v{lr}")))
+        lr = VL[lset][qb][j % 2]
+        src = VL[1 - lset][qb][j % 2] if (c == 0 and half == 0) else lr
+        out.append(valu(f"v_dot2_f32_bf16 {vr(lr)}, {vr(pr)}, {vr(VONES)}, {vr(src)}",
+                        (f"v{lr}",), (f"v{pr}", f"v{VONES}", f"v{src}")))
     return out
 
 
-MAX_CHAINS = 4      # independent max3 chains per query block (1 or 4)
-EXP_PAIRS = True    # interleave the exponential groups two by two
-EXP_WEAVE = False   # within a pair, put a non-exponential instruction after each v_exp
-MERGE_WAITS = False # fold an lgkmcnt wait into the one before it when possible
-ABLATE = ()         # timing probes only: work left out of the main steps
+def exp_chunk(buf, c, lset):
+    """The exponentials of chunk c of S(buf), both query blocks: the two
+    halves of a block merged stage by stage (fma, exp, cvt, dot2), each with
+    its own four temporaries."""
+    out = []
+    for qb in range(2):
+        a = exp_group(buf, qb, c, 0, lset, VT[0:4])
+        b = exp_group(buf, qb, c, 1, lset, VT[4:8])
+        for lo, hi in ((0, 4), (4, 8), (8, 10), (10, 12)):
+            out += a[lo:hi] + b[lo:hi]
+    return out
 
 
-def cross_max(tmp):
-    """v[tmp] = max of v[tmp] over the lane and its partner (l ^ 32), the
-    other half of the same query column (v[tmp+1] is clobbered)."""
-    m, t2 = f"v{tmp}", f"v{tmp + 1}"
-    return [valu(f"v_mov_b32 {t2}, {m}", (t2,), (m,)),
-            valu(f"v_permlane32_swap_b32 {m}, {t2}", (m, t2), (m, t2), "perm"),
-            valu(f"v_max_f32 {m}, {m}, {t2}", (m,), (m, t2))]
-
-
-def max_ops(buf, qb, tmp, chain_tmps=(), cross=True):
-    """Row maximum of S(buf)[*][qb] over this lane's 32 keys, then (cross)
-    over the partner lane (l ^ 32), in raw score units: result in v[tmp]
-    (v[tmp+1] is clobbered).  With MAX_CHAINS = 4 the 32 values are reduced
-    in four independent chains (temporaries v[tmp], v[tmp+1] and chain_tmps)
-    joined at the end, so consecutive max3 do not wait on each other.  The
-    main steps take the lane's own maximum only: whether to rescale is
-    decided per lane, and the rescale block itself takes the row's."""
+def max_ops(buf, qb, tmp, chain_tmps):
+    """Row maximum of S(buf)[*][qb] over the lane's 32 keys (four chains of
+    8 joined), then over the partner lane (l ^ 32), in raw score units:
+    result in v[tmp] (v[tmp+1] and chain_tmps clobbered)."""
     vals = [S(buf, kb, qb) + r for kb in range(2) for r in range(16)]
     m = f"v{tmp}"
 
@@ -290,54 +319,76 @@ def max_ops(buf, qb, tmp, chain_tmps=(), cross=True):
                 i += 1
         return out
 
-    if MAX_CHAINS == 1 or not chain_tmps:
-        out = chain(m, vals)
-    else:
-        dsts = [m, f"v{tmp + 1}"] + [f"v{x}" for x in chain_tmps]
-        parts = [chain(d, vals[8 * i:8 * i + 8]) for i, d in enumerate(dsts)]
-        out = [ins for grp in zip(*parts) for ins in grp]          # round-robin
-        out.append(valu(f"v_max3_f32 {m}, {dsts[0]}, {dsts[1]}, {dsts[2]}", (m,),
-                        tuple(dsts[:3])))
-        out.append(valu(f"v_max_f32 {m}, {m}, {dsts[3]}", (m,), (m, dsts[3])))
-    if cross:
-        out += cross_max(tmp)
+    dsts = [m, f"v{tmp + 1}"] + [f"v{x}" for x in chain_tmps]
+    parts = [chain(d, vals[8 * i:8 * i + 8]) for i, d in enumerate(dsts)]
+    out = [ins for grp in zip(*parts) for ins in grp]
+    out.append(valu(f"v_max3_f32 {m}, {dsts[0]}, {dsts[1]}, {dsts[2]}", (m,), tuple(dsts[:3])))
+    out.append(valu(f"v_max_f32 {m}, {m}, {dsts[3]}", (m,), (m, dsts[3])))
+    out += cross_max(tmp)
     return out
 
 
-def threshold(qb):
-    """VTH[qb] = (m + 8) / c: a raw score above it would give p > 2^8."""
-    t = VTH[qb]
-    return [valu(f"v_add_f32 {vr(t)}, 0x41000000, {vr(VM[qb])}", (f"v{t}",), (f"v{VM[qb]}",)),
-            valu(f"v_mul_f32 {vr(t)}, {sr(sIC)}, {vr(t)}", (f"v{t}",), (f"v{t}",))]
+def cross_max(tmp):
+    """v[tmp] = max of v[tmp] over the lane and its partner (l ^ 32), the
+    other half of the same query column (v[tmp+1] is clobbered)."""
+    m, t2 = f"v{tmp}", f"v{tmp + 1}"
+    return [valu(f"v_mov_b32 {t2}, {m}", (t2,), (m,)),
+            valu(f"v_permlane32_swap_b32 {m}, {t2}", (m, t2), (m, t2), "perm"),
+            valu(f"v_max_f32 {m}, {m}, {t2}", (m,), (m, t2))]
 
 
-def rescale_block(cur_buf, tag):
-    """Raise the running max where a row's new maximum exceeds it by more
-    than 2^8 and rescale that row's sums and O (rare: early tiles).  The
-    lanes' raw maxima are in VT[0] (qb 0) and VT[2] (qb 1); the row maxima
-    and the per-lane decisions (sN0 / sN1) are taken here, so both halves of
-    a row decide alike.  S(cur_buf) is free here and serves as the buffer
-    for O."""
-    out = [label(f"{tag}")]
+def sum_check(lset, tag):
+    """Branch to `tag` when any lane's row-sum chain of set lset passed 2^31
+    (a NaN sum never does)."""
+    (a, b), (c, d) = VL[lset]
+    t = VT[0]
+    return [valu(f"v_max3_f32 {vr(t)}, {vr(a)}, {vr(b)}, {vr(c)}", (f"v{t}",),
+                 (f"v{a}", f"v{b}", f"v{c}")),
+            valu(f"v_max_f32 {vr(t)}, {vr(t)}, {vr(d)}", (f"v{t}",), (f"v{t}", f"v{d}")),
+            valu(f"v_cmp_lt_f32_e64 {sr(sN0, 2)}, {sr(sLIM)}, {vr(t)}", (f"s{sN0}",),
+                 (f"v{t}",)),
+            salu(f"s_cmp_lg_u64 {sr(sN0, 2)}, 0"),
+            branch(f"s_cbranch_scc1 {tag}", tag)]
+
+
+def rescale_block(buf, lset, tag, back):
+    """A tile whose probabilities summed past 2^31 in some lane: per query
+    block, m' = max(m, c * rowmax(S(buf)), m + log2(row sum before the tile)
+    - 8) (taken across the lane pair, so both halves of a row agree), the
+    sums before the tile and O scaled by 2^(m - m'), and the tile's
+    probabilities and sums recomputed with m'.  Afterwards every p of the
+    tile is <= 1 and the sums are below 2^8 + 64.  S(buf) is then free and
+    buffers O."""
+    out = [label(tag)]
+    prev = 1 - lset
     for qb in range(2):
-        mc, need = VT[2 * qb], (sN0, sN1)[qb]
-        mn, al = VT[4 + 2 * qb], VT[5 + 2 * qb]
-        out += cross_max(mc)
-        out.append(valu(f"v_cmp_gt_f32_e64 {sr(need, 2)}, {vr(mc)}, {vr(VTH[qb])}",
-                        (f"s{need}",), (f"v{mc}", f"v{VTH[qb]}")))
-        out += [valu(f"v_mul_f32 {vr(mc)}, {sr(sC)}, {vr(mc)}", (f"v{mc}",), (f"v{mc}",)),
-                valu(f"v_cndmask_b32_e64 {vr(mn)}, {vr(VM[qb])}, {vr(mc)}, {sr(need, 2)}",
-                     (f"v{mn}",), (f"v{VM[qb]}", f"v{mc}")),
-                valu(f"v_sub_f32 {vr(al)}, {vr(VM[qb])}, {vr(mn)}", (f"v{al}",),
-                     (f"v{VM[qb]}", f"v{mn}")),
+        mx, t1, t2, t3, al = VT[0], VT[1], VT[2], VT[3], VT[4]
+        out += max_ops(buf, qb, mx, (t2, t3))
+        (la, lb) = VL[prev][qb]
+        out += [valu(f"v_mul_f32 {vr(mx)}, {sr(sC)}, {vr(mx)}", (f"v{mx}",), (f"v{mx}",)),
+                valu(f"v_max_f32 {vr(mx)}, {vr(mx)}, {vr(VM[qb])}", (f"v{mx}",),
+                     (f"v{mx}", f"v{VM[qb]}")),
+                valu(f"v_add_f32 {vr(t2)}, {vr(la)}, {vr(lb)}", (f"v{t2}",), (f"v{la}", f"v{lb}")),
+                valu(f"v_log_f32 {vr(t2)}, {vr(t2)}", (f"v{t2}",), (f"v{t2}",), "trans"),
+                valu(f"v_add_f32 {vr(t2)}, {vr(t2)}, {vr(VM[qb])}", (f"v{t2}",),
+                     (f"v{t2}", f"v{VM[qb]}")),
+                valu(f"v_add_f32 {vr(t2)}, 0xc1000000, {vr(t2)}", (f"v{t2}",), (f"v{t2}",)),
+                valu(f"v_max_f32 {vr(mx)}, {vr(mx)}, {vr(t2)}", (f"v{mx}",), (f"v{mx}", f"v{t2}"))]
+        out += cross_max(mx)
+        out += [valu(f"v_sub_f32 {vr(al)}, {vr(VM[qb])}, {vr(mx)}", (f"v{al}",),
+                     (f"v{VM[qb]}", f"v{mx}")),
                 valu(f"v_exp_f32 {vr(al)}, {vr(al)}", (f"v{al}",), (f"v{al}",), "trans"),
-                valu(f"v_mov_b32 {vr(VM[qb])}, {vr(mn)}", (f"v{VM[qb]}",), (f"v{mn}",))]
-        out += threshold(qb)
-        for ch in range(2):
-            lr = VL[qb][ch]
-            out.append(valu(f"v_mul_f32 {vr(lr)}, {vr(lr)}, {vr(al)}", (f"v{lr}",),
-                            (f"v{lr}", f"v{al}")))
-        tmp = S(cur_buf, 0, 0)   # 64 free registers
+                valu(f"v_mov_b32 {vr(VM[qb])}, {vr(mx)}", (f"v{VM[qb]}",), (f"v{mx}",)),
+                valu(f"v_mul_f32 {vr(la)}, {vr(la)}, {vr(al)}", (f"v{la}",), (f"v{la}", f"v{al}")),
+                valu(f"v_mul_f32 {vr(lb)}, {vr(lb)}, {vr(al)}", (f"v{lb}",), (f"v{lb}", f"v{al}"))]
+        out.append(valu(f"v_mov_b32 {vr(VA[qb])}, {vr(al)}", (f"v{VA[qb]}",), (f"v{al}",)))
+    # the tile's probabilities again, with the new maximum
+    for c in range(4):
+        out += exp_chunk(buf, c, lset)
+    # O *= alpha, 64 accumulators at a time through S(buf)
+    tmp = S(buf, 0, 0)
+    for qb in range(2):
+        al = VA[qb]
         regs = [(O(db, qb) + r) for db in range(4) for r in range(16)]
         for i, a in enumerate(regs):
             out.append(Ins(f"v_accvgpr_read_b32 v{tmp + i}, a{a}", "accr", (f"v{tmp + i}",),
@@ -348,6 +399,7 @@ def rescale_block(cur_buf, tag):
         for i, a in enumerate(regs):
             out.append(Ins(f"v_accvgpr_write_b32 a{a}, v{tmp + i}", "accw", (f"a{a}",),
                            (f"v{tmp + i}",)))
+    out.append(branch(f"s_branch {back}", back))
     return out
 
 
@@ -393,8 +445,8 @@ def qk_mfmas(buf):
 
 
 def pv_mfmas():
-    """O += V^T P^T, chunk by chunk of 16 keys (the order the exponentials
-    finish in); each V^T fragment feeds two consecutive products."""
+    """O += V^T P^T, chunk by chunk of 16 keys; each V^T fragment feeds two
+    consecutive products."""
     out = []
     for c in range(4):
         for db in range(4):
@@ -405,150 +457,47 @@ def pv_mfmas():
     return out
 
 
-def exp_chunk(cur, c):
-    """The exponentials of chunk c of S(cur), both query blocks: 4 groups of
-    12 instructions; with EXP_PAIRS two groups are merged stage by stage
-    (fma, exp, cvt, dot2), doubling the distance between each instruction
-    and the one that reads its result."""
-    groups = [exp_group(cur, qb, c, half) for qb in range(2) for half in range(2)]
-    if not EXP_PAIRS:
-        return [i for g in groups for i in g]
-    out = []
-    for a, b in ((groups[0], groups[1]), (groups[2], groups[3])):
-        if EXP_WEAVE:
-            # fma a | exp a with fma b | exp b with cvt/dot2 a | cvt/dot2 b
-            out += a[0:4]
-            for k in range(4):
-                out += [a[4 + k], b[k]]
-            x = a[8:12]
-            for k in range(4):
-                out += [b[4 + k], x[k]]
-            out += b[8:12]
-        else:
-            for lo, hi in ((0, 4), (4, 8), (8, 10), (10, 12)):
-                out += a[lo:hi] + b[lo:hi]
-    return out
-
-
-def exp_items(cur, lo, hi):
-    """The exponentials of S(cur), chunk by chunk (chunk c is read by the PV
-    products base + 8c + qb), spread over gaps [lo, hi)."""
-    instrs = []
-    for c in range(4):
-        instrs += exp_chunk(cur, c)
-    return spread(instrs, lo, hi)
-
-
-def exp_items_due(cur):
-    """The same when the PV products start at once (the last tile): chunk 0
-    before the first product, chunk c spread over the 8 products of chunk
-    c - 1."""
-    out = []
-    for c in range(4):
-        instrs = exp_chunk(cur, c)
-        out += [(0, i) for i in instrs] if c == 0 else spread(instrs, 8 * c - 8, 8 * c - 1)
-    return out
-
-
 KR_AHEAD = 2.5      # gaps between a K fragment's read and its first product
 VR_AHEAD = 3.0      # the same for V^T fragments (ring of 4: at most 6)
 
 
-def k_read_items(stage, frags):
-    """K fragment f feeds QK products 2f and 2f+1; its ring slot was last read
-    by product 2f - 7, so it can be read up to six products ahead."""
-    return [(2 * f - KR_AHEAD, ins) for f in frags for ins in k_read(f, stage)]
+def k_read_items(stage, base, frags):
+    """K fragment f feeds QK products base + 2f and base + 2f + 1; its ring
+    slot was last read by product base + 2f - 7."""
+    return [(base + 2 * f - KR_AHEAD, ins) for f in frags for ins in k_read(f, stage)]
 
 
-def v_read_items(stage, base):
-    """V^T fragment g feeds PV products base + 2g and base + 2g + 1; its ring
-    slot was last read by product base + 2g - 7."""
+def v_read_items(stage, base, frags):
+    """V^T fragment g feeds PV products base + 2g and base + 2g + 1; its
+    ring slot was last read by product base + 2g - 7."""
     out = []
-    for g in range(16):
+    for g in frags:
         for j, ins in enumerate(v_read(g, stage)):
             out.append((base + 2 * g - VR_AHEAD + 0.1 * j, ins))
     return out
 
 
-def _ablate(items):
-    """Drop classes of work from a step's items (timing probes: the results
-    are wrong, every access stays where it was)."""
-    def drop(i):
-        t = i.text
-        return (("exp" in ABLATE and (t.startswith("v_fma_f32") or t.startswith("v_exp_f32") or
-                                      t.startswith("v_cvt_pk") or t.startswith("v_dot2"))) or
-                ("max" in ABLATE and (t.startswith("v_max") or "permlane" in t or
-                                      (t.startswith("v_mov_b32") and i.kind == "valu"))) or
-                ("lds" in ABLATE and i.kind == "lds") or
-                ("dma" in ABLATE and (i.kind == "vmem" or t.startswith("s_add_u32 m0"))) or
-                ("barrier" in ABLATE and (i.kind == "barrier" or t.startswith("s_waitcnt vmcnt"))))
-    return [(t, i) for t, i in items if not drop(i)]
+def exp_items(buf, lset, windows):
+    """The exponentials of S(buf), chunk c spread over windows[c]."""
+    out = []
+    for c in range(4):
+        out += spread(exp_chunk(buf, c, lset), *windows[c])
+    return out
 
 
-def step(phi):
-    """Main step of phase phi: tile t in the loop counter sT."""
-    cur, nxt = phi % 2, 1 - phi % 2
-    kst, vst, dst = (phi + 1) % NS, phi % NS, (phi + 3) % NS
-    head = [label(f"crt_ph{phi}"),
-            salu(f"s_cmp_ge_u32 {sr(sT)}, {sr(sLAST)}"),
-            branch(f"s_cbranch_scc1 crt_last{phi}", f"crt_last{phi}"),
-            salu(f"s_add_u32 {sr(sT3)}, {sr(sT)}, 3"),
-            salu(f"s_min_u32 {sr(sTILE)}, {sr(sT3)}, {sr(sLAST)}"),
-            salu(f"s_cmp_eq_u32 {sr(sTILE)}, {sr(sLAST)}"),
-            branch(f"s_cbranch_scc1 crt_sw{phi}", f"crt_sw{phi}"),
-            label(f"crt_swr{phi}")] + tile_bases(sTILE, dst)
-    mf = qk_mfmas(nxt) + pv_mfmas()
-    items = []
-    # K fragments 0..3 of tile t+1 were read at the end of the previous step
-    items += k_read_items(kst, range(4, 16))
-    # the copy of tile t+3: one slot every second gap
-    for n in range(10):
-        for j, ins in enumerate(dma(n, sKA, sVA)):
-            items.append((1 + 2 * n + 0.1 * j, ins))
-    items += exp_items(cur, 0, 54)
-    items += v_read_items(vst, 32)
-    # row maximum of S(t+1) (its last products are 28..31)
-    m0 = max_ops(nxt, 0, VT[0], (VT[4], VT[5]), cross=False)
-    m1 = max_ops(nxt, 1, VT[2], (VT[6], VT[7]), cross=False)
-    mx = [i for pair in zip(m0, m1) for i in pair]   # the two blocks interleaved
-    items += spread(mx, 34, 63)
-    # before the last two products: tile t+2 has landed and every wave is
-    # past its reads of tile t's V; then tile t+2's first K fragments
-    items += [(62.5, Ins("s_waitcnt lgkmcnt(0)", "wait")),
-              (62.6, Ins("s_waitcnt vmcnt(10)", "wait")),
-              (62.7, Ins("s_barrier", "barrier"))]
-    nkst = (phi + 2) % NS
-    items += [(62.8 + 0.01 * f, ins) for f in range(4) for ins in k_read(f, nkst)]
-    if ABLATE:
-        items = _ablate(items)
-        if "mfma" in ABLATE:
-            mf = mf[:1]
-    body = place(mf, items, head)
-    tail = []
-    for qb in range(2):
-        mc = VT[2 * qb]
-        tail.append(valu(f"v_cmp_gt_f32_e64 {sr((sN0, sN1)[qb], 2)}, {vr(mc)}, {vr(VTH[qb])}",
-                         (f"s{(sN0, sN1)[qb]}",), (f"v{mc}", f"v{VTH[qb]}")))
-    tail += [salu(f"s_or_b64 {sr(sTMP, 2)}, {sr(sN0, 2)}, {sr(sN1, 2)}"),
-             branch(f"s_cbranch_scc1 crt_resc{phi}", f"crt_resc{phi}"),
-             label(f"crt_rescr{phi}"),
-             salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1")]
-    if phi == NS - 1:
-        tail.append(branch("s_branch crt_ph0", "crt_ph0"))
-    cold = [label(f"crt_sw{phi}")] + switch_to_last_offsets() + \
-        [branch(f"s_branch crt_swr{phi}", f"crt_swr{phi}")]
-    cold += rescale_block(cur, f"crt_resc{phi}") + \
-        [branch(f"s_branch crt_rescr{phi}", f"crt_rescr{phi}")]
-    return body + tail, cold
+# chunk c of the next tile's P may be written once the products reading the
+# current P[c] (8c .. 8c+7) have issued
+MID_EXP = [(8 + 14 * c, 22 + 14 * c) for c in range(4)]
+LAST_EXP = [(8 * c + 6, 8 * c + 14) for c in range(4)]
+FIRST_EXP = [(8 * c, 8 * c + 8) for c in range(4)]
 
 
-def last_step(phi):
-    """Tile t = last: exponentials of S(cur) (keys at or past the valid count
-    masked when the tile is partial) and O += P V; no next tile."""
-    cur, vst = phi % 2, phi % NS
-    out = [label(f"crt_last{phi}"),
-           salu(f"s_cmp_lt_u32 {sr(sREM)}, {BN}"),
-           branch(f"s_cbranch_scc0 crt_nomask{phi}", f"crt_nomask{phi}"),
+def mask_tail(buf, tag):
+    """Scores of keys at or past the valid count -> -inf (the final tile,
+    when it is partial)."""
+    tag = f"{tag}_nomask"
+    out = [salu(f"s_cmp_lt_u32 {sr(sREM)}, {BN}"),
+           branch(f"s_cbranch_scc0 {tag}", tag),
            valu(f"v_mov_b32 {vr(VT[7])}, 0xff800000", (f"v{VT[7]}",), ())]
     for kb in range(2):
         for r in range(16):
@@ -557,77 +506,188 @@ def last_step(phi):
             out += [valu(f"v_add_u32 {vr(t)}, {key}, {vr(VKH8)}", (f"v{t}",), (f"v{VKH8}",)),
                     valu(f"v_cmp_le_i32_e32 vcc, {sr(sREM)}, {vr(t)}", ("vcc",), (f"v{t}",))]
             for qb in range(2):
-                x = S(cur, kb, qb) + r
+                x = S(buf, kb, qb) + r
                 out.append(valu(f"v_cndmask_b32_e32 {vr(x)}, {vr(x)}, {vr(VT[7])}, vcc",
                                 (f"v{x}",), (f"v{x}", f"v{VT[7]}", "vcc")))
-    out.append(label(f"crt_nomask{phi}"))
-    items = exp_items_due(cur) + v_read_items(vst, 0)
-    body = place(pv_mfmas(), items, out)
+    out.append(label(tag))
+    return out
+
+
+def step_head(tag, kstage, vstage):
+    """Copy targets of the step: K tile min(t+3, last) and V tile min(t+2,
+    last) (rows clamped once a tile is the last), their stage bases."""
+    return (tile_index(sTILE, 3) +
+            [branch(f"s_cbranch_scc1 {tag}_swk", f"{tag}_swk"), label(f"{tag}_swkr")] +
+            tile_index(sTV, 2) +
+            [branch(f"s_cbranch_scc1 {tag}_swv", f"{tag}_swv"), label(f"{tag}_swvr")] +
+            k_bases(sTILE, kstage) + v_bases(sTV, vstage))
+
+
+def head_cold(tag):
+    return ([label(f"{tag}_swk")] + clamp_offsets(range(5)) +
+            [branch(f"s_branch {tag}_swkr", f"{tag}_swkr"), label(f"{tag}_swv")] +
+            clamp_offsets(range(5, 10)) + [branch(f"s_branch {tag}_swvr", f"{tag}_swvr")])
+
+
+def end_of_step(n_mf, vstage_next):
+    """Before the last two products: every LDS read of the step is back,
+    the tiles copied before this step have landed, every wave is past its
+    reads; then the first V^T fragments of the next step's product."""
+    items = [(n_mf - 1.5, Ins("s_waitcnt lgkmcnt(0)", "wait")),
+             (n_mf - 1.4, Ins("s_waitcnt vmcnt(10)", "wait")),
+             (n_mf - 1.3, Ins("s_barrier", "barrier"))]
+    items += [(n_mf - 1.2 + 0.01 * g, ins) for g in range(2) for ins in v_read(g, vstage_next)]
+    return items
+
+
+def dma_items(lo, hi):
+    ins = dma_k() + dma_v()
+    return [(lo + (hi - lo) * (k // 2) / 10 + 0.01 * (k % 2), i) for k, i in enumerate(ins)]
+
+
+def first_step():
+    """t = first tile: S(t+1) = K(t+1) Q^T and the exponentials of S(t);
+    no product with V yet."""
+    tag = "crt_first"
+    head = [label(tag)] + step_head(tag, 3, 2)
+    items = k_read_items(1, 0, range(16)) + dma_items(0, 20) + exp_items(0, 0, FIRST_EXP)
+    items += end_of_step(32, 0)
+    body = place(qk_mfmas(1), items, head)
+    tail = sum_check(0, f"{tag}_resc") + [label(f"{tag}_rescr"),
+                                         salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1"),
+                                         branch("s_branch crt_ph1", "crt_ph1")]
+    cold = head_cold(tag) + rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
+    return body + tail, cold
+
+
+def step(phi):
+    """Main step of phase phi (tile t = first + phi mod 4): O += P(t-1)
+    V(t-1), then S(t+1) = K(t+1) Q^T, the exponentials of S(t) beside
+    both, the copies of K(t+3) and V(t+2)."""
+    cur, nxt, lset = phi % 2, 1 - phi % 2, phi % 2
+    tag = f"crt_ph{phi}"
+    head = [label(tag), salu(f"s_cmp_ge_u32 {sr(sT)}, {sr(sLAST)}"),
+            branch(f"s_cbranch_scc1 crt_last{phi}", f"crt_last{phi}")]
+    head += step_head(tag, (phi + 3) % NS, (phi + 2) % NS)
+    mf = pv_mfmas() + qk_mfmas(nxt)
+    items = v_read_items((phi + 3) % NS, 0, range(2, 16))
+    items += k_read_items((phi + 1) % NS, 32, range(16))
+    items += dma_items(1, 21)
+    items += exp_items(cur, lset, MID_EXP)
+    items += end_of_step(64, phi % NS)
+    body = place(mf, items, head)
+    tail = sum_check(lset, f"{tag}_resc") + [label(f"{tag}_rescr"),
+                                            salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1")]
+    if phi == NS - 1:
+        tail.append(branch("s_branch crt_ph0", "crt_ph0"))
+    cold = head_cold(tag) + rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
+    return body + tail, cold
+
+
+def drain(vstage, tag):
+    """O += P(last) V(last): the products of the final tile."""
+    body = place(pv_mfmas(), v_read_items(vstage, 0, range(16)), [label(tag)])
     return body + [branch("s_branch crt_end", "crt_end")]
+
+
+def last_step(phi):
+    """t = last (after the first): O += P(t-1) V(t-1) beside the
+    exponentials of the (masked) final tile, then its own products."""
+    cur, lset = phi % 2, phi % 2
+    tag = f"crt_last{phi}"
+    head = [label(tag)] + mask_tail(cur, tag)
+    items = v_read_items((phi + 3) % NS, 0, range(2, 16)) + exp_items(cur, lset, LAST_EXP)
+    body = place(pv_mfmas(), items, head)
+    tail = sum_check(lset, f"{tag}_resc") + [label(f"{tag}_rescr")]
+    if lset == 1:   # the row sums leave the loop in set 0
+        for qb in range(2):
+            for ch in range(2):
+                d, s_ = VL[0][qb][ch], VL[1][qb][ch]
+                tail.append(valu(f"v_mov_b32 {vr(d)}, {vr(s_)}", (f"v{d}",), (f"v{s_}",)))
+    check_p_war(body, f"last {phi}")
+    tail += drain(phi % NS, f"{tag}_drain")
+    cold = rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
+    return body + tail, cold
+
+
+def only_step():
+    """The first tile is also the last: its exponentials, then its products."""
+    tag = "crt_only"
+    body = [label(tag)] + mask_tail(0, tag)
+    for c in range(4):
+        body += exp_chunk(0, c, 0)
+    body += sum_check(0, f"{tag}_resc") + [label(f"{tag}_rescr")]
+    body += drain(0, f"{tag}_drain")
+    cold = rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
+    return body, cold
 
 
 def prologue():
     out = [Ins("s_nop 7", "nop"),
-           valu(f"v_mov_b32 {vr(VONES)}, 0x3f803f80", (f"v{VONES}",), ())]
-    for qb in range(2):
-        for ch in range(2):
-            out.append(valu(f"v_mov_b32 {vr(VL[qb][ch])}, 0", (f"v{VL[qb][ch]}",), ()))
-    # copies of tiles t, t+1, t+2 (clamped to the last) into stages 0, 1, 2
-    for i in range(3):
-        out += [salu(f"s_add_u32 {sr(sT3)}, {sr(sT)}, {i}"),
-                salu(f"s_min_u32 {sr(sTILE)}, {sr(sT3)}, {sr(sLAST)}"),
-                salu(f"s_cmp_eq_u32 {sr(sTILE)}, {sr(sLAST)}"),
-                branch(f"s_cbranch_scc0 crt_pro{i}", f"crt_pro{i}")]
-        out += switch_to_last_offsets()
+           valu(f"v_mov_b32 {vr(VONES)}, 0x3f803f80", (f"v{VONES}",), ()),
+           salu(f"s_mov_b32 {sr(sLIM)}, {SUM_LIMIT:#x}")]
+    for st in range(2):
+        for qb in range(2):
+            for ch in range(2):
+                r = VL[st][qb][ch]
+                out.append(valu(f"v_mov_b32 {vr(r)}, 0", (f"v{r}",), ()))
+    # K(t), K(t+1), V(t), K(t+2), V(t+1) (tiles clamped to the last) into
+    # K stages 0, 1, 2 and V stages 0, 1
+    for i, (kind, ahead, stage) in enumerate([("k", 0, 0), ("k", 1, 1), ("v", 0, 0),
+                                              ("k", 2, 2), ("v", 1, 1)]):
+        dst = sTILE if kind == "k" else sTV
+        out += tile_index(dst, ahead) + [branch(f"s_cbranch_scc0 crt_pro{i}", f"crt_pro{i}")]
+        out += clamp_offsets(range(5) if kind == "k" else range(5, 10))
         out.append(label(f"crt_pro{i}"))
-        out += tile_bases(sTILE, i)
-        for n in range(10):
-            out += dma(n, sKA, sVA)
+        out += (k_bases(dst, stage) + dma_k()) if kind == "k" else (v_bases(dst, stage) + dma_v())
     out += [Ins("s_waitcnt vmcnt(20)", "wait"), Ins("s_barrier", "barrier")]
-    # S of the first tile into buffer 0, then its row maximum
-    out = place(qk_mfmas(0), k_read_items(0, range(16)), out)
+    # S of the first tile into buffer 0, then its exact row maximum
+    out = place(qk_mfmas(0), k_read_items(0, 0, range(16)), out)
     for qb in range(2):
-        out += max_ops(0, qb, VT[2 * qb])
+        out += max_ops(0, qb, VT[2 * qb], (VT[4 + 2 * qb], VT[5 + 2 * qb]))
         out.append(valu(f"v_mul_f32 {vr(VM[qb])}, {sr(sC)}, {vr(VT[2 * qb])}", (f"v{VM[qb]}",),
                         (f"v{VT[2 * qb]}",)))
-        out += threshold(qb)
-    # tile t+1 has landed and is visible: its first K fragments
-    out += [Ins("s_waitcnt vmcnt(10)", "wait"), Ins("s_barrier", "barrier")]
-    for f in range(4):
-        out += k_read(f, 1)
+    # K(t+1) and V(t) have landed and are visible
+    out += [Ins("s_waitcnt vmcnt(10)", "wait"), Ins("s_barrier", "barrier"),
+            salu(f"s_cmp_ge_u32 {sr(sT)}, {sr(sLAST)}"),
+            branch("s_cbranch_scc1 crt_only", "crt_only")]
     return out
 
 
-def check_p_ready(body):
-    """Every PV product must come after the conversions that write all four
-    registers of its P operand in the same step."""
+def check_p_war(body, what):
+    """No probability register may be rewritten before the products that
+    read its previous value in the same block have issued."""
     written = set()
     for ins in body:
         if ins.kind == "valu" and ins.text.startswith("v_cvt_pk_bf16_f32"):
             written |= set(ins.dst)
         if ins.kind == "mfma" and ins.dst[0].startswith("a"):
-            p = [r for r in ins.src if r.startswith("v") and 128 <= int(r[1:]) < 160]
-            missing = [r for r in p if r not in written]
-            if missing:
-                raise RuntimeError(f"{ins.text}: P registers {missing} not yet written")
+            hit = [r for r in ins.src if r in written]
+            if hit:
+                raise RuntimeError(f"{what}: {ins.text} reads {hit} after they were rewritten")
 
 
 def program():
-    main, cold = [], []
+    cold = []
+    first, c = first_step()
+    check_p_war(first, "first")
+    cold += c
+    main = []
     for phi in range(NS):
         b, c = step(phi)
-        if "exp" not in ABLATE:
-            check_p_ready(b)
+        check_p_war(b, f"phase {phi}")
         main += b
         cold += c
     lasts = []
     for phi in range(NS):
-        b = last_step(phi)
-        check_p_ready(b)
+        b, c = last_step(phi)
         lasts += b
+        cold += c
+    only, c = only_step()
+    cold += c
     end = [label("crt_end"), Ins("s_waitcnt vmcnt(0) lgkmcnt(0)", "wait"),
            Ins("s_nop 7", "nop"), Ins("s_nop 7", "nop"), Ins("s_nop 7", "nop")]
-    return prologue() + main + cold + lasts + end
+    return prologue() + first + main + lasts + only + cold + end
 
 
 # ------------------------------------------------------------------ hazard checker
@@ -776,56 +836,6 @@ def fix(prog):
     raise RuntimeError("hazard fixing did not converge")
 
 
-def merge_waits(prog, window=12):
-    """Fold an s_waitcnt lgkmcnt(n2) into an earlier lgkmcnt(n1) of the same
-    straight-line run when at most `window` instructions lie between them:
-    with k LDS reads issued in between, lgkmcnt(min(n1, n2 - k)) at the first
-    point already guarantees the second (reads complete in order)."""
-    out = list(prog)
-    i = 0
-    while i < len(out):
-        a = out[i]
-        if a.kind == "wait" and a.text.startswith("s_waitcnt lgkmcnt("):
-            n1 = int(a.text.split("(")[1].split(")")[0])
-            k = 0
-            for j in range(i + 1, min(len(out), i + 1 + window)):
-                b = out[j]
-                if b.kind in ("label", "branch", "barrier"):
-                    break
-                if b.kind == "lds":
-                    k += 1
-                if b.kind == "wait" and b.text.startswith("s_waitcnt lgkmcnt("):
-                    n2 = int(b.text.split("(")[1].split(")")[0])
-                    if n2 - k >= 0:
-                        out[i] = Ins(f"s_waitcnt lgkmcnt({min(n1, n2 - k)})", "wait")
-                        del out[j]
-                    break
-        i += 1
-    return out
-
-
-def stats(prog):
-    import collections
-    c = collections.Counter(i.kind for i in prog)
-    nops = sum(ws_of(i) for i in prog if i.kind == "nop")
-    return dict(c), nops
-
-
-def step_report(prog):
-    """Instructions and nop wait states inside each phase's main step."""
-    out = []
-    for phi in range(NS):
-        s = next(k for k, i in enumerate(prog) if i.text == f"crt_ph{phi}:")
-        e = next(k for k, i in enumerate(prog) if i.text.startswith("s_add_u32 s68, s68, 1")
-                 and k > s)
-        seg = prog[s:e]
-        n = sum(1 for i in seg if i.kind not in ("label",))
-        nop = sum(ws_of(i) for i in seg if i.kind == "nop")
-        waits = sum(1 for i in seg if i.kind == "wait")
-        out.append((phi, n, nop, waits))
-    return out
-
-
 def render(prog):
     """Assembly lines.  Labels become numeric local labels (each number
     defined once per instance of the asm statement, references resolved
@@ -847,6 +857,30 @@ def render(prog):
     return out
 
 
+
+
+def stats(prog):
+    import collections
+    c = collections.Counter(i.kind for i in prog)
+    nops = sum(ws_of(i) for i in prog if i.kind == "nop")
+    return dict(c), nops
+
+
+def step_report(prog):
+    """Instructions and nop wait states inside each phase's main step."""
+    out = []
+    for phi in range(NS):
+        s = next(k for k, i in enumerate(prog) if i.text == f"crt_ph{phi}:")
+        e = next(k for k, i in enumerate(prog) if i.text.startswith(f"s_add_u32 s{sT}, s{sT}, 1")
+                 and k > s)
+        seg = prog[s:e]
+        n = sum(1 for i in seg if i.kind not in ("label",))
+        nop = sum(ws_of(i) for i in seg if i.kind == "nop")
+        waits = sum(1 for i in seg if i.kind == "wait")
+        out.append((phi, n, nop, waits))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -854,31 +888,13 @@ def main():
     ap.add_argument("--report", action="store_true")
     ap.add_argument("--kr-ahead", type=float, default=None, help="K fragment read distance")
     ap.add_argument("--vr-ahead", type=float, default=None, help="V fragment read distance")
-    ap.add_argument("--max-chains", type=int, default=None, choices=(1, 4))
-    ap.add_argument("--exp-pairs", type=int, default=None, choices=(0, 1))
-    ap.add_argument("--exp-weave", type=int, default=None, choices=(0, 1))
-    ap.add_argument("--merge-waits", type=int, default=None, choices=(0, 1))
-    ap.add_argument("--ablate", default="", help="timing probe: comma list of exp, max, lds, "
-                    "dma, barrier, mfma left out of the main steps")
     args = ap.parse_args()
-    global KR_AHEAD, VR_AHEAD, MAX_CHAINS, EXP_PAIRS, EXP_WEAVE, MERGE_WAITS, ABLATE
-    if args.ablate:
-        ABLATE = tuple(args.ablate.split(","))
-    if args.exp_weave is not None:
-        EXP_WEAVE = bool(args.exp_weave)
-    if args.merge_waits is not None:
-        MERGE_WAITS = bool(args.merge_waits)
-    if args.max_chains is not None:
-        MAX_CHAINS = args.max_chains
-    if args.exp_pairs is not None:
-        EXP_PAIRS = bool(args.exp_pairs)
+    global KR_AHEAD, VR_AHEAD
     if args.kr_ahead is not None:
         KR_AHEAD = args.kr_ahead
     if args.vr_ahead is not None:
         VR_AHEAD = args.vr_ahead
     prog = fix(program())
-    if MERGE_WAITS:
-        prog = fix(merge_waits(prog))
     lines = render(prog)
     text = ("// Generated by gen_attn_loop.py; do not edit.  The key loop of the dense\n"
             "// chunk-causal attention kernel (head_dim 128) in CDNA4 assembly: one\n"

@@ -35,10 +35,10 @@ AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
   const int64_t min_ktiles = (min_keys + p.bn - 1) / p.bn;
   constexpr int64_t kSlots = 256;  // one workgroup per compute unit of an MI355X
   p.splits = 1;
-  // head_dim 64: split the key range only when the query tiles alone leave
-  // most of the chip idle (partials cost (D + 1) * 4 bytes per row and split
-  // of traffic, merged by a second kernel).
-  if (allow_split && D != 128 && units * 2 <= kSlots) {
+  // Split the key range uniformly only when the query tiles alone leave most
+  // of the chip idle (partials cost (D + 1) * 4 bytes per row and split of
+  // traffic, merged by a second kernel).
+  if (allow_split && units * 2 <= kSlots) {
     double best = (double)units / (double)(((units + kSlots - 1) / kSlots) * kSlots);
     for (int s = 2; s <= 16; ++s) {
       if (min_ktiles / s < 8) break;
@@ -54,12 +54,16 @@ AttnPlan attn_plan(int B, int H, int64_t Lq, int64_t kv_len, int64_t q_pos0,
   p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0;
   p.stream = false;
   p.steps_bh = p.total_steps = 0;
-  if (D == 128 && allow_split) {
-    // Balanced split of the dense head_dim-128 kernel: one workgroup per
-    // compute unit, each taking an equal share of all key steps (whole
-    // tiles where the shares line up, parts of a tile where they do not),
-    // so no unit idles while the last query tiles finish.  Segment s (query
-    // rows of chunk c0 + s) sees min(kv_len, (c0 + s + 1) L) keys.
+  // Balanced split of the dense head_dim-128 kernel, for launches whose
+  // query tiles number between half and all of the compute units and whose
+  // tiles are long (at least 192 key tiles): one workgroup per compute unit,
+  // each taking an equal share of all key steps (whole tiles where the
+  // shares line up, parts of a tile where they do not), so no unit idles
+  // while the last tiles finish.  With fewer tiles the uniform split above
+  // (partials merged by a second kernel) serves better, with more tiles or
+  // short ones one workgroup per tile.  Segment s (query rows of chunk
+  // c0 + s) sees min(kv_len, (c0 + s + 1) L) keys.
+  if (D == 128 && allow_split && units * 2 > kSlots && units <= kSlots && min_ktiles >= 192) {
     const int64_t n_seg = 1 + p.n_full + (p.last_rows > 0 ? 1 : 0);
     int64_t steps = 0;
     for (int64_t s = 0; s < n_seg; ++s) {

@@ -42,18 +42,24 @@ def test_rope_table_bytes():
 
 
 def test_workspace_bytes():
-    # head_dim 128: balanced split over G <= 256 workgroups, 1 KB of counters
-    # then two partial slots of 256 rows x (128 + 1) fp32 per workgroup
     slot = 256 * 129 * 4
-    # 480P chunk: 12 x 19 tiles x 512 key steps over 256 workgroups
+    # head_dim 128, 480P chunk: 12 x 19 tiles of 512 key tiles, between half
+    # and all of the 256 compute units -> balanced split over 256
+    # workgroups: 1 KB of counters, two partial slots (256 rows x (128 + 1)
+    # fp32) per workgroup
     assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 32760, 28080, 4680, 128) == \
         1024 + 2 * 256 * slot
-    # one sequence-parallel rank's 585 queries: 12 x 3 tiles x 512 steps, 256 workgroups
+    # one sequence-parallel rank's 585 queries: 36 tiles -> uniform split
+    # into 7 (252 workgroups), partials O fp32 + lse per row and split
     assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680,
-                                                    128) == 1024 + 2 * 256 * slot
-    # one head, 3 tiles: at least 512 / 8 = 64 steps per workgroup -> 24
+                                                    128) == 7 * 12 * 585 * 129 * 4
+    # one head of it: 3 tiles, split into 16
     assert crattn.chunk_causal_attn_workspace_bytes(1, 1, 585, 32760, 28080 + 2925, 4680,
-                                                    128) == 1024 + 2 * 24 * slot
+                                                    128) == 16 * 585 * 129 * 4
+    # short tiles (the first rollout chunk, 74 key tiles): one tile per workgroup
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 12, 4680, 4680, 0, 4680, 128) == 0
+    # more tiles than compute units (720P window): one tile per workgroup
+    assert crattn.chunk_causal_attn_workspace_bytes(1, 40, 10800, 75600, 64800, 10800, 128) == 0
     # head_dim 64: split-KV partials (O fp32 + lse) when the tiles leave the chip idle
     ws = crattn.chunk_causal_attn_workspace_bytes(1, 12, 585, 32760, 28080 + 2925, 4680, 64)
     assert ws > 0 and ws % (12 * 585 * 65 * 4) == 0
@@ -159,17 +165,16 @@ def test_chunk_causal_attn_noalloc_rejects(kw, code):
 
 
 def test_noalloc_scratch_covers_every_shape():
-    # head_dim 128 needs at most 1 KB + 512 slots (the balanced split's
-    # bound, whatever the shape); head_dim 64 splits only small launches
+    # the balanced split needs at most 1 KB + 512 slots whatever the shape;
+    # uniform splits happen only when the tiles fill at most half the chip
     cap = 72 << 20
     for args in [(1, 12, 585, 32760, 28080 + 2925, 4680), (1, 12, 4680, 32760, 28080, 4680),
                  (1, 4, 4096, 65536, 61440, 4096), (2, 40, 10800, 64800, 54000, 10800),
-                 (1, 1, 64, 64, 0, 64), (1, 2, 300, 100000, 99900, 100)]:
+                 (1, 1, 64, 64, 0, 64), (1, 2, 300, 100000, 99900, 100),
+                 (1, 8, 8192, 1 << 20, (1 << 20) - 8192, 8192)]:
         for D in (64, 128):
             need = crattn.chunk_causal_attn_workspace_bytes(*args, D)
             assert 0 <= need <= cap, (args, D, need)
-    assert crattn.chunk_causal_attn_workspace_bytes(2, 40, 10800, 64800, 54000, 10800, 128) == \
-        1024 + 2 * 256 * 256 * 129 * 4
 
 
 def _attn_rope(**kw):

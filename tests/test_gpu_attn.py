@@ -189,25 +189,70 @@ def test_stress_distributions(kind):
     assert_attn_close(f64(out), o_ref, kind)
 
 
-def test_balanced_split_many_parts_all_rows():
-    # one head of the SP slice: 3 query tiles of 512 key steps cut over 24
-    # workgroups of 64 steps, so every tile has 8 or 9 parts merged by the
-    # last to finish; every row against the oracle, and five reruns agree
-    # bit for bit whichever part finishes last
+def test_uniform_split_one_head_all_rows():
+    # one head of the SP slice: 3 query tiles, each key range split 16 ways
+    # and merged by the combine kernel; every row against the oracle, and
+    # five reruns agree bit for bit
     w = SP480
     q = rand_bf16((1, w.lq, 1, w.D), 61)
     kc = rand_bf16((1, 1, w.cap, w.D), 62)
     vc = rand_bf16((1, 1, w.cap, w.D), 63)
     assert crattn.chunk_causal_attn_workspace_bytes(1, 1, w.lq, w.kv_len, w.q_pos0,
-                                                    w.chunk_tokens, w.D) == \
-        1024 + 2 * 24 * 256 * 129 * 4
+                                                    w.chunk_tokens, w.D) == 16 * w.lq * 129 * 4
     out, lse = run_attn(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens)
     o_ref, lse_ref = oracle_rows(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens)
-    assert_attn_close(f64(out), o_ref, "many parts")
+    assert_attn_close(f64(out), o_ref, "16 splits")
     np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3)
     for _ in range(5):
         o2, l2 = run_attn(q, kc, vc, w.kv_len, w.q_pos0, w.chunk_tokens)
         assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+def test_balanced_split_three_parts_all_rows():
+    # 130 query tiles (a little over half the compute units) of 1024 key
+    # tiles: the balanced split cuts each tile into 2 or 3 parts merged by
+    # the last to finish; every row of 2 heads against the oracle, reruns
+    # bit for bit
+    B, H, D, L, Lq, kv_len, q_pos0 = 1, 65, 128, 512, 512, 65536, 65024
+    assert crattn.chunk_causal_attn_workspace_bytes(B, H, Lq, kv_len, q_pos0, L, D) == \
+        1024 + 2 * 256 * 256 * 129 * 4
+    q = rand_bf16((B, Lq, H, D), 64)
+    kc = rand_bf16((B, H, kv_len, D), 65)
+    vc = rand_bf16((B, H, kv_len, D), 66)
+    out, lse = run_attn(q, kc, vc, kv_len, q_pos0, L)
+    heads = [0, 64]
+    o_ref, lse_ref = oracle_rows(q, kc, vc, kv_len, q_pos0, L, heads=heads)
+    assert_attn_close(f64(out[:, :, heads]), o_ref, "balanced split")
+    np.testing.assert_allclose(f64(lse[:, heads]), lse_ref, atol=2e-3)
+    for _ in range(3):
+        o2, l2 = run_attn(q, kc, vc, kv_len, q_pos0, L)
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
+@pytest.mark.parametrize("kind", ["single_jump", "rising_steps", "jump_in_last_tile"])
+def test_score_jumps_take_the_rescale_path(kind):
+    # The key loop keeps the first tile's row maximum until a lane's row sum
+    # passes 2^31; these keys make later scores jump by far more than 31
+    # (base 2), so exact results need the rescale block (without it p would
+    # overflow to inf).  All rows against the oracle, split and unsplit.
+    # chunk 1 of 4083-key chunks: 8166 keys, the final tile holds 38
+    B, H, D, L, Lq, kv_len, q_pos0 = 1, 2, 128, 4083, 300, 8166, 4083
+    q = rand_bf16((B, Lq, H, D), 71)
+    kc = normal((B, H, kv_len, D), 72, torch.float32)
+    vc = rand_bf16((B, H, kv_len, D), 73)
+    if kind == "single_jump":
+        kc[:, :, 3000:3064] *= 40.0
+    elif kind == "rising_steps":
+        for i, t in enumerate(range(1000, 8000, 1500)):
+            kc[:, :, t:t + 64] *= 10.0 * (i + 1)
+    else:  # inside the partial final tile (keys 8128..8165)
+        kc[:, :, 8140:8150] *= 60.0
+    kc = kc.to(torch.bfloat16).to(dev())
+    o_ref, lse_ref = oracle_rows(q, kc, vc, kv_len, q_pos0, L)
+    for use_ws in (True, False):
+        out, lse = run_attn(q, kc, vc, kv_len, q_pos0, L, use_ws=use_ws)
+        assert_attn_close(f64(out), o_ref, f"{kind} ws={use_ws}")
+        np.testing.assert_allclose(f64(lse), lse_ref, atol=2e-3, rtol=1e-6)
 
 
 def test_deterministic_rerun():
