@@ -35,7 +35,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "chunk-causal attn TFLOP/s + ms/chunk (480P, 1.3B shape); % of bf16 MFMA peak"
 COUNTERS = os.path.join(ROOT, "profiles", "attn_step480_hbm_counters.txt")
-ATTN_SRC = os.path.join(ROOT, "autoregressive_video_diffusion_amd", "csrc", "attn.hip")
+_CSRC = os.path.join(ROOT, "autoregressive_video_diffusion_amd", "csrc")
+# the attention's device code: the kernel, its generated key loop, the planner
+ATTN_SRC = tuple(os.path.join(_CSRC, f) for f in ("attn.hip", "attn_loop.inc", "plan.cpp"))
 
 
 def attn_flops(B, H, Lq, visible_keys, D):
@@ -66,7 +68,11 @@ def qkv_bytes(B, n, C, H, D, elt=2):
 
 
 def source_digest(path=ATTN_SRC) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of a source file, or of several in order."""
+    h = hashlib.sha256()
+    for p in (path,) if isinstance(path, str) else path:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel="attn"):
