@@ -997,7 +997,11 @@ __device__ inline FwdTile fwd_locate(const AttnKArgs &a, int64_t x) {
   return t;
 }
 
-template <bool ROPE>
+// Largest key-tile table of the block-sparse instance (own chunk tiles,
+// selected blocks, four padding entries): its LDS beside the ring.
+constexpr int kListMax = 1500;
+
+template <bool ROPE, bool LIST>
 __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
   constexpr int D = 128, kBN = 64;
   constexpr int DK = D / 16, DB = D / 32;
@@ -1078,6 +1082,56 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     if (!first) __syncthreads();
     const int b = ti.b, h = ti.h;
     const int64_t row0 = ti.row0, nrows = ti.nrows;
+
+    // ---- block-sparse instance: the key tiles as a table of (first row,
+    // rows) in LDS: the own chunk's 64-key tiles, then the selected history
+    // blocks in selection order, then four copies of the last entry.  Ids
+    // that are not history blocks (negative, past the visible frames, or in
+    // the own chunk) are dropped, so nothing outside the own chunk and the
+    // history is ever read and no tile is empty.  (One tile per workgroup:
+    // the loop runs once.) ----
+    [[maybe_unused]] uint32_t tab_addr = 0;
+    if constexpr (LIST) {
+      static_assert(CRATTN_HSA_QBLOCK == 256, "one selection row per query tile");
+      static_assert(CRATTN_HSA_KBLOCK == kBN, "a selected block is one key tile");
+      __shared__ int2 tab[kListMax];
+      __shared__ int tab_count[4];
+      const int own_first = (int)((a.q_pos0 / a.L) * a.L);
+      const int n_own = (ti.limit - own_first + kBN - 1) / kBN;
+      for (int i = tid; i < n_own; i += 256)
+        tab[i] = make_int2(own_first + i * kBN, min(kBN, ti.limit - (own_first + i * kBN)));
+      const int32_t *sl = a.sel + (((int64_t)b * a.H + h) * a.n_tiles + w % a.n_tiles) * a.kb;
+      int nsel = 0;
+      for (int i0 = 0; i0 < a.kb; i0 += 256) {
+        const int i = i0 + tid;
+        const int id = i < a.kb ? sl[i] : -1;
+        const bool v = id >= 0 && id < a.vis_blocks && (id < a.own_b0 || id >= a.own_b1);
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(v);
+        const int before = __builtin_popcountll(bal & ((uint64_t(1) << lane) - 1));
+        if (lane == 0) tab_count[wave] = __builtin_popcountll(bal);
+        __syncthreads();
+        int off = n_own + nsel, tot = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          off += w2 < wave ? tab_count[w2] : 0;
+          tot += tab_count[w2];
+        }
+        if (v) {
+          const int f = id / a.nbf, j = id - f * a.nbf;
+          const int start = f * a.blk_frame + j * kBN;
+          tab[off + before] = make_int2(start, min(kBN, a.blk_frame - j * kBN));
+        }
+        nsel += tot;
+        __syncthreads();
+      }
+      const int n = n_own + nsel;
+      if (tid < 4) tab[n + tid] = tab[n - 1];
+      __syncthreads();
+      k0 = 0;
+      k1 = __builtin_amdgcn_readfirstlane(n);
+      tab_addr = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(tab));
+    }
     const int last = k1 - 1;
     const int rem = __builtin_amdgcn_readfirstlane(min(kBN, ti.limit - last * kBN));
 
@@ -1158,7 +1212,8 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
         const int row = cell / pitch, c = cell - row * pitch;
         const uint32_t col = (uint32_t)(c < D / 8 ? c * 16 : 0);
         off[n] = (uint32_t)row * (D * 2) + col;
-        offl[n] = (uint32_t)min(row, rem - 1) * (D * 2) + col;
+        // (the block-sparse instance clamps each ragged tile from the full offsets)
+        offl[n] = LIST ? off[n] : (uint32_t)min(row, rem - 1) * (D * 2) + col;
       }
       for (int n = 0; n < 8; ++n) {
         dma_a[n] = off[n];
@@ -1182,27 +1237,53 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
     int t = k0;
     if (k0 < k1) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile(CRATTN_ATTN_LOOP_ASM
-                   : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
-                     "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
-                     "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t)
-                   : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
-                     "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
-                     "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
-                     "{s71}"(sc), "{s72}"(wb), "{s73}"(k5)
-                   : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
-                     CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5),
-                     CRT_D("v", 6), CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9),
-                     CRT_D("v", 10), CRT_D("v", 11), CRT_D("v", 12), CRT_D("v", 13),
-                     CRT_D("v", 14), CRT_D("v", 15), CRT_D("v", 16), CRT_D("v", 17),
-                     CRT_D("v", 18), "v190", "v191", "v198", "v199", "v200", "v201", "v202",
-                     "v203", "v204", "v205", "v206", "v236", "v237", "v238", "v239", "v240", "v241",
-                     "s74", "s75", "s76", "s77",
-                     "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "m0",
-                     "vcc", "scc", "memory");
-#pragma clang diagnostic pop
+      if constexpr (LIST) {
+    #pragma clang diagnostic push
+    #pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile(CRATTN_ATTN_LOOP_LIST_ASM
+                       : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
+                         "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
+                         "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t)
+                       : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
+                         "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
+                         "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last),
+                         "{s71}"(sc), "{s72}"(wb), "{s73}"(k5), "{s88}"(tab_addr)
+                       : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
+                         CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5),
+                         CRT_D("v", 6), CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9),
+                         CRT_D("v", 10), CRT_D("v", 11), CRT_D("v", 12), CRT_D("v", 13),
+                         CRT_D("v", 14), CRT_D("v", 15), CRT_D("v", 16), CRT_D("v", 17),
+                         CRT_D("v", 18), "v190", "v191", "v198", "v199", "v200", "v201", "v202",
+                         "v203", "v204", "v205", "v206", "v236", "v237", "v238", "v239", "v240", "v241",
+                         "s74", "s75", "s76", "s77",
+                         "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "s89",
+                         "s90", "s91", "s92", "s93", "s94", "s95", "s96", "s97", "v242", "v243",
+                         "v244", "m0",
+                         "vcc", "scc", "memory");
+    #pragma clang diagnostic pop
+      } else {
+    #pragma clang diagnostic push
+    #pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile(CRATTN_ATTN_LOOP_ASM
+                       : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
+                         "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
+                         "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t)
+                       : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
+                         "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
+                         "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
+                         "{s71}"(sc), "{s72}"(wb), "{s73}"(k5)
+                       : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
+                         CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5),
+                         CRT_D("v", 6), CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9),
+                         CRT_D("v", 10), CRT_D("v", 11), CRT_D("v", 12), CRT_D("v", 13),
+                         CRT_D("v", 14), CRT_D("v", 15), CRT_D("v", 16), CRT_D("v", 17),
+                         CRT_D("v", 18), "v190", "v191", "v198", "v199", "v200", "v201", "v202",
+                         "v203", "v204", "v205", "v206", "v236", "v237", "v238", "v239", "v240", "v241",
+                         "s74", "s75", "s76", "s77",
+                         "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87", "m0",
+                         "vcc", "scc", "memory");
+    #pragma clang diagnostic pop
+      }
     }
 
     // ---- this tile's rows: base-2 log-sum-exp and the normalised O ----
@@ -1241,7 +1322,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
 
     bool merge = false;
     int64_t part0 = 0, part1 = 0, a0 = 0;
-    if (k0 != 0 || k1 != ti.nkt) {
+    if (!LIST && (k0 != 0 || k1 != ti.nkt)) {
       // A part of a tile cut between workgroups (balanced split only): the
       // parts are those of workgroups part0 .. part1; a part writes its
       // normalised O and log-sum-exp to its slot (slot 0 of a workgroup for
@@ -1590,7 +1671,16 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
                    : launch_fwd<64, 8, 1, 1, false, false, true>(k, grid, s);
   } else if (a.D == 128) {
     if (a.sel != nullptr) {
-      e = launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s);
+      // block-sparse: the hand-scheduled loop over a table of key tiles when
+      // the own chunk's tiles and the selection fit it
+      const int64_t own_tiles = (a.chunk_tokens + 63) / 64;
+      if (p.splits == 1 && own_tiles + a.sel_kb + 4 <= kListMax) {
+        hipLaunchKernelGGL((attn_fwd64_kernel<false, true>), dim3((unsigned)p.grid), dim3(256), 0,
+                           s, k);
+        e = hipGetLastError();
+      } else {
+        e = launch_fwd<128, 8, 1, 1, false, true>(k, p.grid, s);
+      }
     } else {
       // dense: the kernel with the hand-scheduled key loop
       if (p.stream) {
@@ -1607,9 +1697,9 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
                            (int)p.grid);
       }
       if (a.rope)
-        hipLaunchKernelGGL(attn_fwd64_kernel<true>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+        hipLaunchKernelGGL((attn_fwd64_kernel<true, false>), dim3((unsigned)p.grid), dim3(256), 0, s, k);
       else
-        hipLaunchKernelGGL(attn_fwd64_kernel<false>, dim3((unsigned)p.grid), dim3(256), 0, s, k);
+        hipLaunchKernelGGL((attn_fwd64_kernel<false, false>), dim3((unsigned)p.grid), dim3(256), 0, s, k);
       e = hipGetLastError();
     }
   } else {

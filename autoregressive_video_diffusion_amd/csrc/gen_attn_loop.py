@@ -105,6 +105,20 @@ sKH, sVH, sT, sLAST, sREM, sC, sWB, sK5 = 64, 66, 68, 69, 70, 71, 72, 73
 sTILE, sTV, sKA, sVA, sSB, sSBV, sN0, sT3, sTMP, sLIM = 74, 75, 76, 78, 80, 81, 82, 84, 85, 86
 SUM_LIMIT = 0x4F000000           # 2^31: a lane's row sum above it calls the rescale
 
+# List mode (the block-sparse instance): tile j is the key rows [first_j,
+# first_j + rows_j) from a table of (first row, rows) in LDS (at byte sTAB,
+# padded with four copies of the last entry), not rows [64j, 64j + 64).
+# Entries travel through a queue of four scalar slots (tile j in slot j mod
+# 4), read one step ahead; a ragged tile's copies re-read its last row (its
+# offsets clamped from the full ones kept in VDMAL) and its scores past the
+# valid rows are masked.
+LIST = False
+sTAB, sCL = 88, 89               # table address; bit 0 / 1: K / V copy offsets clamped
+sQK = (90, 91, 92, 93)           # first key row of the tile in each slot
+sQR = (94, 95, 96, 97)           # its valid rows (1..64)
+VTAB = (242, 243)                # the next entry, read a step ahead
+VTA = 244                        # its LDS address
+
 
 def vr(base, n=1):
     return f"v{base}" if n == 1 else f"v[{base}:{base + n - 1}]"
@@ -492,6 +506,32 @@ LAST_EXP = [(8 * c + 6, 8 * c + 14) for c in range(4)]
 FIRST_EXP = [(8 * c, 8 * c + 8) for c in range(4)]
 
 
+def mask_body(buf, rows):
+    """Scores of keys at or past `rows` (a scalar register) -> -inf."""
+    out = [valu(f"v_mov_b32 {vr(VT[7])}, 0xff800000", (f"v{VT[7]}",), ())]
+    for kb in range(2):
+        for r in range(16):
+            key = kb * 32 + 16 * (r // 8) + r % 8
+            t = VT[6]
+            out += [valu(f"v_add_u32 {vr(t)}, {key}, {vr(VKH8)}", (f"v{t}",), (f"v{VKH8}",)),
+                    valu(f"v_cmp_le_i32_e32 vcc, {sr(rows)}, {vr(t)}", ("vcc",), (f"v{t}",))]
+            for qb in range(2):
+                x = S(buf, kb, qb) + r
+                out.append(valu(f"v_cndmask_b32_e32 {vr(x)}, {vr(x)}, {vr(VT[7])}, vcc",
+                                (f"v{x}",), (f"v{x}", f"v{VT[7]}", "vcc")))
+    return out
+
+
+def mask_check(buf, slot, tag):
+    """List mode: branch to a cold mask of S(buf) when the tile in `slot`
+    is ragged.  Returns (hot, cold)."""
+    hot = [salu(f"s_cmp_lt_u32 {sr(sQR[slot])}, {BN}"),
+           branch(f"s_cbranch_scc1 {tag}_mk", f"{tag}_mk"), label(f"{tag}_mkr")]
+    cold = [label(f"{tag}_mk")] + mask_body(buf, sQR[slot]) + \
+        [branch(f"s_branch {tag}_mkr", f"{tag}_mkr")]
+    return hot, cold
+
+
 def mask_tail(buf, tag):
     """Scores of keys at or past the valid count -> -inf (the final tile,
     when it is partial)."""
@@ -529,6 +569,77 @@ def head_cold(tag):
             clamp_offsets(range(5, 10)) + [branch(f"s_branch {tag}_swvr", f"{tag}_swvr")])
 
 
+def tab_read():
+    """List mode: read the next table entry (the address advances first)."""
+    return [valu(f"v_add_u32 {vr(VTA)}, 8, {vr(VTA)}", (f"v{VTA}",), (f"v{VTA}",)),
+            ds_read(f"ds_read_b64 {vr(VTAB[0], 2)}, {vr(VTA)}", vset(VTAB[0], 2))]
+
+
+def tab_take(slot):
+    """List mode: the entry read a step ahead into queue slot `slot` (five
+    wait states before a scalar instruction reads what v_readfirstlane
+    wrote)."""
+    return [valu(f"v_readfirstlane_b32 {sr(sQK[slot])}, {vr(VTAB[0])}", (), (f"v{VTAB[0]}",)),
+            valu(f"v_readfirstlane_b32 {sr(sQR[slot])}, {vr(VTAB[1])}", (), (f"v{VTAB[1]}",)),
+            Ins("s_nop 4", "nop")]
+
+
+def list_bases(slot, kind, stage):
+    base, dst, sb, ring = ((sKH, sKA, sSB, 0) if kind == "k" else
+                           (sVH, sVA, sSBV, V_RING))
+    size = K_STAGE if kind == "k" else V_STAGE
+    return [salu(f"s_lshl_b32 {sr(sTMP)}, {sr(sQK[slot])}, {(2 * D).bit_length() - 1}"),
+            salu(f"s_add_u32 {sr(dst)}, {sr(base)}, {sr(sTMP)}"),
+            salu(f"s_addc_u32 {sr(dst + 1)}, {sr(base + 1)}, 0"),
+            salu(f"s_add_u32 {sr(sb)}, {sr(sWB)}, {ring + stage * size}")]
+
+
+def list_clamp(slots, rows):
+    """Copy offsets of `slots` from the full ones with rows clamped to
+    rows - 1: offset = min(row, rows - 1) * 256 + column."""
+    t, c = VT[6], VT[7]
+    out = [salu(f"s_sub_u32 {sr(sTMP)}, {sr(rows)}, 1")]
+    for i in slots:
+        d, f = VDMA[i], VDMAL[i]
+        out += [valu(f"v_lshrrev_b32 {vr(t)}, 8, {vr(f)}", (f"v{t}",), (f"v{f}",)),
+                valu(f"v_min_u32 {vr(t)}, {sr(sTMP)}, {vr(t)}", (f"v{t}",), (f"v{t}",)),
+                valu(f"v_and_b32 {vr(c)}, 0xff, {vr(f)}", (f"v{c}",), (f"v{f}",)),
+                valu(f"v_lshl_or_b32 {vr(d)}, {vr(t)}, 8, {vr(c)}", (f"v{d}",),
+                     (f"v{t}", f"v{c}"))]
+    return out
+
+
+def list_copy_check(tag, kind, slot):
+    """List mode: the copy offsets of K (bit 0) or V (bit 1) follow the
+    tile in `slot`: clamped when it is ragged, restored after one that
+    was.  Returns (hot, cold)."""
+    bit = 0 if kind == "k" else 1
+    slots = range(5) if kind == "k" else range(5, 10)
+    t = f"{tag}_{kind}"
+    hot = [salu(f"s_cmp_lt_u32 {sr(sQR[slot])}, {BN}"),
+           branch(f"s_cbranch_scc1 {t}c", f"{t}c"),
+           salu(f"s_bitcmp1_b32 {sr(sCL)}, {bit}"),
+           branch(f"s_cbranch_scc1 {t}u", f"{t}u"),
+           label(f"{t}r")]
+    cold = ([label(f"{t}c")] + list_clamp(slots, sQR[slot]) +
+            [salu(f"s_bitset1_b32 {sr(sCL)}, {bit}"), branch(f"s_branch {t}r", f"{t}r"),
+             label(f"{t}u")] + clamp_offsets(slots) +
+            [salu(f"s_bitset0_b32 {sr(sCL)}, {bit}"), branch(f"s_branch {t}r", f"{t}r")])
+    return hot, cold
+
+
+def list_head(tag, phi, kstage, vstage, cur):
+    """List mode step head: take the entry of tile t+3, bases and copy
+    offsets of K(t+3) and V(t+2), mask S(t) if tile t is ragged."""
+    ks, vs, ms = (phi + 3) % NS, (phi + 2) % NS, phi % NS
+    hot = tab_take(ks)
+    kh, kc = list_copy_check(tag, "k", ks)
+    vh, vc = list_copy_check(tag, "v", vs)
+    mh, mc = mask_check(cur, ms, tag)
+    hot += kh + list_bases(ks, "k", kstage) + vh + list_bases(vs, "v", vstage) + mh
+    return hot, kc + vc + mc
+
+
 def end_of_step(n_mf, vstage_next):
     """Before the last two products: every LDS read of the step is back,
     the tiles copied before this step have landed, every wave is past its
@@ -537,6 +648,8 @@ def end_of_step(n_mf, vstage_next):
              (n_mf - 1.4, Ins("s_waitcnt vmcnt(10)", "wait")),
              (n_mf - 1.3, Ins("s_barrier", "barrier"))]
     items += [(n_mf - 1.2 + 0.01 * g, ins) for g in range(2) for ins in v_read(g, vstage_next)]
+    if LIST:   # before the fragment reads, so the next head waits for it alone
+        items += [(n_mf - 1.25 + 0.01 * k, ins) for k, ins in enumerate(tab_read())]
     return items
 
 
@@ -549,14 +662,18 @@ def first_step():
     """t = first tile: S(t+1) = K(t+1) Q^T and the exponentials of S(t);
     no product with V yet."""
     tag = "crt_first"
-    head = [label(tag)] + step_head(tag, 3, 2)
+    if LIST:
+        hh, lcold = list_head(tag, 0, 3, 2, 0)
+        head = [label(tag)] + hh
+    else:
+        head = [label(tag)] + step_head(tag, 3, 2)
     items = k_read_items(1, 0, range(16)) + dma_items(0, 20) + exp_items(0, 0, FIRST_EXP)
     items += end_of_step(32, 0)
     body = place(qk_mfmas(1), items, head)
     tail = sum_check(0, f"{tag}_resc") + [label(f"{tag}_rescr"),
                                          salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1"),
                                          branch("s_branch crt_ph1", "crt_ph1")]
-    cold = head_cold(tag) + rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
+    cold = (lcold if LIST else head_cold(tag)) + rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
     return body + tail, cold
 
 
@@ -568,7 +685,11 @@ def step(phi):
     tag = f"crt_ph{phi}"
     head = [label(tag), salu(f"s_cmp_ge_u32 {sr(sT)}, {sr(sLAST)}"),
             branch(f"s_cbranch_scc1 crt_last{phi}", f"crt_last{phi}")]
-    head += step_head(tag, (phi + 3) % NS, (phi + 2) % NS)
+    if LIST:
+        hh, lcold = list_head(tag, phi, (phi + 3) % NS, (phi + 2) % NS, cur)
+        head += hh
+    else:
+        head += step_head(tag, (phi + 3) % NS, (phi + 2) % NS)
     mf = pv_mfmas() + qk_mfmas(nxt)
     items = v_read_items((phi + 3) % NS, 0, range(2, 16))
     items += k_read_items((phi + 1) % NS, 32, range(16))
@@ -580,7 +701,8 @@ def step(phi):
                                             salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1")]
     if phi == NS - 1:
         tail.append(branch("s_branch crt_ph0", "crt_ph0"))
-    cold = head_cold(tag) + rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
+    cold = (lcold if LIST else head_cold(tag)) + \
+        rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
     return body + tail, cold
 
 
@@ -595,7 +717,12 @@ def last_step(phi):
     exponentials of the (masked) final tile, then its own products."""
     cur, lset = phi % 2, phi % 2
     tag = f"crt_last{phi}"
-    head = [label(tag)] + mask_tail(cur, tag)
+    mcold = []
+    if LIST:
+        mh, mcold = mask_check(cur, phi % NS, tag)
+        head = [label(tag)] + mh
+    else:
+        head = [label(tag)] + mask_tail(cur, tag)
     items = v_read_items((phi + 3) % NS, 0, range(2, 16)) + exp_items(cur, lset, LAST_EXP)
     body = place(pv_mfmas(), items, head)
     tail = sum_check(lset, f"{tag}_resc") + [label(f"{tag}_rescr")]
@@ -606,19 +733,24 @@ def last_step(phi):
                 tail.append(valu(f"v_mov_b32 {vr(d)}, {vr(s_)}", (f"v{d}",), (f"v{s_}",)))
     check_p_war(body, f"last {phi}")
     tail += drain(phi % NS, f"{tag}_drain")
-    cold = rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
+    cold = mcold + rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
     return body + tail, cold
 
 
 def only_step():
     """The first tile is also the last: its exponentials, then its products."""
     tag = "crt_only"
-    body = [label(tag)] + mask_tail(0, tag)
+    mcold = []
+    if LIST:
+        mh, mcold = mask_check(0, 0, tag)
+        body = [label(tag)] + mh
+    else:
+        body = [label(tag)] + mask_tail(0, tag)
     for c in range(4):
         body += exp_chunk(0, c, 0)
     body += sum_check(0, f"{tag}_resc") + [label(f"{tag}_rescr")]
     body += drain(0, f"{tag}_drain")
-    cold = rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
+    cold = mcold + rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
     return body, cold
 
 
@@ -633,8 +765,28 @@ def prologue():
                 out.append(valu(f"v_mov_b32 {vr(r)}, 0", (f"v{r}",), ()))
     # K(t), K(t+1), V(t), K(t+2), V(t+1) (tiles clamped to the last) into
     # K stages 0, 1, 2 and V stages 0, 1
-    for i, (kind, ahead, stage) in enumerate([("k", 0, 0), ("k", 1, 1), ("v", 0, 0),
-                                              ("k", 2, 2), ("v", 1, 1)]):
+    parts = [("k", 0, 0), ("k", 1, 1), ("v", 0, 0), ("k", 2, 2), ("v", 1, 1)]
+    if LIST:
+        # entries 0..2 into slots 0..2, entry 3 left in flight for the first step
+        out.append(valu(f"v_mov_b32 {vr(VTA)}, {sr(sTAB)}", (f"v{VTA}",), ()))
+        for j in range(3):
+            if j:
+                out += tab_read()
+            else:
+                out.append(ds_read(f"ds_read_b64 {vr(VTAB[0], 2)}, {vr(VTA)}", vset(VTAB[0], 2)))
+            out += tab_take(j)
+        out += tab_read()
+        for kind, ahead, stage in parts:
+            slots = range(5) if kind == "k" else range(5, 10)
+            out += list_clamp(slots, sQR[ahead]) + list_bases(ahead, kind, stage)
+            out += dma_k() if kind == "k" else dma_v()
+        # clamped-offset flags after the last K part (tile 2) and V part (tile 1)
+        out += [salu(f"s_cmp_lt_u32 {sr(sQR[2])}, {BN}"),
+                salu(f"s_cselect_b32 {sr(sCL)}, 1, 0"),
+                salu(f"s_cmp_lt_u32 {sr(sQR[1])}, {BN}"),
+                salu(f"s_cselect_b32 {sr(sTMP)}, 2, 0"),
+                salu(f"s_or_b32 {sr(sCL)}, {sr(sCL)}, {sr(sTMP)}")]
+    for i, (kind, ahead, stage) in enumerate(parts if not LIST else []):
         dst = sTILE if kind == "k" else sTV
         out += tile_index(dst, ahead) + [branch(f"s_cbranch_scc0 crt_pro{i}", f"crt_pro{i}")]
         out += clamp_offsets(range(5) if kind == "k" else range(5, 10))
@@ -894,14 +1046,21 @@ def main():
         KR_AHEAD = args.kr_ahead
     if args.vr_ahead is not None:
         VR_AHEAD = args.vr_ahead
-    prog = fix(program())
-    lines = render(prog)
-    text = ("// Generated by gen_attn_loop.py; do not edit.  The key loop of the dense\n"
-            "// chunk-causal attention kernel (head_dim 128) in CDNA4 assembly: one\n"
-            "// string for an asm statement whose registers are fixed by its operands\n"
-            "// and clobbers (see attn.hip).\n"
-            "#define CRATTN_ATTN_LOOP_ASM \\\n" +
-            " \\\n".join(f'  "{ln}\\n"' for ln in lines) + "\n")
+    global LIST
+    text = ("// Generated by gen_attn_loop.py; do not edit.  The key loop of the\n"
+            "// chunk-causal attention kernel (head_dim 128) in CDNA4 assembly, one\n"
+            "// string each for an asm statement whose registers are fixed by its\n"
+            "// operands and clobbers (see attn.hip): consecutive key tiles\n"
+            "// (CRATTN_ATTN_LOOP_ASM) and key tiles from a table of (first row, rows)\n"
+            "// in LDS (CRATTN_ATTN_LOOP_LIST_ASM, the block-sparse instance).\n")
+    progs = {}
+    for LIST, name in ((False, "CRATTN_ATTN_LOOP_ASM"), (True, "CRATTN_ATTN_LOOP_LIST_ASM")):
+        prog = fix(program())
+        progs[name] = prog
+        lines = render(prog)
+        text += (f"#define {name} \\\n" +
+                 " \\\n".join(f'  "{ln}\\n"' for ln in lines) + "\n")
+    prog = progs["CRATTN_ATTN_LOOP_ASM"]
     with open(args.out + ".tmp", "w") as f:
         f.write(text)
     os.replace(args.out + ".tmp", args.out)
