@@ -56,6 +56,7 @@ struct QkvKArgs {
   const float2 *table;
   int64_t cap, cache_pos, n;
   int M, F, f_begin, C, H, D;
+  int fg;  // feature tiles per group of the tile order
   uint32_t per_frame, gw, t0, tok_off;
   TabGeom tg;
 };
@@ -115,13 +116,19 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
   const int fw = wave & 1, tw = wave >> 1;
 
   // workgroups go round-robin over the 8 XCDs; renumber them so that each
-  // XCD gets a contiguous range of tiles, feature tile fastest
+  // XCD gets a contiguous range of tiles.  Tiles are ordered in groups of
+  // fg feature tiles, token tile slowest inside a group, so the tiles an XCD
+  // runs at once form a block of about fg feature tiles by a few token
+  // tiles, and its L2 serves their shared rows of W and X
   const int G = (int)gridDim.x, q8 = G >> 3, r8 = G & 7;
   const int xcd = (int)blockIdx.x & 7;
   const int tile = xcd * q8 + min(xcd, r8) + ((int)blockIdx.x >> 3);
   const int n_ft = (a.F - a.f_begin + kBM - 1) / kBM;
-  const int f0 = a.f_begin + (tile % n_ft) * kBM;
-  const int m0 = (tile / n_ft) * kBN;
+  const int n_tt = (a.M + kBN - 1) / kBN;
+  const int grp = tile / (a.fg * n_tt), in_grp = tile - grp * a.fg * n_tt;
+  const int fg = min(a.fg, n_ft - grp * a.fg);
+  const int f0 = a.f_begin + (grp * a.fg + in_grp % fg) * kBM;
+  const int m0 = (in_grp / fg) * kBN;
 
   // ---- per-lane DMA offsets (bytes from the tile's first row, column 0).
   // LDS row r holds its 8 chunks of 8 C-values (128 bytes) in swizzled
@@ -257,11 +264,18 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
     head[i] = h >= a.H ? h - a.H : h;
   }
   const int n32 = (int)a.n;
+  // the (cos, sin) gathers of all token blocks are issued before any of
+  // them is used, so their latencies overlap
+  float2 cs[TN][TM][4][2];
+  int mrow[TN], bidx[TN], itok[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int m = m0 + tw * 32 * TN + j * 32 + l32;
     const int mc = min(m, a.M - 1);
     const int b = mc / n32, i_tok = mc - b * n32;
+    mrow[j] = m;
+    bidx[j] = b;
+    itok[j] = i_tok;
     const Pos p = decode_pos(a.tok_off + (uint32_t)i_tok, a.per_frame, a.gw, a.t0);
     // per-lane table pointers of the three axes, offset so that entry q of
     // the lane's pair set is ptr[axis][q] (the high half-wave's pairs are 2
@@ -270,7 +284,6 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
                            a.table + a.tg.base_h + p.h * HH - HT + 2 * hf,
                            a.table + a.tg.base_w + p.w * HH - HT - HH + 2 * hf};
     auto axis = [](int q) { return q < HT ? 0 : q < HT + HH ? 1 : 2; };
-    float2 cs[TM][4][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (fw0 + 32 * i >= a.F || part[i] >= 2) continue;
@@ -281,9 +294,13 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
           const int q0 = ((32 * i) % D) / 2 + 4 * g + e;  // pair of the low half-wave
           const int a0 = axis(q0), a1 = axis(q0 + 2);
           const float2 *ptr = a0 == a1 ? ax[a0] : (hf ? ax[a1] : ax[a0]);
-          cs[i][g][e] = ptr[q0];
+          cs[j][i][g][e] = ptr[q0];
         }
     }
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int m = mrow[j], b = bidx[j], i_tok = itok[j];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (fw0 + 32 * i >= a.F) continue;
@@ -297,7 +314,7 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_kernel(QkvKArgs a) {
         if (part[i] < 2) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float2 r = rotate_pair(y[2 * e], y[2 * e + 1], cs[i][g][e]);
+            const float2 r = rotate_pair(y[2 * e], y[2 * e + 1], cs[j][i][g][e]);
             y[2 * e] = r.x;
             y[2 * e + 1] = r.y;
           }
@@ -378,6 +395,9 @@ hipError_t launch_qkv_rope(const QkvArgs &q, hipStream_t s) {
     if (best_cost < 0 || cost < best_cost) best_cost = cost, best_tn = tn;
   }
   const int64_t grid = (int64_t)n_ft * ((a.M + 64 * best_tn - 1) / (64 * best_tn));
+  // 6 feature tiles per group: an XCD's 32 concurrent tiles then cover
+  // about 6 x 5 tiles, near the fewest distinct rows of W and X for 32 tiles
+  a.fg = min(n_ft, 6);
   // ring depth: as many 64-wide stages as fit in LDS (2 or 3)
   const dim3 g((unsigned)grid), blk(kNW * 64);
   if (q.D == 128) {
