@@ -137,6 +137,26 @@ def test_large_token_counts_every_element(B, n, C):
     assert bool((kc[:, :, :pos] == 7.0).all()) and bool((vc[:, :, :pos] == -7.0).all())
 
 
+@pytest.mark.parametrize("B,n,C,H,D,with_q", [
+    (1, 4000, 256, 23, 64, True),    # 4416 features: a ragged last feature tile
+    (2, 3000, 192, 12, 128, False),  # cache update only: 3072 features, 6 C stages
+])
+def test_wide_tiles_every_element(B, n, C, H, D, with_q):
+    # shapes whose 256 x 384 tiles fill the chip in one round while the
+    # narrower tiles need two (the 480P chunk's choice too); every element
+    gh, gw, t0 = 25, 40, 3
+    cap, pos = n + 100, 100
+    x, w = _inputs(B, n, C, H, D, 7000 + n)
+    q, kc, vc = _run(x, w, H, D, cap, pos, t0, 0, gh, gw, with_q=with_q)
+    (qe, ke, ve), (q0, k0), (aq, ak, av) = _expected(x, w, H, D, t0, 0, gh, gw)
+    if with_q:
+        _check(f64(q), qe, aq, q0, C, True, "Q'")
+    _check(f64(kc[:, :, pos:pos + n]).transpose(0, 2, 1, 3), ke, ak, k0, C, True, "K'")
+    _check(f64(vc[:, :, pos:pos + n]).transpose(0, 2, 1, 3), ve, av, ve, C, False, "V")
+    for c, fill in ((kc, 7.0), (vc, -7.0)):
+        assert bool((c[:, :, :pos] == fill).all()) and bool((c[:, :, pos + n:] == fill).all())
+
+
 def test_projection_replays_from_a_hip_graph():
     # the fused projection + rotation + append captured once and replayed:
     # every replay writes the eager call's Q' and cache rows bit for bit,
