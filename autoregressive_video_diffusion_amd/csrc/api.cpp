@@ -672,8 +672,9 @@ size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int n_slots, i
   if (B < 1 || H < 1 || Lq < 1 || Lq > kMaxElems || (D != 64 && D != 128) || splits < 1 ||
       splits > 16 || n_slots < 1 || (double)B * H * n_slots >= 1073741824.0)
     return 0;
-  // the work counter and slot count, the work order, then the split partials
-  const size_t order = ((size_t)B * H * n_slots * 4u + 255u) & ~size_t(255);
+  // the work counter and slot count, the work order (16-byte records), then
+  // the split partials
+  const size_t order = ((size_t)B * H * n_slots * 16u + 255u) & ~size_t(255);
   return 256u + order +
          (splits > 1 ? (size_t)splits * (size_t)B * H * Lq * (size_t)(D + 1) * 4u : 0);
 }

@@ -89,7 +89,7 @@ struct AttnKArgs {
   int stream;
   int64_t steps_bh, total_steps;
   unsigned *counters;  // per workgroup: parts of the tile it ends in that are done
-  const int32_t *order;      // (b, h, slot) of the non-empty slots, costliest first
+  const int4 *order;         // work records (list, first row, rows, keys), costliest first
   const int32_t *n_real;     // their number
 };
 
@@ -243,8 +243,13 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   int64_t bid = item;
   const int split = (int)(bid % a.splits);
   bid /= a.splits;
-  if constexpr (GATHER)  // (b, h, slot), costliest first
-    bid = __builtin_amdgcn_readfirstlane(a.order[bid]);
+  [[maybe_unused]] int4 rec = make_int4(0, 0, 0, 0);
+  if constexpr (GATHER) {  // the work record: (b, h, query cluster), rows, keys
+    const int4 rv = a.order[bid];
+    rec = make_int4(__builtin_amdgcn_readfirstlane(rv.x), __builtin_amdgcn_readfirstlane(rv.y),
+                    __builtin_amdgcn_readfirstlane(rv.z), __builtin_amdgcn_readfirstlane(rv.w));
+    bid = (rec.x / a.cq) * a.n_tiles;
+  }
   const int64_t tile = bid % a.n_tiles;
   bid /= a.n_tiles;
   const int h = (int)(bid % a.H);
@@ -260,23 +265,12 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
   [[maybe_unused]] const int32_t *g_qperm = nullptr;
   if constexpr (GATHER) {
     static_assert(BM == CRATTN_SVG2_QTILE, "a query tile of the plan is one workgroup's rows");
-    // an empty (or out of range) slot runs with no rows and no keys
-    // (loads inside the persistent loop are not known to be uniform: the
-    // values are made wave-uniform explicitly)
+    // (gather_order_kernel checked the slot and clamped the list length)
     const int64_t bhi = (int64_t)b * a.H + h;
-    const int4 sv = reinterpret_cast<const int4 *>(a.gslots)[bhi * a.n_tiles + tile];
-    const int4 sl = make_int4(__builtin_amdgcn_readfirstlane(sv.x),
-                              __builtin_amdgcn_readfirstlane(sv.y),
-                              __builtin_amdgcn_readfirstlane(sv.z), 0);
-    const bool ok = !(sl.y <= 0 || sl.y > BM || sl.x < 0 || (int64_t)sl.x + sl.y > a.Lq ||
-                      sl.z < 0 || sl.z >= a.cq);
-    row0 = ok ? sl.x : 0;
-    nrows = ok ? sl.y : 0;
-    const int64_t li = bhi * a.cq + (ok ? sl.z : 0);
-    limit = ok ? (int)min((int64_t)max(__builtin_amdgcn_readfirstlane(a.list_len[li]), 0),
-                          a.list_cap)
-               : 0;
-    g_list = a.lists + li * a.list_cap;
+    row0 = rec.y;
+    nrows = rec.z;
+    limit = rec.w;
+    g_list = a.lists + (int64_t)rec.x * a.list_cap;
     g_qperm = a.q_perm + bhi * a.Lq;
   } else {
   int64_t seg, t_in, seg_row0, seg_rows;
@@ -922,6 +916,7 @@ __global__ void __launch_bounds__(NW * 64, MINB) attn_fwd_kernel(AttnKArgs a) {
 // stores.
 typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 typedef float f32x32_t __attribute__((ext_vector_type(32)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -1001,8 +996,9 @@ __device__ inline FwdTile fwd_locate(const AttnKArgs &a, int64_t x) {
 // selected blocks, four padding entries): its LDS beside the ring.
 constexpr int kListMax = 1500;
 
-template <bool ROPE, bool LIST>
+template <bool ROPE, bool LIST, bool GATHER = false>
 __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
+  static_assert(!(GATHER && (ROPE || LIST)), "one instance kind at a time");
   constexpr int D = 128, kBN = 64;
   constexpr int DK = D / 16, DB = D / 32;
   constexpr int KP = Pitch<D>::K, VP = Pitch<D>::V;
@@ -1059,10 +1055,49 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
   const float sc = a.scale_log2;
 
   int64_t x_end = s_hi;
+  // Gather instance: persistent, one workgroup per compute unit taking work
+  // items (a query tile of one query cluster, one key split of its list) in
+  // the cost order of gather_order_kernel from a device counter.
+  [[maybe_unused]] __shared__ int64_t next_item;
+  [[maybe_unused]] int64_t n_items = 0, item = blockIdx.x;
+  [[maybe_unused]] const int32_t *g_list = nullptr;
+  [[maybe_unused]] const int32_t *g_qperm = nullptr;
+  [[maybe_unused]] int g_split = 0;
+  if constexpr (GATHER)
+    n_items = (int64_t)__builtin_amdgcn_readfirstlane(*a.n_real) * a.splits;
   for (bool first = true;; first = false) {
     FwdTile ti;
     int k0, k1;
-    if (!a.stream) {
+    if constexpr (GATHER) {
+      if (!first) {
+        // every wavefront is done with this item's LDS (and with next_item)
+        // before the next item is taken (taking it earlier, to hide the
+        // counter's latency, holds cheap items back from idle workgroups at
+        // the end: measured slower)
+        __syncthreads();
+        if (tid == 0) next_item = (int64_t)atomicAdd(a.work, 1ull);
+        __syncthreads();
+        item = (int64_t)__builtin_amdgcn_readfirstlane((int)min(next_item, (int64_t)0x7fffffff));
+      }
+      if (item >= n_items) break;
+      g_split = (int)(item % a.splits);
+      // the work record (gather_order_kernel checked the slot and clamped
+      // the list length): list (b, h, query cluster), first row, rows, keys
+      const int4 rv = a.order[item / a.splits];
+      const int li = __builtin_amdgcn_readfirstlane(rv.x);
+      const int64_t bh = li / a.cq;
+      ti.b = (int)(bh / a.H);
+      ti.h = (int)(bh % a.H);
+      ti.row0 = __builtin_amdgcn_readfirstlane(rv.y);
+      ti.nrows = __builtin_amdgcn_readfirstlane(rv.z);
+      ti.limit = __builtin_amdgcn_readfirstlane(rv.w);
+      ti.nkt = (ti.limit + kBN - 1) / kBN;
+      ti.pos0 = 0;
+      g_list = a.lists + (int64_t)li * a.list_cap;
+      g_qperm = a.q_perm + bh * a.Lq;
+      k0 = g_split * ti.nkt / a.splits;
+      k1 = (g_split + 1) * ti.nkt / a.splits;
+    } else if (!a.stream) {
       // one tile per workgroup, or one of its uniform key splits
       if (!first) break;
       ti = fwd_tile(a, w / a.splits);
@@ -1079,7 +1114,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     k1 = __builtin_amdgcn_readfirstlane(k1);
     // every wavefront is done with the previous tile's LDS before this
     // tile's copies start
-    if (!first) __syncthreads();
+    if (!GATHER && !first) __syncthreads();
     const int b = ti.b, h = ti.h;
     const int64_t row0 = ti.row0, nrows = ti.nrows;
 
@@ -1138,11 +1173,18 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     // ---- this wavefront's 64 queries as B operands (Q in registers) ----
     const int64_t wrow0 = row0 + (int64_t)wave * 64;
     bf16x8_t qf[2][DK];
+    // (gather instance) the queries' rows in memory, kept for the stores
+    [[maybe_unused]] int32_t g_mrow[2] = {0, 0};
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const int64_t row = wrow0 + qb * 32 + l32;
       const bool ok = row < row0 + nrows;
-      const uint16_t *qp = a.q + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 8;
+      int64_t mrow = row;
+      if constexpr (GATHER) {
+        mrow = ok ? min((uint32_t)g_qperm[row], (uint32_t)(a.Lq - 1)) : 0;
+        g_mrow[qb] = (int32_t)mrow;
+      }
+      const uint16_t *qp = a.q + (((int64_t)b * a.Lq + mrow) * a.H + h) * D + hf * 8;
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         uint4 x = make_uint4(0, 0, 0, 0);
@@ -1200,6 +1242,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     // key of the final tile ----
     u32x8_t dma_a, dmal_a;
     u32x2_t dma_b, dmal_b;
+    [[maybe_unused]] u32x3_t gcol = {0u, 0u, 0u};
     {
       uint32_t off[10], offl[10];
 #pragma unroll
@@ -1212,8 +1255,12 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
         const int row = cell / pitch, c = cell - row * pitch;
         const uint32_t col = (uint32_t)(c < D / 8 ? c * 16 : 0);
         off[n] = (uint32_t)row * (D * 2) + col;
-        // (the block-sparse instance clamps each ragged tile from the full offsets)
-        offl[n] = LIST ? off[n] : (uint32_t)min(row, rem - 1) * (D * 2) + col;
+        // (the block-sparse instance clamps each ragged tile from the full
+        // offsets; the gather instance takes the lane's row index with
+        // ds_bpermute from lane `row` and or-s the column bytes in)
+        offl[n] = LIST ? off[n] : GATHER ? (uint32_t)row * 4u
+                                         : (uint32_t)min(row, rem - 1) * (D * 2) + col;
+        if constexpr (GATHER) gcol[n / 4] |= col << (8 * (n % 4));
       }
       for (int n = 0; n < 8; ++n) {
         dma_a[n] = off[n];
@@ -1237,7 +1284,44 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
     f32x4_t l4 = {0.f, 0.f, 0.f, 0.f};
     int t = k0;
     if (k0 < k1) {
-      if constexpr (LIST) {
+      if constexpr (GATHER) {
+        const uint32_t lane4 = (uint32_t)lane * 4u;
+        const uint32_t capm1 = (uint32_t)(a.cap - 1);
+        // row indices of tiles k0 .. k0+3 (clamped to the last tile; lanes
+        // past its rows read its last row), loaded here so that their
+        // latency passes beside the query loads
+        int32_t gi[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int tj = min(k0 + j, last);
+          const int rl = tj == last ? rem - 1 : kBN - 1;
+          gi[j] = g_list[(int64_t)tj * kBN + min(lane, rl)];
+        }
+    #pragma clang diagnostic push
+    #pragma clang diagnostic ignored "-Winline-asm"
+          asm volatile(CRATTN_ATTN_LOOP_GATHER_ASM
+                       : "+{a[0:31]}"(o[0]), "+{a[32:63]}"(o[1]), "+{a[64:95]}"(o[2]),
+                         "+{a[96:127]}"(o[3]), "={v[192:193]}"(m2), "={v[194:197]}"(l4),
+                         "+{v[208:215]}"(dma_a), "+{v[216:217]}"(dma_b), "+{s68}"(t),
+                         "+{v242}"(gi[0]), "+{v243}"(gi[1]), "+{v244}"(gi[2]), "+{v245}"(gi[3])
+                       : "{a[128:159]}"(qa[0]), "{a[160:191]}"(qa[1]), "{v[218:225]}"(dmal_a),
+                         "{v[226:227]}"(dmal_b), "{v[228:235]}"(bases), "{v207}"(kh8),
+                         "{s[64:65]}"(kh), "{s[66:67]}"(vh), "{s69}"(last), "{s70}"(rem),
+                         "{s71}"(sc), "{s72}"(wb), "{s73}"(k5), "{s[88:89]}"(g_list),
+                         "{s95}"(capm1), "{v246}"(lane4), "{v[248:250]}"(gcol)
+                       : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", CRT_D("v", 1),
+                         CRT_D("v", 2), CRT_D("v", 3), CRT_D("v", 4), CRT_D("v", 5),
+                         CRT_D("v", 6), CRT_D("v", 7), CRT_D("v", 8), CRT_D("v", 9),
+                         CRT_D("v", 10), CRT_D("v", 11), CRT_D("v", 12), CRT_D("v", 13),
+                         CRT_D("v", 14), CRT_D("v", 15), CRT_D("v", 16), CRT_D("v", 17),
+                         CRT_D("v", 18), "v190", "v191", "v198", "v199", "v200", "v201", "v202",
+                         "v203", "v204", "v205", "v206", "v236", "v237", "v238", "v239", "v240", "v241",
+                         "s74", "s75", "s76", "s77",
+                         "s78", "s79", "s80", "s81", "s82", "s83", "s84", "s85", "s86", "s87",
+                         "s90", "s91", "s92", "s93", "s94", "v247",
+                         "m0", "vcc", "scc", "memory");
+    #pragma clang diagnostic pop
+      } else if constexpr (LIST) {
     #pragma clang diagnostic push
     #pragma clang diagnostic ignored "-Winline-asm"
           asm volatile(CRATTN_ATTN_LOOP_LIST_ASM
@@ -1298,13 +1382,16 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
 
     if (a.splits > 1) {
       // uniform split: the partial (normalised O, base-2 log-sum-exp) of
-      // this key range, merged by attn_combine_kernel
-      const int64_t split = w % a.splits;
+      // this key range, merged by attn_combine_kernel (gather instance: at
+      // the query's own row)
+      const int64_t split = GATHER ? g_split : w % a.splits;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int r = trow0 + qb * 32;
         if (r >= nrows) continue;
-        const int64_t prow = ((split * a.B + b) * a.H + h) * a.Lq + row0 + r;
+        int64_t orow = row0 + r;
+        if constexpr (GATHER) orow = g_mrow[qb];
+        const int64_t prow = ((split * a.B + b) * a.H + h) * a.Lq + orow;
         float *op = a.ws_o + prow * D + hf * 4;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -1322,7 +1409,7 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
 
     bool merge = false;
     int64_t part0 = 0, part1 = 0, a0 = 0;
-    if (!LIST && (k0 != 0 || k1 != ti.nkt)) {
+    if (!LIST && !GATHER && (k0 != 0 || k1 != ti.nkt)) {
       // A part of a tile cut between workgroups (balanced split only): the
       // parts are those of workgroups part0 .. part1; a part writes its
       // normalised O and log-sum-exp to its slot (slot 0 of a workgroup for
@@ -1428,7 +1515,8 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
         scl = wsum > 0.f ? 1.0f / wsum : 0.f;
         lse_f = wsum > 0.f ? mx + __log2f(wsum) : -INFINITY;
       }
-      const int64_t row = row0 + r;
+      int64_t row = row0 + r;
+      if constexpr (GATHER) row = g_mrow[qb];
       uint16_t *op = a.out + (((int64_t)b * a.Lq + row) * a.H + h) * D + hf * 4;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -1496,10 +1584,12 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   if (c4 == 0 && a.lse != nullptr) a.lse[r] = (mx + __log2f(wsum)) * kLn2;
 }
 
-// Work order of the gather instance: the (b, h, slot) entries with rows,
-// by decreasing key-tile count (a counting sort over 2048 cost bins; the
-// order inside a bin is whatever the atomics give, which changes no
-// result), so the persistent workgroups take the longest tiles first.
+// Work order of the gather instance: a record per (b, h, slot) entry with
+// rows -- its key list, first row, rows and key count, so a workgroup finds
+// its work in one load -- by decreasing key-tile count (a counting sort over
+// 2048 cost bins; the order inside a bin is whatever the atomics give, which
+// changes no result), so the persistent workgroups take the longest tiles
+// first.
 constexpr int kCostBins = 2048;
 
 // It also starts the work counter at the persistent grid's size.
@@ -1511,16 +1601,24 @@ __global__ void __launch_bounds__(1024) gather_order_kernel(AttnKArgs a, int n_e
   if (tid == 0) *a.work = grid;
   for (int c = tid; c < kCostBins; c += 1024) hist[c] = 0;
   __syncthreads();
-  // bin (kCostBins - 1 - tiles) of entry e, or -1 without rows
-  auto bin_of = [&](int e) {
+  // the work record of entry e -- list (b, h, query cluster), first row,
+  // rows, keys (the list length clamped to the capacity) -- or one with no
+  // rows for a slot that is empty or out of range
+  auto rec_of = [&](int e) {
     const int4 sl = reinterpret_cast<const int4 *>(a.gslots)[e];
-    if (sl.y <= 0 || sl.z < 0 || sl.z >= a.cq) return -1;
-    const int64_t bh = e / a.n_tiles;
-    const int len = min(max(a.list_len[bh * a.cq + sl.z], 0), (int)a.list_cap);
-    return kCostBins - 1 - min((len + 63) / 64, kCostBins - 1);
+    if (sl.y <= 0 || sl.y > CRATTN_SVG2_QTILE || sl.x < 0 || (int64_t)sl.x + sl.y > a.Lq ||
+        sl.z < 0 || sl.z >= a.cq)
+      return make_int4(0, 0, 0, 0);
+    const int64_t li = e / a.n_tiles * a.cq + sl.z;
+    const int len = min(max(a.list_len[li], 0), (int)a.list_cap);
+    return make_int4((int)li, sl.x, sl.y, len);
+  };
+  // bin (kCostBins - 1 - tiles) of a record, or -1 without rows
+  auto bin_of = [&](int4 r) {
+    return r.z <= 0 ? -1 : kCostBins - 1 - min((r.w + 63) / 64, kCostBins - 1);
   };
   for (int e = tid; e < n_entries; e += 1024) {
-    const int b = bin_of(e);
+    const int b = bin_of(rec_of(e));
     if (b >= 0) atomicAdd(&hist[b], 1);
   }
   __syncthreads();
@@ -1541,10 +1639,11 @@ __global__ void __launch_bounds__(1024) gather_order_kernel(AttnKArgs a, int n_e
   hist[2 * tid + 1] = base + h0;
   if (tid == 1023) *const_cast<int32_t *>(a.n_real) = base + h0 + h1;
   __syncthreads();
-  int32_t *order = const_cast<int32_t *>(a.order);
+  int4 *order = const_cast<int4 *>(a.order);
   for (int e = tid; e < n_entries; e += 1024) {
-    const int b = bin_of(e);
-    if (b >= 0) order[atomicAdd(&hist[b], 1)] = e;
+    const int4 r = rec_of(e);
+    const int b = bin_of(r);
+    if (b >= 0) order[atomicAdd(&hist[b], 1)] = r;
   }
 }
 
@@ -1656,10 +1755,10 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
     // partials
     char *ws = static_cast<char *>(a.workspace);
     const int64_t n_entries = (int64_t)a.B * a.H * p.n_tiles;
-    const size_t order_bytes = ((size_t)n_entries * 4u + 255u) & ~size_t(255);
+    const size_t order_bytes = ((size_t)n_entries * 16u + 255u) & ~size_t(255);
     k.work = reinterpret_cast<unsigned long long *>(ws);
     k.n_real = reinterpret_cast<const int32_t *>(ws + 8);
-    k.order = reinterpret_cast<const int32_t *>(ws + 256);
+    k.order = reinterpret_cast<const int4 *>(ws + 256);
     if (p.splits > 1) {
       k.ws_o = reinterpret_cast<float *>(ws + 256 + order_bytes);
       k.ws_lse = reinterpret_cast<float *>(ws + 256 + order_bytes + o_bytes);
@@ -1667,8 +1766,14 @@ hipError_t launch_attn(const AttnArgs &a, const AttnPlan &p, hipStream_t s) {
     const int64_t grid = std::min<int64_t>(p.grid, device_cu_count());
     hipLaunchKernelGGL(gather_order_kernel, dim3(1), dim3(1024), 0, s, k, (int)n_entries,
                        (unsigned long long)grid);
-    e = a.D == 128 ? launch_fwd<128, 8, 1, 1, false, false, true>(k, grid, s)
-                   : launch_fwd<64, 8, 1, 1, false, false, true>(k, grid, s);
+    if (a.D == 128) {
+      // the kernel with the hand-scheduled key loop, in its gather form
+      hipLaunchKernelGGL((attn_fwd64_kernel<false, false, true>), dim3((unsigned)grid), dim3(256),
+                         0, s, k);
+      e = hipGetLastError();
+    } else {
+      e = launch_fwd<64, 8, 1, 1, false, false, true>(k, grid, s);
+    }
   } else if (a.D == 128) {
     if (a.sel != nullptr) {
       // block-sparse: the hand-scheduled loop over a table of key tiles when

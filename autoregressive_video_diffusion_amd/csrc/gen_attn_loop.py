@@ -119,6 +119,23 @@ sQR = (94, 95, 96, 97)           # its valid rows (1..64)
 VTAB = (242, 243)                # the next entry, read a step ahead
 VTA = 244                        # its LDS address
 
+# Gather mode (the semantic-permutation instance): tile j is key rows
+# list[64j .. 64j + 63] of a list of row indices in global memory, not rows
+# [64j, 64j + 64).  Each step loads the 64 indices of tile t+4 (one per
+# lane, lanes past a short final tile clamped to its last entry) into
+# VIDX[(j - first) mod 4]; a loaded vector is shifted to byte offsets
+# (x 256) once, and a copy slot's per-lane offset is the index of the
+# lane's row, fetched across lanes with ds_bpermute_b32 (address VDMAL[n]
+# = row * 4), or-ed with the lane's column bytes (byte n % 4 of VCOL[n / 4]).
+GATHER = False
+VIDX = (242, 243, 244, 245)      # index vectors of four consecutive tiles
+VLANE4 = 246                     # lane * 4
+VGT = 247                        # address of the index load
+VCOL = (248, 249, 250)           # column bytes of the ten copy slots
+sLST, sLA, sILIM, sTL, sRL4 = 88, 90, 92, 93, 94   # list base, load address, lane clamp,
+                                                     # loaded tile, (rows of last - 1) * 4
+sCAPM1 = 95                      # last row of the cache: indices are clamped to it
+
 
 def vr(base, n=1):
     return f"v{base}" if n == 1 else f"v[{base}:{base + n - 1}]"
@@ -640,6 +657,60 @@ def list_head(tag, phi, kstage, vstage, cur):
     return hot, kc + vc + mc
 
 
+def gather_load(ahead, slot):
+    """Gather mode: load the indices of tile min(t + ahead, last) into
+    VIDX[slot], lanes past a short final tile clamped to its last row."""
+    return tile_index(sTL, ahead) + [
+        salu(f"s_cselect_b32 {sr(sILIM)}, {sr(sRL4)}, 0xfc"),   # (SCC: the last tile)
+        salu(f"s_lshl_b32 {sr(sTMP)}, {sr(sTL)}, 8"),
+        salu(f"s_add_u32 {sr(sLA)}, {sr(sLST)}, {sr(sTMP)}"),
+        salu(f"s_addc_u32 {sr(sLA + 1)}, {sr(sLST + 1)}, 0"),
+        valu(f"v_min_u32 {vr(VGT)}, {sr(sILIM)}, {vr(VLANE4)}", (f"v{VGT}",), (f"v{VLANE4}",)),
+        Ins(f"global_load_dword {vr(VIDX[slot])}, {vr(VGT)}, {sr(sLA, 2)}", "vmem",
+            (f"v{VIDX[slot]}",), (f"v{VGT}",))]
+
+
+def gather_shift(slot):
+    """Indices clamped to the cache's rows, then to byte offsets of rows."""
+    x = vr(VIDX[slot])
+    return [valu(f"v_min_u32 {x}, {sr(sCAPM1)}, {x}", (f"v{VIDX[slot]}",), (f"v{VIDX[slot]}",)),
+            valu(f"v_lshlrev_b32 {x}, 8, {x}", (f"v{VIDX[slot]}",), (f"v{VIDX[slot]}",))]
+
+
+def gather_offsets(slots, src):
+    """Per-lane copy offsets of `slots` from the shifted index vector
+    VIDX[src]: (bpermute, or) pairs, one pair per slot."""
+    out = []
+    for n in slots:
+        out.append([ds_read(f"ds_bpermute_b32 {vr(VDMA[n])}, {vr(VDMAL[n])}, {vr(VIDX[src])}",
+                            (f"v{VDMA[n]}",)),
+                    valu(f"v_or_b32_sdwa {vr(VDMA[n])}, {vr(VDMA[n])}, {vr(VCOL[n // 4])} "
+                         f"dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD "
+                         f"src1_sel:BYTE_{n % 4}", (f"v{VDMA[n]}",),
+                         (f"v{VDMA[n]}", f"v{VCOL[n // 4]}"))])
+    return out
+
+
+def gather_head(tag, phi, kstage, vstage):
+    """Gather mode step head: the index load of tile t+4 (first of the
+    step's vector-memory operations, so the step's closing vmcnt wait covers
+    it), the shift of tile t+3's indices, the stage bases of K(t+3) and
+    V(t+2).  The copy offsets follow as items (gather_items)."""
+    return (gather_load(4, phi % NS) + gather_shift((phi + 3) % NS) +
+            [salu(f"s_add_u32 {sr(sSB)}, {sr(sWB)}, {kstage * K_STAGE}"),
+             salu(f"s_add_u32 {sr(sSBV)}, {sr(sWB)}, {V_RING + vstage * V_STAGE}")])
+
+
+def gather_items(phi, lo):
+    """The offsets of copy slot n placed two gaps before its copy (dma_items
+    puts copy n at gap lo + 2n)."""
+    items = []
+    pairs = gather_offsets(range(5), (phi + 3) % NS) + gather_offsets(range(5, 10), (phi + 2) % NS)
+    for n, (bp, orr) in enumerate(pairs):
+        items += [(max(lo - 1, lo + 2 * n - 2) - 0.5, bp), (lo + 2 * n - 0.2, orr)]
+    return items
+
+
 def end_of_step(n_mf, vstage_next):
     """Before the last two products: every LDS read of the step is back,
     the tiles copied before this step have landed, every wave is past its
@@ -665,15 +736,20 @@ def first_step():
     if LIST:
         hh, lcold = list_head(tag, 0, 3, 2, 0)
         head = [label(tag)] + hh
+    elif GATHER:
+        head = [label(tag)] + gather_head(tag, 0, 3, 2)
     else:
         head = [label(tag)] + step_head(tag, 3, 2)
     items = k_read_items(1, 0, range(16)) + dma_items(0, 20) + exp_items(0, 0, FIRST_EXP)
+    if GATHER:
+        items += gather_items(0, 0)
     items += end_of_step(32, 0)
     body = place(qk_mfmas(1), items, head)
     tail = sum_check(0, f"{tag}_resc") + [label(f"{tag}_rescr"),
                                          salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1"),
                                          branch("s_branch crt_ph1", "crt_ph1")]
-    cold = (lcold if LIST else head_cold(tag)) + rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
+    cold = (lcold if LIST else [] if GATHER else head_cold(tag)) + \
+        rescale_block(0, 0, f"{tag}_resc", f"{tag}_rescr")
     return body + tail, cold
 
 
@@ -688,12 +764,16 @@ def step(phi):
     if LIST:
         hh, lcold = list_head(tag, phi, (phi + 3) % NS, (phi + 2) % NS, cur)
         head += hh
+    elif GATHER:
+        head += gather_head(tag, phi, (phi + 3) % NS, (phi + 2) % NS)
     else:
         head += step_head(tag, (phi + 3) % NS, (phi + 2) % NS)
     mf = pv_mfmas() + qk_mfmas(nxt)
     items = v_read_items((phi + 3) % NS, 0, range(2, 16))
     items += k_read_items((phi + 1) % NS, 32, range(16))
     items += dma_items(1, 21)
+    if GATHER:
+        items += gather_items(phi, 1)
     items += exp_items(cur, lset, MID_EXP)
     items += end_of_step(64, phi % NS)
     body = place(mf, items, head)
@@ -701,7 +781,7 @@ def step(phi):
                                             salu(f"s_add_u32 {sr(sT)}, {sr(sT)}, 1")]
     if phi == NS - 1:
         tail.append(branch("s_branch crt_ph0", "crt_ph0"))
-    cold = (lcold if LIST else head_cold(tag)) + \
+    cold = (lcold if LIST else [] if GATHER else head_cold(tag)) + \
         rescale_block(cur, lset, f"{tag}_resc", f"{tag}_rescr")
     return body + tail, cold
 
@@ -786,7 +866,28 @@ def prologue():
                 salu(f"s_cmp_lt_u32 {sr(sQR[1])}, {BN}"),
                 salu(f"s_cselect_b32 {sr(sTMP)}, 2, 0"),
                 salu(f"s_or_b32 {sr(sCL)}, {sr(sCL)}, {sr(sTMP)}")]
-    for i, (kind, ahead, stage) in enumerate(parts if not LIST else []):
+    if GATHER:
+        # the copies read rows through their own offsets from the head bases;
+        # the indices of tiles t .. t+2 shifted (t+3 is left for the first step)
+        out += [salu(f"s_mov_b64 {sr(sKA, 2)}, {sr(sKH, 2)}"),
+                salu(f"s_mov_b64 {sr(sVA, 2)}, {sr(sVH, 2)}"),
+                salu(f"s_sub_u32 {sr(sRL4)}, {sr(sREM)}, 1"),
+                salu(f"s_lshl_b32 {sr(sRL4)}, {sr(sRL4)}, 2")]
+        # (the kernel loads the indices of tiles t .. t+3 into VIDX before
+        # the loop, beside the queries)
+        for j in range(3):
+            out += gather_shift(j)
+        for kind, ahead, stage in parts:
+            slots = range(5) if kind == "k" else range(5, 10)
+            pairs = gather_offsets(slots, ahead)
+            out += [bp for bp, _ in pairs] + [orr for _, orr in pairs]
+            if kind == "k":
+                out.append(salu(f"s_add_u32 {sr(sSB)}, {sr(sWB)}, {stage * K_STAGE}"))
+                out += dma_k()
+            else:
+                out.append(salu(f"s_add_u32 {sr(sSBV)}, {sr(sWB)}, {V_RING + stage * V_STAGE}"))
+                out += dma_v()
+    for i, (kind, ahead, stage) in enumerate(parts if not (LIST or GATHER) else []):
         dst = sTILE if kind == "k" else sTV
         out += tile_index(dst, ahead) + [branch(f"s_cbranch_scc0 crt_pro{i}", f"crt_pro{i}")]
         out += clamp_offsets(range(5) if kind == "k" else range(5, 10))
@@ -1046,15 +1147,19 @@ def main():
         KR_AHEAD = args.kr_ahead
     if args.vr_ahead is not None:
         VR_AHEAD = args.vr_ahead
-    global LIST
+    global LIST, GATHER
     text = ("// Generated by gen_attn_loop.py; do not edit.  The key loop of the\n"
             "// chunk-causal attention kernel (head_dim 128) in CDNA4 assembly, one\n"
             "// string each for an asm statement whose registers are fixed by its\n"
             "// operands and clobbers (see attn.hip): consecutive key tiles\n"
-            "// (CRATTN_ATTN_LOOP_ASM) and key tiles from a table of (first row, rows)\n"
-            "// in LDS (CRATTN_ATTN_LOOP_LIST_ASM, the block-sparse instance).\n")
+            "// (CRATTN_ATTN_LOOP_ASM), key tiles from a table of (first row, rows)\n"
+            "// in LDS (CRATTN_ATTN_LOOP_LIST_ASM, the block-sparse instance) and key\n"
+            "// rows from a list of row indices (CRATTN_ATTN_LOOP_GATHER_ASM, the\n"
+            "// semantic-permutation instance).\n")
     progs = {}
-    for LIST, name in ((False, "CRATTN_ATTN_LOOP_ASM"), (True, "CRATTN_ATTN_LOOP_LIST_ASM")):
+    for LIST, GATHER, name in ((False, False, "CRATTN_ATTN_LOOP_ASM"),
+                               (True, False, "CRATTN_ATTN_LOOP_LIST_ASM"),
+                               (False, True, "CRATTN_ATTN_LOOP_GATHER_ASM")):
         prog = fix(program())
         progs[name] = prog
         lines = render(prog)

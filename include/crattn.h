@@ -487,8 +487,8 @@ int svg2_plan(const float *q_cent, const int32_t *q_off, const float *k_cent,
 
 /* Workspace bytes of svg2_attn with n_slots query tiles per head and
  * `splits` key-range splits: 256 (the work counter of its persistent
- * launch), the work order (4 bytes per slot, rounded up to 256) and the
- * split partials; 0 for invalid arguments. */
+ * launch), the work order (a 16-byte record per slot, rounded up to 256)
+ * and the split partials; 0 for invalid arguments. */
 size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int n_slots, int splits);
 
 /*
@@ -507,7 +507,8 @@ size_t svg2_attn_workspace_bytes(int B, int H, int64_t Lq, int D, int n_slots, i
  *
  * Launch: one workgroup per compute unit takes the non-empty query tiles,
  * longest key list first, from a counter in the workspace (reset by the
- * call) until none are left.
+ * call) until none are left.  A slot with rows outside [1, 256] or past Lq,
+ * or a cluster outside [0, Cq), is skipped (its rows are not written).
  *   lse         NULL or device float [B][H][Lq] (natural log).
  *
  * Arithmetic: chunk_causal_attn's (bf16 products, fp32 online softmax) over

@@ -288,7 +288,7 @@ def test_svg2_sizes():
     assert crattn.svg2_n_slots(4680, 20) == 19 + 20
     assert crattn.svg2_n_slots(256, 1) == 2 and crattn.svg2_n_slots(257, 1) == 3
     assert crattn.svg2_n_slots(0, 1) == 0 and crattn.svg2_n_slots(10, 0) == 0
-    order = (12 * 39 * 4 + 255) // 256 * 256
+    order = (12 * 39 * 16 + 255) // 256 * 256   # 16-byte work records
     assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 39, 1) == 256 + order
     assert crattn.svg2_attn_workspace_bytes(1, 12, 4680, 128, 39, 4) == \
         256 + order + 4 * 12 * 4680 * 129 * 4
