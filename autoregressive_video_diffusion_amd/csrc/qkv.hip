@@ -157,6 +157,53 @@ __device__ inline TabView stage_table(const QkvKArgs &a, lds_f2 *dst) {
 
 // Epilogue of a wavefront's TM x TN accumulator blocks (features f0 +
 // 32 TM fw.., tokens m0 + 32 TN tw..): rotate Q/K pairs, store Q', K', V.
+// One 32-feature block of one token block: rotate its pairs (ROT) with the
+// lane's (cos, sin), pack to bf16, trade halves with the lane 32 apart and
+// store 16 bytes a lane at dst (null for tokens past the end).
+template <bool ROT>
+__device__ __forceinline__ void store_block(const f32x16_t &acc, const float2 (&cs)[4][2],
+                                            uint16_t *dst) {
+  uint32_t wv[4][2];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = acc[4 * g + e];
+    if constexpr (ROT) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float2 r = rotate_pair(y[2 * e], y[2 * e + 1], cs[g][e]);
+        y[2 * e] = r.x;
+        y[2 * e + 1] = r.y;
+      }
+    }
+    wv[g][0] = pack_bf16(y[0], y[1]);
+    wv[g][1] = pack_bf16(y[2], y[3]);
+  }
+  // lane l < 32 holds features 8g..8g+3 of its token, lane l+32 the
+  // features 8g+4..8g+7: swapping group 2u+1 of the low lane with group 2u
+  // of the high lane leaves 16u..16u+7 in the low lane, 16u+8..16u+15 in
+  // the high one
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const auto r = __builtin_amdgcn_permlane32_swap(wv[2 * u][c], wv[2 * u + 1][c], false, false);
+      wv[2 * u][c] = r[0];
+      wv[2 * u + 1][c] = r[1];
+    }
+  if (dst == nullptr) return;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    uint4 o;
+    o.x = wv[2 * u][0];
+    o.y = wv[2 * u][1];
+    o.z = wv[2 * u + 1][0];
+    o.w = wv[2 * u + 1][1];
+    *reinterpret_cast<uint4 *>(dst + 16 * u) = o;
+  }
+}
+
 template <int TM, int TN, int JG, int D, bool LDS_TAB>
 __device__ __forceinline__ void rope_store_tile(const QkvKArgs &a, const f32x16_t (&acc)[TM][TN],
                                                 int f0, int m0, int fw, int tw, int l32, int hf,
@@ -280,6 +327,94 @@ __device__ __forceinline__ void rope_store_tile(const QkvKArgs &a, const f32x16_
       }
     }
   }
+  }
+}
+
+template <int TM, int TN, int D>
+__device__ __forceinline__ void rope_store_tile_wide(const QkvKArgs &a, const f32x16_t (&acc)[TM][TN],
+                                                     int f0, int m0, int fw, int tw, int l32,
+                                                     int hf, const lds_f2 *tl, TabView tv) {
+  constexpr int JG = 1;
+  // The wide tile's epilogue (the narrow tile's is rope_store_tile, which
+  // gathers from the table in global memory).  The wavefront's TM blocks
+  // cover 32 TM consecutive features starting on a head boundary, so each
+  // block's head, part (Q, K, V) and offset in the head follow from one
+  // division, made once per wavefront in scalar registers: the choice
+  // between rotating and not is a uniform branch per block.  Per token block: the (cos, sin) of the lane's pairs are
+  // gathered in one batch (tokens past the end use the last token's
+  // position), rotated, then lanes l and l+32 trade halves so that each
+  // lane holds 8 consecutive features and writes 16 bytes.
+  constexpr int HT = (D - 4 * (D / 6)) / 2;  // pairs of the t group
+  constexpr int HH = D / 6;                  // pairs of the h group (= w group)
+  const int fw0 = __builtin_amdgcn_readfirstlane(f0 + fw * 32 * TM);
+  const int hg0 = fw0 / D;                   // global head index (over Q, K, V)
+  const int part0 = __builtin_amdgcn_readfirstlane(hg0 / a.H);
+  const int h0 = hg0 - part0 * a.H;
+  int part[TM], head[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int h = h0 + (32 * i) / D;
+    part[i] = __builtin_amdgcn_readfirstlane(h >= a.H ? part0 + 1 : part0);
+    head[i] = __builtin_amdgcn_readfirstlane(h >= a.H ? h - a.H : h);
+  }
+  const int n32 = (int)a.n;
+  // one token block at a time (the table rows are in LDS)
+#pragma unroll
+  for (int j0 = 0; j0 < TN; j0 += JG) {
+    float2 cs[JG][TM][4][2];
+    // the lane's token row in Q' and in the caches (elements), -1 past the end
+    int64_t rowq[JG], rowc[JG];
+#pragma unroll
+    for (int jj = 0; jj < JG; ++jj) {
+      const int j = j0 + jj;
+      const int m = m0 + tw * 32 * TN + j * 32 + l32;
+      const int mc = min(m, a.M - 1);
+      const int b = mc / n32, i_tok = mc - b * n32;
+      rowq[jj] = m < a.M ? (int64_t)m * a.H * D : -1;
+      rowc[jj] = ((int64_t)b * a.H * a.cap + a.cache_pos + i_tok) * D;
+      const Pos p = decode_pos(a.tok_off + (uint32_t)i_tok, a.per_frame, a.gw, a.t0);
+      // per-lane table pointers of the three axes (into the table, or its
+      // copy in LDS), offset so that entry q of the lane's pair set is
+      // ptr[axis][q] (the high half-wave's pairs are 2 further on)
+      auto fetch = [&](auto base) {
+        decltype(base) ax[3] = {base + (p.t - tv.t_lo) * HT + 2 * hf,
+                                base + tv.base_h + p.h * HH - HT + 2 * hf,
+                                base + tv.base_w + p.w * HH - HT - HH + 2 * hf};
+        auto axis = [](int q) { return q < HT ? 0 : q < HT + HH ? 1 : 2; };
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if (fw0 + 32 * i >= a.F || part[i] >= 2) continue;
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int q0 = ((32 * i) % D) / 2 + 4 * g + e;  // pair of the low half-wave
+              const int a0 = axis(q0), a1 = axis(q0 + 2);
+              const auto ptr = a0 == a1 ? ax[a0] : (hf ? ax[a1] : ax[a0]);
+              const auto v = ptr[q0];
+              cs[jj][i][g][e] = make_float2(v.x, v.y);
+            }
+        }
+      };
+      fetch(tl);
+    }
+#pragma unroll
+    for (int jj = 0; jj < JG; ++jj) {
+      const int j = j0 + jj;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (fw0 + 32 * i >= a.F) continue;
+        // the block's base (scalar) plus the lane's token row
+        uint16_t *base = part[i] == 0 ? a.q_out : part[i] == 1 ? a.k_cache : a.v_cache;
+        base += (int64_t)head[i] * (part[i] == 0 ? D : a.cap * D) + (32 * i) % D;
+        uint16_t *dst = rowq[jj] < 0 ? nullptr
+                        : base + (part[i] == 0 ? rowq[jj] : rowc[jj]) + 8 * hf;
+        if (part[i] < 2)
+          store_block<true>(acc[i][j], cs[jj][i], dst);
+        else
+          store_block<false>(acc[i][j], cs[jj][i], dst);
+      }
+    }
   }
 }
 
@@ -620,7 +755,7 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   pin_acc();
 
-  rope_store_tile<TM, TN, 1, D, true>(a, acc, f0, m0, fw, tw, l32, hf, tl, tv);
+  rope_store_tile_wide<TM, TN, D>(a, acc, f0, m0, fw, tw, l32, hf, tl, tv);
 }
 
 }  // namespace
