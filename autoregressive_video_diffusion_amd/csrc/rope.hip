@@ -17,6 +17,7 @@
 #include "rope_common.h"
 #include "../../include/crattn.h"
 
+
 namespace crattn {
 namespace {
 
@@ -74,55 +75,99 @@ __device__ inline uint32_t rot_bf16(uint32_t u, float2 cs) {
   return pack_bf16(r.x, r.y);
 }
 
+// Unsigned division by a divisor fixed for the launch as a multiply-high, an
+// add and a shift (Granlund and Montgomery, "Division by Invariant Integers
+// using Multiplication", 1994: the round-up multiplier for 32-bit operands
+// with a 33-bit add): l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
+// n / d = (mulhi(n, m) + n) >> l for every 32-bit n.  d in [1, 2^31].
+struct FastDiv {
+  uint32_t m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  return FastDiv{(uint32_t)m, l};
+}
+__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.l);
+}
+
 struct AppendGeom {
   uint32_t total;      // B * n * H * V threads
   uint32_t V;          // 16-byte vectors per row
   uint32_t n, H;
   uint32_t per_frame, gw, t0, tok_off;
+  FastDiv dV, dH, dn, dframe, dgw;  // the same divisors for the bf16 pass
 };
 
-// One thread per 16-byte vector of one (b, token, head) row.  Thread order is
-// the input order (vector, head, token, batch), so Q/K/V reads are fully
+// Where one 16-byte vector of one (b, token, head) row lives.  Vector order
+// is the input order (vector, head, token, batch), so Q/K/V reads are fully
 // contiguous and each cache write covers whole rows of one head.
+struct VecAt {
+  size_t in_off, cache_off;  // in elements
+  uint32_t pair0;            // first feature pair of the vector
+  Pos p;
+};
+
+__device__ inline VecAt locate(uint32_t t, const RopeAppendArgs &a, const AppendGeom &g) {
+  const uint32_t row = fdiv(t, g.dV);  // (b * n + i) * H + h
+  const uint32_t c = t - row * g.V;
+  const uint32_t bi = fdiv(row, g.dH);
+  const uint32_t h = row - bi * g.H;
+  const uint32_t b = fdiv(bi, g.dn);
+  const uint32_t i = bi - b * g.n;
+  const uint32_t tok = g.tok_off + i;
+  const uint32_t f = fdiv(tok, g.dframe);
+  const uint32_t in_frame = tok - f * g.per_frame;
+  const uint32_t r = fdiv(in_frame, g.dgw);
+  VecAt v;
+  v.p = Pos{g.t0 + f, r, in_frame - r * g.gw};
+  v.in_off = (size_t)row * (size_t)a.D + (size_t)c * 8;
+  v.cache_off = (((size_t)b * g.H + h) * (size_t)a.cap + (size_t)a.cache_pos + i) * (size_t)a.D +
+                (size_t)c * 8;
+  v.pair0 = c * 4;
+  return v;
+}
+
+// The inputs of one vector: K, V, Q (zero when there is no Q) and the four
+// (cos, sin) pairs it rotates by.
+struct VecIn {
+  uint4 k, v, q;
+  float2 cs[4];
+};
+
+__device__ inline VecIn load_vec(const VecAt &at, const RopeAppendArgs &a, const TabGeom &tg) {
+  VecIn x;
+  x.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + at.in_off);
+  x.v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + at.in_off);
+  x.q = make_uint4(0, 0, 0, 0);
+  if (a.q != nullptr)
+    x.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + at.in_off);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x.cs[j] = pair_cs(a.table, tg, at.pair0 + j, at.p);
+  return x;
+}
+
+__device__ inline void store_vec(const VecAt &at, const VecIn &x, const RopeAppendArgs &a) {
+  const uint4 ko = make_uint4(rot_bf16(x.k.x, x.cs[0]), rot_bf16(x.k.y, x.cs[1]),
+                              rot_bf16(x.k.z, x.cs[2]), rot_bf16(x.k.w, x.cs[3]));
+  ntstore(ko, static_cast<uint16_t *>(a.k_cache) + at.cache_off);
+  ntstore(x.v, static_cast<uint16_t *>(a.v_cache) + at.cache_off);
+  if (a.q != nullptr) {
+    const uint4 qo = make_uint4(rot_bf16(x.q.x, x.cs[0]), rot_bf16(x.q.y, x.cs[1]),
+                                rot_bf16(x.q.z, x.cs[2]), rot_bf16(x.q.w, x.cs[3]));
+    ntstore(qo, static_cast<uint16_t *>(a.q_out) + at.in_off);
+  }
+}
+
+// One thread per 16-byte vector.
 __global__ void __launch_bounds__(256) rope_append_bf16_kernel(RopeAppendArgs a, AppendGeom g,
                                                                 TabGeom tg) {
   const uint32_t t = blockIdx.x * 256u + threadIdx.x;
   if (t >= g.total) return;
-  const uint32_t c = t % g.V;
-  const uint32_t row = t / g.V;  // (b * n + i) * H + h
-  const uint32_t h = row % g.H;
-  const uint32_t bi = row / g.H;
-  const uint32_t i = bi % g.n;
-  const uint32_t b = bi / g.n;
-  const Pos p = decode_pos(g.tok_off + i, g.per_frame, g.gw, g.t0);
-
-  const size_t in_off = (size_t)row * (size_t)a.D + (size_t)c * 8;
-  const size_t cache_off =
-      (((size_t)b * g.H + h) * (size_t)a.cap + (size_t)a.cache_pos + i) * (size_t)a.D +
-      (size_t)c * 8;
-
-  const uint4 kv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + in_off);
-  const uint4 vv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + in_off);
-  uint4 qv = make_uint4(0, 0, 0, 0);
-  const bool has_q = a.q != nullptr;
-  if (has_q) qv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + in_off);
-
-  const uint32_t pair0 = c * 4;
-  const float2 cs0 = pair_cs(a.table, tg, pair0 + 0, p);
-  const float2 cs1 = pair_cs(a.table, tg, pair0 + 1, p);
-  const float2 cs2 = pair_cs(a.table, tg, pair0 + 2, p);
-  const float2 cs3 = pair_cs(a.table, tg, pair0 + 3, p);
-
-  const uint4 ko = make_uint4(rot_bf16(kv.x, cs0), rot_bf16(kv.y, cs1), rot_bf16(kv.z, cs2),
-                              rot_bf16(kv.w, cs3));
-  ntstore(ko, static_cast<uint16_t *>(a.k_cache) + cache_off);
-  ntstore(vv, static_cast<uint16_t *>(a.v_cache) + cache_off);
-  if (has_q) {
-    const uint4 qo = make_uint4(rot_bf16(qv.x, cs0), rot_bf16(qv.y, cs1), rot_bf16(qv.z, cs2),
-                                rot_bf16(qv.w, cs3));
-    ntstore(qo, static_cast<uint16_t *>(a.q_out) + in_off);
-
-  }
+  const VecAt at = locate(t, a, g);
+  store_vec(at, load_vec(at, a, tg), a);
 }
 
 __device__ inline float2 rot_f32(float x, float y, float2 cs) { return rotate_pair(x, y, cs); }
@@ -194,6 +239,11 @@ hipError_t launch_rope_append(const RopeAppendArgs &a, hipStream_t s) {
   g.gw = (uint32_t)a.grid_w;
   g.t0 = (uint32_t)a.t0;
   g.tok_off = (uint32_t)a.tok_off;
+  g.dV = make_fastdiv(g.V);
+  g.dH = make_fastdiv(g.H);
+  g.dn = make_fastdiv(g.n);
+  g.dframe = make_fastdiv(g.per_frame);
+  g.dgw = make_fastdiv(g.gw);
   const dim3 grid((g.total + 255u) / 256u);
   if (a.dtype == CRATTN_BF16)
     hipLaunchKernelGGL(rope_append_bf16_kernel, grid, dim3(256), 0, s, a, g, tg);

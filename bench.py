@@ -639,6 +639,29 @@ def rope_append_rate(crattn, w, dev, sets=1, bursts=5, burst=10):
                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}
 
 
+def device_copy_us(nbytes, sets=8, bursts=7, burst=40):
+    """torch's device-to-device copy of one nbytes buffer into another, over
+    `sets` buffer pairs used round-robin (past the Infinity Cache, as the
+    RoPE/append pass is timed): per-launch µs of the median burst.  The same
+    bytes cross HBM as in a pass that reads nbytes and writes nbytes."""
+    import torch
+
+    n = nbytes // 2
+    src = [torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(sets)]
+    dst = [torch.empty_like(x) for x in src]
+
+    def call(i):
+        dst[i % sets].copy_(src[i % sets])
+
+    for i in range(2 * sets):
+        call(i)
+    torch.cuda.synchronize()
+    ms = burst_ms(call, bursts, burst)[bursts // 2]
+    del src, dst
+    torch.cuda.empty_cache()
+    return ms * 1e3
+
+
 def sample_rows(lq, per_frame, stride=16):
     """Every stride-th query row plus the first and last row of every frame."""
     import numpy as np
@@ -864,6 +887,8 @@ def main():
 
     rope_bursts = burst_ms(rope_call, 7, burst)
     rope_burst_ms = rope_bursts[len(rope_bursts) // 2]
+    # the same bytes moved by torch's device copy (half read, half written)
+    copy_us = device_copy_us(rope_bytes(w.B, w.lq, w.H, w.D) // 2)
 
     # fused QKV projection (the next row of the path), timed on its own
     qkv_bursts = time_qkv(crattn, w, dev, table, ext)
@@ -948,7 +973,10 @@ def main():
         "rope_roofline": {"bound": "hbm", "achieved": round(rope_gbs, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(rope_gbs / PEAK_HBM_GBS, 4),
                           "bytes_per_launch": rb, "launches_timed": 7 * burst,
-                          "traffic": read_traffic("rope")},
+                          "traffic": read_traffic("rope"),
+                          "device_copy_same_bytes_us": round(copy_us, 2),
+                          "device_copy_frac": round(rb / (copy_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                                    4)},
         "qkv_rope_append": {"us": round(qkv_ms * 1e3, 2), "hidden": C,
                             "us_per_burst": [round(x * 1e3, 2) for x in qkv_bursts],
                             "roofline": {"bound": "mfma", "achieved": round(qkv_tflops, 1),
