@@ -1423,12 +1423,17 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
       // the other wavefronts' slot stores before its release and its acquire
       // before their slot loads.  Slot writers release (L2 write-back) once;
       // only the merging part acquires (L2 invalidate).
+      // A workgroup's first part (the head of its last tile) is never the
+      // tile's last part in practice: it writes its slot without first
+      // asking whether the others are done (one counter round trip less).
       unsigned *cnt = a.counters + part0;
-      if (tid == 0)
-        sh_count = (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      merge = sh_count == n_parts - 1;
-      __syncthreads();
+      if (!first) {
+        if (tid == 0)
+          sh_count = (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        merge = sh_count == n_parts - 1;
+        __syncthreads();
+      }
       if (!merge) {
         const int64_t slot = 2 * w + (s_lo >= a0 ? 0 : 1);
         float *so = a.ws_o + slot * (256 * D);
@@ -1473,7 +1478,46 @@ __global__ void __launch_bounds__(256, 1) attn_fwd64_kernel(AttnKArgs a) {
       const int r = trow0 + qb * 32;
       if (r >= nrows) continue;
       float scl = inv[qb], lse_f = lse2[qb];
-      if (merge) {
+      if (merge && part1 == part0 + 1) {
+        // two parts, the usual cut: the other part's log-sum-exp and O are
+        // loaded together, then combined in workgroup order with the same
+        // operations, in the same order, as the general merge below
+        const int64_t vo = part0 == w ? part1 : part0;
+        const int64_t so = 2 * vo + (vo * T / G >= a0 ? 0 : 1);
+        const float lo = a.ws_lse[so * 256 + r];
+        const float *opo = a.ws_o + so * (256 * D) + (int64_t)r * D + hf * 4;
+        float4 xo[DB][4];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4)
+            xo[db][i4] = *reinterpret_cast<const float4 *>(opo + db * 32 + i4 * 8);
+        const bool own0 = part0 == w;
+        const float l0 = own0 ? lse2[qb] : lo, l1 = own0 ? lo : lse2[qb];
+        float mx = -INFINITY;
+        mx = fmaxf(mx, l0);
+        mx = fmaxf(mx, l1);
+        const float w0 = l0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l0 - mx);
+        const float w1 = l1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(l1 - mx);
+        float wsum = 0.f;
+        wsum += w0;
+        wsum += w1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i4 = 0; i4 < 4; ++i4) {
+            const int base = qb * 16 + i4 * 4;
+            const float4 own = make_float4(o[db][base + 0] * inv[qb], o[db][base + 1] * inv[qb],
+                                           o[db][base + 2] * inv[qb], o[db][base + 3] * inv[qb]);
+            const float4 x0 = own0 ? own : xo[db][i4], x1 = own0 ? xo[db][i4] : own;
+            o[db][base + 0] = fmaf(w1, x1.x, fmaf(w0, x0.x, 0.f));
+            o[db][base + 1] = fmaf(w1, x1.y, fmaf(w0, x0.y, 0.f));
+            o[db][base + 2] = fmaf(w1, x1.z, fmaf(w0, x0.z, 0.f));
+            o[db][base + 3] = fmaf(w1, x1.w, fmaf(w0, x0.w, 0.f));
+          }
+        scl = wsum > 0.f ? 1.0f / wsum : 0.f;
+        lse_f = wsum > 0.f ? mx + __log2f(wsum) : -INFINITY;
+      } else if (merge) {
         float mx = -INFINITY;
         for (int64_t v = part0; v <= part1; ++v) {
           const int64_t slot = 2 * v + (v * T / G >= a0 ? 0 : 1);
