@@ -662,6 +662,25 @@ def device_copy_us(nbytes, sets=8, bursts=7, burst=40):
     return ms * 1e3
 
 
+def matmul_tflops(n=8192, reps=20):
+    """torch's bf16 matmul (hipBLASLt) of two n x n N(0,1) matrices on this
+    box: a reference for what the matrix cores sustain on random operands
+    under the same power limit (TFLOP/s of the median of five bursts)."""
+    import torch
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(5):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    ms = burst_ms(lambda i: torch.matmul(a, b, out=c), 5, reps)[2]
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def sample_rows(lq, per_frame, stride=16):
     """Every stride-th query row plus the first and last row of every frame."""
     import numpy as np
@@ -889,6 +908,8 @@ def main():
     rope_burst_ms = rope_bursts[len(rope_bursts) // 2]
     # the same bytes moved by torch's device copy (half read, half written)
     copy_us = device_copy_us(rope_bytes(w.B, w.lq, w.H, w.D) // 2)
+    # the same box's bf16 matmul rate on random operands (power-limited)
+    mm_tflops = matmul_tflops()
 
     # fused QKV projection (the next row of the path), timed on its own
     qkv_bursts = time_qkv(crattn, w, dev, table, ext)
@@ -966,6 +987,10 @@ def main():
                                        round(rope_burst_ms * 1e3, 2),
                                        round(rope_bursts[-1] * 1e3, 2)],
         "rope_append_in_step_us": round(rope_ms * 1e3, 2),
+        "box_reference": {"torch_matmul_bf16_8192_tflops": round(mm_tflops, 1),
+                          "attn_over_matmul": round(attn_tflops / mm_tflops, 4),
+                          "note": "the same box's hipBLASLt GEMM on N(0,1) operands: what "
+                                  "its matrix cores sustain under the power limit"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
