@@ -693,8 +693,9 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
 
   // ---- main loop.  Step s: wait for this wavefront's copies of stage s+1,
   // barrier (every wavefront's copies of it have landed, and every
-  // wavefront has finished reading stage s-1), issue the copies of stage
-  // s+NS-1 into the slot of stage s-1, then the two sub-steps of stage s.
+  // wavefront has finished reading stage s-1), then the two sub-steps of
+  // stage s, with the copies of stage s+NS-1 into the slot of stage s-1
+  // spread over both.
   // Each sub-step's products run block row by block row; the reads of the
   // next sub-step's fragments (stage s's second half, or stage s+1's first)
   // are spread between them.  Past the last stage the copies repeat it
@@ -716,12 +717,14 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
 #pragma unroll
   for (int j = 0; j < TN; ++j) fb0[j] = frag_b(0, 0, j);
 
-  // one sub-step: products from fa and bc; `copies` of stage cs into slot
-  // cslot go between the first products, then the reads of the next
-  // sub-step's B fragments (slot nslot, sub-step nkk) into bn; A block i is
+  // one sub-step: products from fa and bc; copies c_lo .. c_hi-1 of stage
+  // cs into slot cslot go after every fourth product (a step's copies are
+  // split between its two sub-steps, so they reach the address unit evenly
+  // rather than in one burst), the reads of the next sub-step's B fragments
+  // (slot nslot, sub-step nkk) into bn after the odd products; A block i is
   // re-read into fa after its row of products
   auto substep = [&](const bf16x8_t (&bc)[TN], bf16x8_t (&bn)[TN], int nslot, int nkk,
-                     bool read_next, int copies, int cs, int cslot) {
+                     bool read_next, int c_lo, int c_hi, int cs, int cslot) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -731,8 +734,8 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
         else
           mfma_reg<false>(acc[i][j], fa[i], bc[j]);
         const int t = i * TN + j;
-        if (t < copies) dma1(t, cs, cslot);
-        if (read_next && t >= copies && t < copies + TN) bn[t - copies] = frag_b(nslot, nkk, t - copies);
+        if (t % 4 == 0 && c_lo + t / 4 < c_hi) dma1(c_lo + t / 4, cs, cslot);
+        if (read_next && (t & 1) && (t >> 1) < TN) bn[t >> 1] = frag_b(nslot, nkk, t >> 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (read_next) fa[i] = frag_a(nslot, nkk, i);
@@ -744,8 +747,8 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
     wait_vmcnt<(NS - 3) * kDma>();
     __syncthreads();
     const int cslot = (s + NS - 1) % NS, slot = s % NS, nslot = (s + 1) % NS;
-    substep(fb0, fb1, slot, 1, true, kDma, s + NS - 1, cslot);
-    substep(fb1, fb0, nslot, 0, kRead, 0, 0, 0);
+    substep(fb0, fb1, slot, 1, true, 0, kDma / 2, s + NS - 1, cslot);
+    substep(fb1, fb0, nslot, 0, kRead, kDma / 2, kDma, s + NS - 1, cslot);
   };
   for (int s = 0; s < nk - 1; ++s) step(s, std::true_type());
   step(nk - 1, std::false_type());
