@@ -88,6 +88,13 @@ __device__ inline void lds_dma16(const void *gbase, uint32_t voff, uint32_t lds_
                : "s"(lds_addr), "v"(voff), "s"(gbase)
                : "memory", "m0");
 }
+// The same with 4 bytes a lane: 256 bytes per instruction.
+__device__ inline void lds_dma4(const void *gbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Tile of workgroup blockIdx.x: first feature f0 and first token m0 of a
@@ -132,25 +139,32 @@ __host__ __device__ inline int staged_rows(uint32_t t0, uint32_t tok_off, int64_
   return (t_hi - t_lo + 1) * HT + (int)(per_frame / gw) * HH + (int)gw * HH;
 }
 
-// Copy those rows into LDS at dst, in that order, and return the view of
-// the copy.  The epilogue's per-lane reads then go to LDS: each lane reads
-// the rows of its own token, which in global memory are a gather over many
-// cache lines per instruction (the w rows differ from lane to lane).  The
-// launcher checks that the rows fit.  Called by every thread of the
-// workgroup; a barrier must follow before the rows are read.
+// Copy those rows into LDS at byte address dst, in that order, and return
+// the view of the copy.  The epilogue's per-lane reads then go to LDS: each
+// lane reads the rows of its own token, which in global memory are a gather
+// over many cache lines per instruction (the w rows differ from lane to
+// lane).  The rows go global -> LDS with 4-byte copies (no registers held,
+// in flight beside the ring's first stages; entries are 8 bytes and the
+// ranges start anywhere), wavefront w taking copies w, w + kNW, ...  The
+// caller waits for them (vmcnt) and passes a barrier before the rows are
+// read; the launcher checks that the rows fit.
 template <int D>
-__device__ inline TabView stage_table(const QkvKArgs &a, lds_f2 *dst) {
+__device__ inline TabView dma_table(const QkvKArgs &a, uint32_t dst, int wave, int lane) {
   constexpr int HT = (D - 4 * (D / 6)) / 2, HH = D / 6;
   int t_lo;
   const int total = staged_rows<D>(a.t0, a.tok_off, a.n, a.per_frame, a.gw, t_lo);
-  const int nt = total - (int)(a.per_frame / a.gw) * HH - (int)a.gw * HH;
   const int nh = (int)(a.per_frame / a.gw) * HH;
-  for (int k = (int)threadIdx.x; k < total; k += (int)blockDim.x) {
-    const int src = k < nt ? t_lo * HT + k
-                    : k < nt + nh ? (int)a.tg.base_h + (k - nt)
-                                  : (int)a.tg.base_w + (k - nt - nh);
-    const float2 v = a.table[src];
-    dst[k] = f32x2_t{v.x, v.y};
+  const int nt = total - nh - (int)a.gw * HH;
+  const int ndw = 2 * total;
+  const int n_copies = (ndw + 63) / 64;
+  for (int k = wave; k < n_copies; k += kNW) {
+    const int q = min(k * 64 + lane, ndw - 1);  // dword of the copy (lanes past the end repeat the last)
+    const int e = q >> 1;
+    const int src = e < nt        ? t_lo * HT + e
+                    : e < nt + nh ? (int)a.tg.base_h + (e - nt)
+                                  : (int)a.tg.base_w + (e - nt - nh);
+    lds_dma4(a.table, (uint32_t)src * 8u + (uint32_t)(q & 1) * 4u,
+             __builtin_amdgcn_readfirstlane(dst + (uint32_t)k * 256u));
   }
   return TabView{t_lo, nt, nt + nh};
 }
@@ -621,9 +635,13 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
   int f0, m0;
   tile_origin(a, kBM, kBN, f0, m0);
   // the table rows of the epilogue, copied while the first stages load (the
-  // barrier before the first fragment reads publishes them)
+  // prologue's vmcnt wait and barrier before the first fragment reads
+  // publish them: the copies are issued before the stages')
   lds_f2 *tl = (lds_f2 *)reinterpret_cast<f32x2_t *>(tab);
-  const TabView tv = stage_table<D>(a, tl);
+  typedef __attribute__((address_space(3))) char lds_char_t;
+  const TabView tv = dma_table<D>(
+      a, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(tab)),
+      wave, lane);
 
   // ---- per-lane copy offsets.  LDS row r holds its 4 chunks of 8 C-values
   // (64 bytes) in swizzled order: physical cell p has chunk p ^ ((r >> 2) &
@@ -640,7 +658,6 @@ __global__ void __launch_bounds__(kNW * 64, 1) qkv_rope_wide_kernel(QkvKArgs a) 
   for (int o = 0; o < kDma; ++o)
     dma_off[o] = o < kAW ? cell_off((wave + o * kNW) * 64 + lane, a.F - f0)
                          : cell_off((wave + (o - kAW) * kNW) * 64 + lane, a.M - m0);
-  typedef __attribute__((address_space(3))) char lds_char_t;
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(lds_char_t *)reinterpret_cast<char *>(ring));
   const uint16_t *wa = a.w + (int64_t)f0 * a.C;
@@ -797,7 +814,8 @@ hipError_t launch_qkv_rope(const QkvArgs &q, hipStream_t s) {
   int t_lo;
   const int rows = q.D == 128 ? staged_rows<128>(a.t0, a.tok_off, q.n, a.per_frame, a.gw, t_lo)
                               : staged_rows<64>(a.t0, a.tok_off, q.n, a.per_frame, a.gw, t_lo);
-  const bool wide_ok = (int64_t)rows * 8 <= kQkvTabBytes;
+  // (the last 256-byte copy of the rows may run past them)
+  const bool wide_ok = (int64_t)rows * 8 + 256 <= kQkvTabBytes;
   int best_tn = 4;
   int64_t best_cost = -1;
   for (int tn : {6, 4, 3, 2}) {
