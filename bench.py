@@ -949,7 +949,7 @@ def main():
         extras["rollout480_hsa_ms_total"] = round(rollout_ms(crattn, dev, hsa=(6, 32)), 3)
         extras["sp480_rope_append"] = rope_append_rate(crattn, SP480, dev, sets=8, burst=40)
         extras["sp480_rope_append"]["note"] = ("10.8 MB per launch: launch-bound, and its 8 "
-                                               "sets fit the Infinity Cache; reported, not judged")
+                                               "sets fit the Infinity Cache; reported for context")
         torch.cuda.empty_cache()
         del sets
         torch.cuda.empty_cache()
