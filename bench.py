@@ -227,6 +227,26 @@ def time_qkv(crattn, w, dev, table, ext, burst=20, bursts=5):
     return burst_ms(call, bursts, burst)
 
 
+def qkv_matmul_us(w, dev, burst=20, bursts=5):
+    """torch's bf16 matmul (hipBLASLt) of the same projection, x [n, C] times
+    W^T [C, 3 H D], without the rotation or the append: per-launch µs of the
+    median burst over the same four hidden-state sets (W^T made contiguous
+    first)."""
+    import torch
+
+    from workloads import projection_inputs
+
+    sets = [projection_inputs(w, i) for i in range(4)]
+    xs = [x.to(dev).reshape(-1, x.shape[-1]) for x, _ in sets]
+    wtt = sets[0][1].to(dev).t().contiguous()
+    y = torch.empty(xs[0].shape[0], wtt.shape[1], dtype=torch.bfloat16, device=dev)
+    for i in range(2 * burst):
+        torch.matmul(xs[i % 4], wtt, out=y)
+    torch.cuda.synchronize()
+    ms = burst_ms(lambda i: torch.matmul(xs[i % 4], wtt, out=y), bursts, burst)[bursts // 2]
+    return ms * 1e3
+
+
 def time_hsa(crattn, w, b, kf=6, kb=32):
     """Hierarchical block-sparse attention on the step's chunk (rotated Q' and
     the 7-chunk cache of buffer set b): per-launch times of the key pooling
@@ -913,6 +933,7 @@ def main():
 
     # fused QKV projection (the next row of the path), timed on its own
     qkv_bursts = time_qkv(crattn, w, dev, table, ext)
+    qkv_mm_us = qkv_matmul_us(w, dev)
     qkv_ms = qkv_bursts[len(qkv_bursts) // 2]
     C = w.H * w.D
     qkv_tflops = qkv_flops(w.B, w.lq, C, w.H, w.D) / (qkv_ms * 1e-3) / 1e12
@@ -1003,6 +1024,7 @@ def main():
                           "device_copy_frac": round(rb / (copy_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
                                                     4)},
         "qkv_rope_append": {"us": round(qkv_ms * 1e3, 2), "hidden": C,
+                            "torch_matmul_same_shape_us": round(qkv_mm_us, 2),
                             "us_per_burst": [round(x * 1e3, 2) for x in qkv_bursts],
                             "roofline": {"bound": "mfma", "achieved": round(qkv_tflops, 1),
                                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
