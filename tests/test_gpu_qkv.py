@@ -157,6 +157,25 @@ def test_wide_tiles_every_element(B, n, C, H, D, with_q):
         assert bool((c[:, :, :pos] == fill).all()) and bool((c[:, :, pos + n:] == fill).all())
 
 
+def test_wide_tile_table_at_its_lds_limit():
+    # a 40 x 200 grid over two frames: the epilogue's table rows (2 x 22 of
+    # axis t, 40 x 21 of h, 200 x 21 of w: 40.7 KB with the copies' tail) all
+    # but fill the wide tile's LDS for them, each wavefront issues 40 of the
+    # 159 256-byte copies, and the rows of axis w end where the table ends
+    # (the copies read no entry past it); 256 x 384 tiles win the tie with
+    # the narrower tiles here.  Every element.
+    B, n, C, H, D, gh, gw, t0 = 1, 12000, 512, 4, 128, 40, 200, 5
+    cap, pos = n + 64, 64
+    x, w = _inputs(B, n, C, H, D, 7100)
+    q, kc, vc = _run(x, w, H, D, cap, pos, t0, 0, gh, gw)
+    (qe, ke, ve), (q0, k0), (aq, ak, av) = _expected(x, w, H, D, t0, 0, gh, gw)
+    _check(f64(q), qe, aq, q0, C, True, "Q'")
+    _check(f64(kc[:, :, pos:pos + n]).transpose(0, 2, 1, 3), ke, ak, k0, C, True, "K'")
+    _check(f64(vc[:, :, pos:pos + n]).transpose(0, 2, 1, 3), ve, av, ve, C, False, "V")
+    for c, fill in ((kc, 7.0), (vc, -7.0)):
+        assert bool((c[:, :, :pos] == fill).all()) and bool((c[:, :, pos + n:] == fill).all())
+
+
 def test_projection_replays_from_a_hip_graph():
     # the fused projection + rotation + append captured once and replayed:
     # every replay writes the eager call's Q' and cache rows bit for bit,
