@@ -150,6 +150,23 @@ def test_batch2_ragged_grid_fp32_and_bf16():
         _check_cache(w, k, v, kc, vc, pos, w.lq, w.tok_off, bf16=(dt == "bf16"))
 
 
+def test_large_odd_divisors_bf16():
+    # the pass finds a vector's row, head, batch, frame and grid row by
+    # dividing by constants of the call (multiply-high division): a 37 x 199
+    # grid, 9973 tokens from token 4999 (so frames 0..2), 5 heads, 3 batches,
+    # head_dim 64 (8 vectors a row) checks them away from small powers of two
+    import dataclasses
+
+    w = dataclasses.replace(TINY, B=3, H=5, D=64, frames=3, grid_h=37, grid_w=199, t0=2,
+                            lq=9973, tok_off=4999, dtype="bf16")
+    q, k, v = call_qkv(w, 11)
+    cap, pos = w.lq + 50, 31
+    q_out, kc, vc = _run(w, q, k, v, cap, pos)
+    q_ref = oracle.rope(f64(q), w.t0, w.tok_off, w.grid_h, w.grid_w, w.theta)
+    assert_rope_bf16(f64(q_out), q_ref, f64(q))
+    _check_cache(w, k, v, kc, vc, pos, w.lq, w.tok_off, bf16=True)
+
+
 def test_win720_beyond_training_length():
     w = WIN720
     q, k, v = call_qkv(w, 0, n=1200)   # first 1200 tokens of the t0 = 81 chunk
