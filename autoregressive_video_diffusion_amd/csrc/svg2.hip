@@ -362,6 +362,8 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
   __shared__ int cpos[kMaxCand + 1];  // first 16-entry chunk of each kept cluster
   __shared__ float redf[4];
   __shared__ int redi[4];
+  __shared__ int st_s[kMaxCand];   // each candidate's first reordered row
+  __shared__ int cnt_s[kMaxCand];  // and its token count
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = (int)(blockIdx.x % (uint32_t)a.Cq);
   const int64_t bh = blockIdx.x / (uint32_t)a.Cq;
@@ -370,16 +372,10 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
   int32_t *sel = a.sel + (bh * a.Cq + i) * (int64_t)NC;
   const int32_t *koff = a.k_off + bh * a.S * (int64_t)(a.Ck + 1);
   // Offsets come from svg2_kmeans; they are clamped to [0, L] anyway, so
-  // that no read of k_perm leaves its slot.
-  auto start_of = [&](int j) {
-    const int s = j / a.Ck, c = j - s * a.Ck;
-    return (int)min(max((int64_t)koff[s * (a.Ck + 1) + c], (int64_t)0), a.L);
-  };
-  auto count_of = [&](int j) {
-    const int s = j / a.Ck, c = j - s * a.Ck;
-    const int64_t e = min(max((int64_t)koff[s * (a.Ck + 1) + c + 1], (int64_t)0), a.L);
-    return (int)max(e - start_of(j), (int64_t)0);
-  };
+  // that no read of k_perm leaves its slot.  Read once into LDS: every
+  // phase below looks them up.
+  auto start_of = [&](int j) { return st_s[j]; };
+  auto count_of = [&](int j) { return cnt_s[j]; };
   if (i == 0 && wave == 0) write_query_tiles(a, bh, lane);
   if (qo[i + 1] <= qo[i]) {
     if (tid == 0) a.list_len[bh * a.Cq + i] = 0;
@@ -387,6 +383,13 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
     return;
   }
   if (tid < D) qc[tid] = a.q_cent[(bh * a.Cq + i) * D + tid];
+  for (int j = tid; j < NC; j += 256) {
+    const int sl = j / a.Ck, c = j - sl * a.Ck;
+    const int64_t b0 = min(max((int64_t)koff[sl * (a.Ck + 1) + c], (int64_t)0), a.L);
+    const int64_t e0 = min(max((int64_t)koff[sl * (a.Ck + 1) + c + 1], (int64_t)0), a.L);
+    st_s[j] = (int)b0;
+    cnt_s[j] = (int)max(e0 - b0, (int64_t)0);
+  }
   __syncthreads();
   // 1. scores (-inf for empty clusters)
   {
