@@ -347,7 +347,7 @@ __device__ void write_query_tiles(const SvgPlanArgs &a, int64_t bh, int lane) {
 // lower id first) are kept while the shares before them add up to less than
 // p times the total -- found by radix selection of the cut, not by sorting.
 // The kept ids are compacted in ascending order, their key counts scanned,
-// and the list is copied 16 entries at a time.
+// and the list is copied in chunks of 16 entries, 16 lanes per chunk.
 template <int D>
 __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
   __shared__ float qc[D];
@@ -364,9 +364,15 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
   __shared__ int redi[4];
   __shared__ int st_s[kMaxCand];   // each candidate's first reordered row
   __shared__ int cnt_s[kMaxCand];  // and its token count
+  __shared__ int4 chunk_s[256];    // a batch of list chunks: source, position, count, s L
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = (int)(blockIdx.x % (uint32_t)a.Cq);
-  const int64_t bh = blockIdx.x / (uint32_t)a.Cq;
+  // Workgroups are dealt to the 8 XCDs in turn; the ones an XCD receives
+  // take consecutive (b, h, cluster) items, so that its L2 fetches the
+  // centroids and reorderings of about gridDim / (8 Cq) heads, not of all.
+  const uint32_t nx = gridDim.x / 8, rx = gridDim.x % 8, x = blockIdx.x % 8, kx = blockIdx.x / 8;
+  const uint32_t item = x < rx ? x * (nx + 1) + kx : rx * (nx + 1) + (x - rx) * nx + kx;
+  const int i = (int)(item % (uint32_t)a.Cq);
+  const int64_t bh = item / (uint32_t)a.Cq;
   const int NC = a.n_vis * a.Ck;
   const int32_t *qo = a.q_off + bh * (a.Cq + 1);
   int32_t *sel = a.sel + (bh * a.Cq + i) * (int64_t)NC;
@@ -578,33 +584,46 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
     }
     __syncthreads();
   }
-  // 7. the list: chunk q of 16 entries finds its kept cluster by binary
-  // search over the chunk positions and copies those entries of the slot's
-  // reordering (entries past list_cap are dropped)
+  // 7. the list, in batches of 256 chunks of 16 entries: each thread finds
+  // the kept cluster of one chunk by binary search over the chunk
+  // positions and leaves the chunk's first source row, list position and
+  // entry count in LDS; then each group of 16 lanes copies one chunk (lane
+  // u its entry u), so that a wave's loads and stores fall in 4 contiguous
+  // runs.  Entries past list_cap are dropped.
   const int n_chunks = cpos[n_kept];
   int32_t *lst = a.lists + (bh * a.Cq + i) * a.list_cap;
   const int32_t *kperm = a.k_perm + bh * a.S * a.L;
-#pragma unroll 2
-  for (int q = tid; q < n_chunks; q += 256) {
-    int lo = 0, hi = n_kept - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (cpos[mid] <= q)
-        lo = mid;
-      else
-        hi = mid - 1;
+  const int u = tid & 15;
+  for (int q0 = 0; q0 < n_chunks; q0 += 256) {
+    const int q = q0 + tid;
+    if (q < n_chunks) {
+      int lo = 0, hi = n_kept - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cpos[mid] <= q)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      const int sL = kept[lo] / a.Ck * a.L;
+      const int c0 = (q - cpos[lo]) * 16;
+      chunk_s[tid] = make_int4(sL + kstart[lo] + c0, lpos[lo] + c0,
+                               min(16, lpos[lo + 1] - lpos[lo] - c0), sL);
     }
-    const int s = kept[lo] / a.Ck;
-    const int c0 = (q - cpos[lo]) * 16;
-    const int cnt = lpos[lo + 1] - lpos[lo];
-    const int32_t *src = kperm + s * a.L + kstart[lo] + c0;
-    const int e0 = lpos[lo] + c0;
+    __syncthreads();
+    const int nb = min(256, n_chunks - q0);
+    int4 c[16];
     int32_t v[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = c0 + u < cnt ? src[u] : 0;
+    for (int m = 0; m < 16; ++m) {
+      const int r = (tid >> 4) + 16 * m;
+      c[m] = r < nb ? chunk_s[r] : make_int4(0, 0, 0, 0);
+      v[m] = u < c[m].z ? kperm[c[m].x + u] : 0;
+    }
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (c0 + u < cnt && e0 + u < a.list_cap) lst[e0 + u] = (int32_t)(s * a.L + v[u]);
+    for (int m = 0; m < 16; ++m)
+      if (u < c[m].z && c[m].y + u < a.list_cap) lst[c[m].y + u] = c[m].w + v[m];
+    __syncthreads();
   }
 }
 
