@@ -424,7 +424,8 @@ def svg2_extras(crattn, w, dev, dense_attn_ms, dense_flops, Cq=20, Ck=64, iters=
             "call_us": round(t["call"] * 1e3, 1),
             "call_graph_replay_us": round(t["call_graph"] * 1e3, 1), "listed_flops": sfl,
             "attn_tflops": round(tf, 1),
-            "call_speedup_vs_dense_attn": round(dense_attn_ms / t["call"], 2),
+            "call_speedup_vs_dense_attn": (round(dense_attn_ms / t["call"], 2)
+                                           if dense_attn_ms is not None else None),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
         del q, kc
@@ -877,7 +878,7 @@ def main():
         return
     if args.svg2_only:
         fl = attn_flops(w.B, w.H, w.lq, w.kv_len, w.D)
-        print(json.dumps({"svg2_480": svg2_extras(crattn, w, dev, float("nan"), fl)}))
+        print(json.dumps({"svg2_480": svg2_extras(crattn, w, dev, None, fl)}))
         return
     table, ext = make_table(w, dev)
     sets = [StepBuffers(w, dev, i) for i in range(args.sets)]
