@@ -120,7 +120,6 @@ __global__ void __launch_bounds__(256) hsa_select_kernel(HsaSelectArgs a) {
   constexpr int TPI = 16, FPT = D / TPI;
   auto scores = [&](int n, auto row_of) {
     const int sub = tid % TPI;
-#pragma unroll 8
     for (int base = tid / TPI; base < n; base += 256 / TPI) {
       const float *row = row_of(base) + sub * FPT;
       float s = 0.f;

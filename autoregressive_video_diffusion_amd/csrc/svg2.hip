@@ -402,7 +402,6 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
     constexpr int TPI = 4, FPT = D / TPI;
     const int sub = tid % TPI;
     const float *kc = a.k_cent + bh * a.S * (int64_t)a.Ck * D;
-#pragma unroll 4
     for (int j = tid / TPI; j < NC; j += 256 / TPI) {
       const float *row = kc + (int64_t)j * D + sub * FPT;
       float s = 0.f;
