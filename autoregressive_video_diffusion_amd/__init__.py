@@ -24,7 +24,7 @@ Entry points (see include/crattn.h for the full contracts):
   hierarchical block-sparse attention: pooled frame and block keys, two-level
   block selection per query block, attention over the own chunk plus the
   selected blocks.
-* ``svg2_kmeans_workspace_bytes`` / ``svg2_kmeans`` / ``svg2_n_slots`` /
+* ``svg2_kmeans_workspace_bytes`` / ``svg2_kmeans`` / ``svg2_kmeans2`` / ``svg2_n_slots`` /
   ``svg2_plan`` / ``svg2_attn_workspace_bytes`` / ``svg2_attn`` --
   semantic-permutation sparse attention: k-means of queries and keys with the
   reordering by cluster, centroid top-p selection with the key lists and
@@ -41,8 +41,8 @@ __all__ = [
     "CrattnError", "lib_path", "load", "rope_table_bytes", "rope_precompute",
     "rope_apply_append", "qkv_rope_append", "chunk_causal_attn_workspace_bytes",
     "chunk_causal_attn", "chunk_causal_attn_noalloc", "chunk_causal_attn_rope", "hsa_pool_bytes",
-    "hsa_pool_keys", "hsa_select", "hsa_attn", "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots",
-    "svg2_plan", "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error", "EXPORTS",
+    "hsa_pool_keys", "hsa_select", "hsa_attn", "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_kmeans2",
+    "svg2_n_slots", "svg2_plan", "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error", "EXPORTS",
     "HSA_QBLOCK", "HSA_KBLOCK", "SVG2_QTILE",
 ]
 
@@ -57,7 +57,8 @@ EXPORTS = ("rope_table_bytes", "rope_precompute", "rope_apply_append", "qkv_rope
            "chunk_causal_attn_workspace_bytes", "chunk_causal_attn", "chunk_causal_attn_noalloc",
            "chunk_causal_attn_rope",
            "hsa_pool_bytes", "hsa_pool_keys", "hsa_select", "hsa_attn",
-           "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_n_slots", "svg2_plan",
+           "svg2_kmeans_workspace_bytes", "svg2_kmeans", "svg2_kmeans2", "svg2_n_slots",
+           "svg2_plan",
            "svg2_attn_workspace_bytes", "svg2_attn", "crattn_last_error")
 HSA_QBLOCK, HSA_KBLOCK = 256, 64
 SVG2_QTILE = 256
@@ -66,6 +67,15 @@ _lib = None
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int
+
+
+class _KmProblem(ctypes.Structure):
+    """svg2_kmeans_problem of include/crattn.h."""
+    _fields_ = [("x", _vp), ("stride_b", _i64), ("stride_h", _i64), ("stride_row", _i64),
+                ("B", _i32), ("H", _i32), ("n", _i32), ("C", _i32),
+                ("centroids", _vp), ("cent_stride", _i64), ("perm", _vp), ("perm_stride", _i64),
+                ("offsets", _vp), ("off_stride", _i64), ("workspace", _vp),
+                ("ws_bytes", ctypes.c_size_t)]
 
 
 class CrattnError(RuntimeError):
@@ -121,6 +131,8 @@ def load():
     lib.svg2_kmeans.argtypes = [_vp, _i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _vp, _i64, _vp, _i64, _vp, _i64, _vp, ctypes.c_size_t, _vp]
     lib.svg2_kmeans.restype = _i32
+    lib.svg2_kmeans2.argtypes = [ctypes.POINTER(_KmProblem), _i32, _i32, _i32, _vp]
+    lib.svg2_kmeans2.restype = _i32
     lib.svg2_n_slots.argtypes = [_i64, _i32]
     lib.svg2_n_slots.restype = _i32
     lib.svg2_plan.argtypes = [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -396,6 +408,22 @@ def _view_ptr(t: torch.Tensor, what: str, dtype: torch.dtype, inner: int):
     return t.data_ptr(), st[1]
 
 
+def _km_problem(x: torch.Tensor, C: int, centroids: torch.Tensor, perm: torch.Tensor,
+                offsets: torch.Tensor, workspace: torch.Tensor):
+    B, H, n, D = x.shape
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(3) != 1:
+        raise ValueError("x must be a bf16 device view with a dense last dim")
+    if tuple(centroids.shape) != (B, H, C, D) or tuple(perm.shape) != (B, H, n) or \
+            tuple(offsets.shape) != (B, H, C + 1):
+        raise ValueError("centroids [B, H, C, D], perm [B, H, n], offsets [B, H, C+1] required")
+    cp, cs = _view_ptr(centroids, "centroids", torch.float32, 2)
+    pp, ps = _view_ptr(perm, "perm", torch.int32, 1)
+    op, os_ = _view_ptr(offsets, "offsets", torch.int32, 1)
+    return _KmProblem(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, n, C, cp, cs,
+                      pp, ps, op, os_, _ptr(workspace),
+                      workspace.numel() * workspace.element_size()), D
+
+
 def svg2_kmeans(x: torch.Tensor, C: int, iters: int, from_tokens: bool,
                 centroids: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor,
                 workspace: torch.Tensor, stream=None):
@@ -407,20 +435,25 @@ def svg2_kmeans(x: torch.Tensor, C: int, iters: int, from_tokens: bool,
     view [B, H, C, D] (in/out); perm: int32 view [B, H, n]; offsets: int32
     view [B, H, C + 1] (each dense inside a head, e.g. slices [:, :, s] of
     per-slot arrays)."""
-    B, H, n, D = x.shape
-    if x.dtype != torch.bfloat16 or not x.is_cuda or x.stride(3) != 1:
-        raise ValueError("x must be a bf16 device view with a dense last dim")
-    if tuple(centroids.shape) != (B, H, C, D) or tuple(perm.shape) != (B, H, n) or \
-            tuple(offsets.shape) != (B, H, C + 1):
-        raise ValueError("centroids [B, H, C, D], perm [B, H, n], offsets [B, H, C+1] required")
-    cp, cs = _view_ptr(centroids, "centroids", torch.float32, 2)
-    pp, ps = _view_ptr(perm, "perm", torch.int32, 1)
-    op, os_ = _view_ptr(offsets, "offsets", torch.int32, 1)
-    _raise(load().svg2_kmeans(x.data_ptr(), x.stride(0), x.stride(1), x.stride(2), B, H, n, D, C,
-                              iters, int(bool(from_tokens)), cp, cs, pp, ps, op, os_,
-                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+    p, D = _km_problem(x, C, centroids, perm, offsets, workspace)
+    _raise(load().svg2_kmeans(p.x, p.stride_b, p.stride_h, p.stride_row, p.B, p.H, p.n, D, C,
+                              iters, int(bool(from_tokens)), p.centroids, p.cent_stride, p.perm,
+                              p.perm_stride, p.offsets, p.off_stride, p.workspace, p.ws_bytes,
                               _stream(stream)))
     return centroids, perm, offsets
+
+
+def svg2_kmeans2(first: tuple, second: tuple, iters: int, from_tokens: bool, stream=None):
+    """svg2_kmeans of two problems in one launch sequence (same head_dim,
+    iters and start).  Each problem is the tuple (x, C, centroids, perm,
+    offsets, workspace) of svg2_kmeans's arguments; the two must not share
+    any buffer."""
+    p0, d0 = _km_problem(*first)
+    p1, d1 = _km_problem(*second)
+    if d0 != d1:
+        raise ValueError("both problems need the same head_dim")
+    arr = (_KmProblem * 2)(p0, p1)
+    _raise(load().svg2_kmeans2(arr, d0, iters, int(bool(from_tokens)), _stream(stream)))
 
 
 def svg2_n_slots(Lq: int, Cq: int) -> int:

@@ -552,55 +552,114 @@ size_t svg2_kmeans_workspace_bytes(int B, int H, int n, int C) {
   return assign + (size_t)B * H * ((n + 127) / 128) * C * 4u;
 }
 
+namespace {
+
+// Checks one k-means problem as svg2_kmeans documents and fills its kernel
+// arguments; `fn` names the call in the error message.
+int km_setup(const char *fn, const svg2_kmeans_problem &p, int D, int iters,
+             crattn::KmArgs *a) {
+  const int B = p.B, H = p.H, n = p.n, C = p.C;
+  if (p.x == nullptr || p.centroids == nullptr || p.perm == nullptr || p.offsets == nullptr ||
+      p.workspace == nullptr)
+    return fail(CRATTN_EINVAL, "%s: x, centroids, perm, offsets, workspace required", fn);
+  if (!aligned16(p.x) || !aligned16(p.centroids) || !aligned16(p.workspace) ||
+      (reinterpret_cast<uintptr_t>(p.perm) & 3u) || (reinterpret_cast<uintptr_t>(p.offsets) & 3u))
+    return fail(CRATTN_EINVAL, "%s: x, centroids, workspace 16-byte aligned required", fn);
+  if (D != 64 && D != 128)
+    return fail(CRATTN_ENOTSUP, "%s: head_dim %d not supported (64 or 128)", fn, D);
+  if (B < 1 || H < 1 || n < 1 || n > CRATTN_SVG2_MAX_N)
+    return fail(CRATTN_EINVAL, "%s: B, H >= 1 and n in [1, %d] required", fn,
+                CRATTN_SVG2_MAX_N);
+  if (C < 1 || C > CRATTN_SVG2_MAX_C || iters < 1 || iters > CRATTN_SVG2_MAX_ITERS)
+    return fail(CRATTN_EINVAL, "%s: C in [1, %d] and iters in [1, %d] required", fn,
+                CRATTN_SVG2_MAX_C, CRATTN_SVG2_MAX_ITERS);
+  if (p.stride_b < 0 || p.stride_h < 0 || p.stride_row < 0 || p.stride_b % 8 ||
+      p.stride_h % 8 || p.stride_row % 8 || p.stride_b > kMaxElems || p.stride_h > kMaxElems ||
+      p.stride_row > kMaxElems)
+    return fail(CRATTN_EINVAL, "%s: strides must be non-negative multiples of 8", fn);
+  if (p.cent_stride < (int64_t)C * D || p.cent_stride % 4 || p.perm_stride < n ||
+      p.off_stride < C + 1 || p.cent_stride > kMaxElems || p.perm_stride > kMaxElems ||
+      p.off_stride > kMaxElems)
+    return fail(CRATTN_EINVAL, "%s: output strides smaller than one head's extent", fn);
+  const size_t need = svg2_kmeans_workspace_bytes(B, H, n, C);
+  if (need == 0 || p.ws_bytes < need)
+    return fail(CRATTN_EINVAL, "%s: workspace of %zu bytes, %zu needed", fn, p.ws_bytes, need);
+  a->x = static_cast<const uint16_t *>(p.x);
+  a->sb = p.stride_b;
+  a->sh = p.stride_h;
+  a->sr = p.stride_row;
+  a->B = B;
+  a->H = H;
+  a->n = n;
+  a->C = C;
+  a->cent = p.centroids;
+  a->cent_s = p.cent_stride;
+  a->perm = p.perm;
+  a->perm_s = p.perm_stride;
+  a->off = p.offsets;
+  a->off_s = p.off_stride;
+  a->assign = static_cast<int32_t *>(p.workspace);
+  a->bcnt = reinterpret_cast<int32_t *>(static_cast<char *>(p.workspace) +
+                                        (((size_t)B * H * n * 4u + 255u) & ~size_t(255)));
+  return CRATTN_OK;
+}
+
+struct ByteRange {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+// The bytes a problem writes (centroids, perm, offsets, workspace) and,
+// last, the bytes of x it reads, from its (already checked) arguments.
+void km_ranges(const svg2_kmeans_problem &p, int D, ByteRange r[5]) {
+  const int64_t heads = (int64_t)p.B * p.H;
+  auto span = [](const void *ptr, int64_t last_elem_end, size_t elem) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+    return ByteRange{lo, lo + (uintptr_t)last_elem_end * elem};
+  };
+  r[0] = span(p.centroids, (heads - 1) * p.cent_stride + (int64_t)p.C * D, 4);
+  r[1] = span(p.perm, (heads - 1) * p.perm_stride + p.n, 4);
+  r[2] = span(p.offsets, (heads - 1) * p.off_stride + p.C + 1, 4);
+  r[3] = span(p.workspace, (int64_t)p.ws_bytes, 1);
+  r[4] = span(p.x, (int64_t)(p.B - 1) * p.stride_b + (int64_t)(p.H - 1) * p.stride_h +
+                       (int64_t)(p.n - 1) * p.stride_row + D, 2);
+}
+
+}  // namespace
+
 int svg2_kmeans(const void *x, int64_t stride_b, int64_t stride_h, int64_t stride_row, int B,
                 int H, int n, int D, int C, int iters, int from_tokens, float *centroids,
                 int64_t cent_stride, int32_t *perm, int64_t perm_stride, int32_t *offsets,
                 int64_t off_stride, void *workspace, size_t ws_bytes, void *stream) {
-  if (x == nullptr || centroids == nullptr || perm == nullptr || offsets == nullptr ||
-      workspace == nullptr)
-    return fail(CRATTN_EINVAL, "svg2_kmeans: x, centroids, perm, offsets, workspace required");
-  if (!aligned16(x) || !aligned16(centroids) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(perm) & 3u) || (reinterpret_cast<uintptr_t>(offsets) & 3u))
-    return fail(CRATTN_EINVAL, "svg2_kmeans: x, centroids, workspace 16-byte aligned required");
-  if (D != 64 && D != 128)
-    return fail(CRATTN_ENOTSUP, "svg2_kmeans: head_dim %d not supported (64 or 128)", D);
-  if (B < 1 || H < 1 || n < 1 || n > CRATTN_SVG2_MAX_N)
-    return fail(CRATTN_EINVAL, "svg2_kmeans: B, H >= 1 and n in [1, %d] required",
-                CRATTN_SVG2_MAX_N);
-  if (C < 1 || C > CRATTN_SVG2_MAX_C || iters < 1 || iters > CRATTN_SVG2_MAX_ITERS)
-    return fail(CRATTN_EINVAL, "svg2_kmeans: C in [1, %d] and iters in [1, %d] required",
-                CRATTN_SVG2_MAX_C, CRATTN_SVG2_MAX_ITERS);
-  if (stride_b < 0 || stride_h < 0 || stride_row < 0 || stride_b % 8 || stride_h % 8 ||
-      stride_row % 8 || stride_b > kMaxElems || stride_h > kMaxElems || stride_row > kMaxElems)
-    return fail(CRATTN_EINVAL, "svg2_kmeans: strides must be non-negative multiples of 8");
-  if (cent_stride < (int64_t)C * D || cent_stride % 4 || perm_stride < n ||
-      off_stride < C + 1 || cent_stride > kMaxElems || perm_stride > kMaxElems ||
-      off_stride > kMaxElems)
-    return fail(CRATTN_EINVAL, "svg2_kmeans: output strides smaller than one head's extent");
-  const size_t need = svg2_kmeans_workspace_bytes(B, H, n, C);
-  if (need == 0 || ws_bytes < need)
-    return fail(CRATTN_EINVAL, "svg2_kmeans: workspace of %zu bytes, %zu needed", ws_bytes, need);
+  const svg2_kmeans_problem p{x,         stride_b,    stride_h, stride_row, B,          H,
+                              n,         C,           centroids, cent_stride, perm,     perm_stride,
+                              offsets,   off_stride,  workspace, ws_bytes};
   crattn::KmArgs a;
-  a.x = static_cast<const uint16_t *>(x);
-  a.sb = stride_b;
-  a.sh = stride_h;
-  a.sr = stride_row;
-  a.B = B;
-  a.H = H;
-  a.n = n;
-  a.C = C;
-  a.cent = centroids;
-  a.cent_s = cent_stride;
-  a.perm = perm;
-  a.perm_s = perm_stride;
-  a.off = offsets;
-  a.off_s = off_stride;
-  a.assign = static_cast<int32_t *>(workspace);
-  a.bcnt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
-                                       (((size_t)B * H * n * 4u + 255u) & ~size_t(255)));
+  const int rc = km_setup("svg2_kmeans", p, D, iters, &a);
+  if (rc != CRATTN_OK) return rc;
   return hip_status(crattn::launch_svg2_kmeans(a, D, iters, from_tokens != 0,
                                                static_cast<hipStream_t>(stream)),
                     "svg2_kmeans launch");
+}
+
+int svg2_kmeans2(const svg2_kmeans_problem *p, int D, int iters, int from_tokens, void *stream) {
+  if (p == nullptr) return fail(CRATTN_EINVAL, "svg2_kmeans2: problems required");
+  crattn::KmArgs a[2];
+  for (int k = 0; k < 2; ++k) {
+    const int rc = km_setup(k == 0 ? "svg2_kmeans2 (problem 0)" : "svg2_kmeans2 (problem 1)",
+                            p[k], D, iters, &a[k]);
+    if (rc != CRATTN_OK) return rc;
+  }
+  ByteRange r0[5], r1[5];
+  km_ranges(p[0], D, r0);
+  km_ranges(p[1], D, r1);
+  // every written range of one problem against every range of the other
+  for (int i = 0; i < 5; ++i)
+    for (int j = 0; j < 5; ++j)
+      if ((i < 4 || j < 4) && r0[i].lo < r1[j].hi && r1[j].lo < r0[i].hi)
+        return fail(CRATTN_EINVAL, "svg2_kmeans2: the two problems' buffers overlap");
+  return hip_status(crattn::launch_svg2_kmeans2(a[0], a[1], D, iters, from_tokens != 0,
+                                                static_cast<hipStream_t>(stream)),
+                    "svg2_kmeans2 launch");
 }
 
 int svg2_n_slots(int64_t Lq, int Cq) {

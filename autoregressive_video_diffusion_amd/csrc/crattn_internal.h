@@ -209,6 +209,9 @@ hipError_t launch_qkv_rope(const QkvArgs &a, hipStream_t s);
 hipError_t launch_hsa_pool(const HsaPoolArgs &a, int D, hipStream_t s);
 hipError_t launch_hsa_select(const HsaSelectArgs &a, int D, hipStream_t s);
 hipError_t launch_svg2_kmeans(const KmArgs &a, int D, int iters, bool from_tokens, hipStream_t s);
+// two problems (same D, iters and start) in one launch sequence
+hipError_t launch_svg2_kmeans2(const KmArgs &a0, const KmArgs &a1, int D, int iters,
+                               bool from_tokens, hipStream_t s);
 hipError_t launch_svg2_plan(const SvgPlanArgs &a, int D, hipStream_t s);
 
 }  // namespace crattn

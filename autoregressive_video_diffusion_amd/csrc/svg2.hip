@@ -19,6 +19,7 @@
 // about 2^-17 relative error instead of bf16's 2^-8.
 #include "crattn_internal.h"
 #include <math.h>
+#include <algorithm>
 #include "../../include/crattn.h"
 
 namespace crattn {
@@ -52,9 +53,12 @@ __device__ inline const uint16_t *token_ptr(const KmArgs &a, int64_t bh, int64_t
 
 // ---- initial centroids: centroid c = token floor(c n / C); grid B*H*C ----
 template <int D>
-__global__ void __launch_bounds__(D) svg2_init_kernel(KmArgs a) {
-  const int c = (int)(blockIdx.x % (uint32_t)a.C);
-  const int64_t bh = blockIdx.x / (uint32_t)a.C;
+__global__ void __launch_bounds__(D) svg2_init_kernel(KmArgs a0, KmArgs a1, uint32_t split) {
+  const bool second = blockIdx.x >= split;  // two problems in one launch
+  const KmArgs a = second ? a1 : a0;
+  const uint32_t bid = second ? blockIdx.x - split : blockIdx.x;
+  const int c = (int)(bid % (uint32_t)a.C);
+  const int64_t bh = bid / (uint32_t)a.C;
   const int64_t t = (int64_t)c * a.n / a.C;
   a.cent[bh * a.cent_s + (int64_t)c * D + threadIdx.x] =
       __uint_as_float((uint32_t)token_ptr(a, bh, t)[threadIdx.x] << 16);
@@ -75,7 +79,10 @@ __global__ void __launch_bounds__(D) svg2_init_kernel(KmArgs a) {
 // stored with its cluster (cluster | rank << 16), and the block's count of
 // every cluster goes to bcnt[head][block][cluster].
 template <int D>
-__global__ void __launch_bounds__(256) svg2_assign_kernel(KmArgs a) {
+__global__ void __launch_bounds__(256) svg2_assign_kernel(KmArgs a0, KmArgs a1, uint32_t split) {
+  const bool second = blockIdx.x >= split;  // two problems in one launch
+  const KmArgs a = second ? a1 : a0;
+  const uint32_t bid = second ? blockIdx.x - split : blockIdx.x;
   constexpr int CPR = D / 8, PITCH = CPR + 1, DK = D / 16;
   extern __shared__ uint4 dyn[];
   const int C = a.C, CP = (C + 31) & ~31;
@@ -87,8 +94,8 @@ __global__ void __launch_bounds__(256) svg2_assign_kernel(KmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int nblk = (a.n + 127) / 128;
-  const int blk = (int)(blockIdx.x % (uint32_t)nblk);
-  const int64_t bh = blockIdx.x / (uint32_t)nblk;
+  const int blk = (int)(bid % (uint32_t)nblk);
+  const int64_t bh = bid / (uint32_t)nblk;
   // this wave's tokens as B operands (16 dims x 32 tokens per k-step)
   const int t = blk * 128 + wave * 32 + l32;
   const uint16_t *xp = token_ptr(a, bh, min(t, a.n - 1)) + hf * 8;
@@ -200,13 +207,16 @@ size_t assign_lds_bytes(int C) {
 // which keeps every cluster's tokens in ascending order.
 constexpr int kSortThreads = 1024;
 
-__global__ void __launch_bounds__(kSortThreads) svg2_sort_kernel(KmArgs a) {
+__global__ void __launch_bounds__(kSortThreads) svg2_sort_kernel(KmArgs a0, KmArgs a1, uint32_t split) {
+  const bool second = blockIdx.x >= split;  // two problems in one launch
+  const KmArgs a = second ? a1 : a0;
+  const uint32_t bid = second ? blockIdx.x - split : blockIdx.x;
   __shared__ uint16_t cnt[(kMaxN / 128) * kMaxC];  // [block][cluster]
   __shared__ int tot[kMaxC];
   __shared__ int coff[kMaxC + 1];
   __shared__ int segsum[kSortThreads];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t bh = blockIdx.x;
+  const int64_t bh = bid;
   const int n = a.n, C = a.C;
   const int nblk = (n + 127) / 128;
   const int32_t *bc = a.bcnt + bh * nblk * (int64_t)C;
@@ -282,12 +292,15 @@ __global__ void __launch_bounds__(kSortThreads) svg2_sort_kernel(KmArgs a) {
 // row (16 bytes each), so a pass takes 256/(D/8) tokens; per-thread sums of
 // a fixed set of tokens meet in LDS and are added in slot order. ----
 template <int D>
-__global__ void __launch_bounds__(256) svg2_update_kernel(KmArgs a) {
+__global__ void __launch_bounds__(256) svg2_update_kernel(KmArgs a0, KmArgs a1, uint32_t split) {
+  const bool second = blockIdx.x >= split;  // two problems in one launch
+  const KmArgs a = second ? a1 : a0;
+  const uint32_t bid = second ? blockIdx.x - split : blockIdx.x;
   constexpr int LPR = D / 8;
   constexpr int RPP = 256 / LPR;
   __shared__ float part[RPP][D + 4];
-  const int c = (int)(blockIdx.x % (uint32_t)a.C);
-  const int64_t bh = blockIdx.x / (uint32_t)a.C;
+  const int c = (int)(bid % (uint32_t)a.C);
+  const int64_t bh = bid / (uint32_t)a.C;
   const int tid = threadIdx.x, sub = tid % LPR, slot = tid / LPR;
   const int32_t *off = a.off + bh * a.off_s;
   const int r0 = off[c], r1 = off[c + 1];
@@ -626,12 +639,20 @@ __global__ void __launch_bounds__(256) svg2_select_kernel(SvgPlanArgs a) {
   }
 }
 
+// One or two problems (a1 == nullptr: one); with two, every launch holds
+// the first problem's workgroups, then the second's.
 template <int D>
-hipError_t kmeans_d(const KmArgs &a, int iters, bool from_tokens, hipStream_t s) {
-  const unsigned gc = (unsigned)((int64_t)a.B * a.H * a.C);
-  const unsigned ga = (unsigned)((int64_t)a.B * a.H * ((a.n + 127) / 128));
-  const unsigned gh = (unsigned)((int64_t)a.B * a.H);
-  const size_t lds = assign_lds_bytes<D>(a.C);
+hipError_t kmeans_d(const KmArgs &a0, const KmArgs *a1, int iters, bool from_tokens,
+                    hipStream_t s) {
+  auto gc = [](const KmArgs &a) { return (unsigned)((int64_t)a.B * a.H * a.C); };
+  auto ga = [](const KmArgs &a) { return (unsigned)((int64_t)a.B * a.H * ((a.n + 127) / 128)); };
+  auto gh = [](const KmArgs &a) { return (unsigned)((int64_t)a.B * a.H); };
+  const KmArgs &b = a1 ? *a1 : a0;
+  const unsigned c0 = gc(a0), c1 = a1 ? gc(b) : 0u;
+  const unsigned s0 = ga(a0), s1 = a1 ? ga(b) : 0u;
+  const unsigned h0 = gh(a0), h1 = a1 ? gh(b) : 0u;
+  const size_t lds = a1 ? std::max(assign_lds_bytes<D>(a0.C), assign_lds_bytes<D>(b.C))
+                        : assign_lds_bytes<D>(a0.C);
   static bool attr = false;
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(
@@ -640,11 +661,12 @@ hipError_t kmeans_d(const KmArgs &a, int iters, bool from_tokens, hipStream_t s)
     if (e != hipSuccess) return e;
     attr = true;
   }
-  if (from_tokens) hipLaunchKernelGGL(svg2_init_kernel<D>, dim3(gc), dim3(D), 0, s, a);
+  if (from_tokens)
+    hipLaunchKernelGGL(svg2_init_kernel<D>, dim3(c0 + c1), dim3(D), 0, s, a0, b, c0);
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL(svg2_assign_kernel<D>, dim3(ga), dim3(256), lds, s, a);
-    hipLaunchKernelGGL(svg2_sort_kernel, dim3(gh), dim3(kSortThreads), 0, s, a);
-    hipLaunchKernelGGL(svg2_update_kernel<D>, dim3(gc), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(svg2_assign_kernel<D>, dim3(s0 + s1), dim3(256), lds, s, a0, b, s0);
+    hipLaunchKernelGGL(svg2_sort_kernel, dim3(h0 + h1), dim3(kSortThreads), 0, s, a0, b, h0);
+    hipLaunchKernelGGL(svg2_update_kernel<D>, dim3(c0 + c1), dim3(256), 0, s, a0, b, c0);
   }
   return hipGetLastError();
 }
@@ -652,7 +674,14 @@ hipError_t kmeans_d(const KmArgs &a, int iters, bool from_tokens, hipStream_t s)
 }  // namespace
 
 hipError_t launch_svg2_kmeans(const KmArgs &a, int D, int iters, bool from_tokens, hipStream_t s) {
-  return D == 128 ? kmeans_d<128>(a, iters, from_tokens, s) : kmeans_d<64>(a, iters, from_tokens, s);
+  return D == 128 ? kmeans_d<128>(a, nullptr, iters, from_tokens, s)
+                  : kmeans_d<64>(a, nullptr, iters, from_tokens, s);
+}
+
+hipError_t launch_svg2_kmeans2(const KmArgs &a0, const KmArgs &a1, int D, int iters,
+                               bool from_tokens, hipStream_t s) {
+  return D == 128 ? kmeans_d<128>(a0, &a1, iters, from_tokens, s)
+                  : kmeans_d<64>(a0, &a1, iters, from_tokens, s);
 }
 
 hipError_t launch_svg2_plan(const SvgPlanArgs &a, int D, hipStream_t s) {

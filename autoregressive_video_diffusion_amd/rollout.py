@@ -35,7 +35,7 @@ import torch
 from . import (HSA_QBLOCK, chunk_causal_attn, chunk_causal_attn_workspace_bytes, hsa_attn,
                hsa_pool_bytes, hsa_pool_keys, hsa_select, rope_apply_append, rope_precompute,
                rope_table_bytes, svg2_attn, svg2_attn_workspace_bytes, svg2_kmeans,
-               svg2_kmeans_workspace_bytes, svg2_n_slots, svg2_plan)
+               svg2_kmeans2, svg2_kmeans_workspace_bytes, svg2_n_slots, svg2_plan)
 
 
 class ChunkRollout:
@@ -145,15 +145,25 @@ class ChunkRollout:
     def _svg2_attend(self, c: int, q_out, out, lse):
         Cq, _, p = self.svg2
         n_vis = min(c + 1, self.window)
-        main = torch.cuda.current_stream(q_out.device)
-        # the queries' k-means on a second stream, beside the keys'
-        self.side.wait_stream(main)
-        svg2_kmeans(q_out.permute(0, 2, 1, 3), Cq, self.svg2_iters if self.q_warm else 3,
-                    not self.q_warm, self.qcent, self.qperm, self.qoff, self.ws_q,
-                    stream=self.side)
+        s = self.slot(c)
+        if self.q_warm == self.k_warm[s]:
+            # the queries' and the keys' k-means in one launch sequence
+            warm, Ck, L = self.q_warm, self.svg2[1], self.L
+            svg2_kmeans2((self.k_cache[:, :, s * L:(s + 1) * L], Ck, self.kcent[:, :, s],
+                          self.kperm[:, :, s], self.koff[:, :, s], self.ws_k),
+                         (q_out.permute(0, 2, 1, 3), Cq, self.qcent, self.qperm, self.qoff,
+                          self.ws_q), self.svg2_iters if warm else 3, not warm)
+            self.k_warm[s] = True
+        else:
+            main = torch.cuda.current_stream(q_out.device)
+            # the queries' k-means on a second stream, beside the keys'
+            self.side.wait_stream(main)
+            svg2_kmeans(q_out.permute(0, 2, 1, 3), Cq, self.svg2_iters if self.q_warm else 3,
+                        not self.q_warm, self.qcent, self.qperm, self.qoff, self.ws_q,
+                        stream=self.side)
+            self._cluster_slot(c)
+            main.wait_stream(self.side)
         self.q_warm = True
-        self._cluster_slot(c)
-        main.wait_stream(self.side)
         B, H, Ck = self.B, self.H, self.svg2[1]
         sel = self.ksel.view(-1)[:B * H * Cq * n_vis * Ck].view(B, H, Cq, n_vis * Ck)
         svg2_plan(self.qcent, self.qoff, self.kcent, self.koff, self.kperm, n_vis, self.L, p,

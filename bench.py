@@ -299,8 +299,10 @@ def time_svg2(crattn, w, q, kc, vc, out, lse, Cq=20, Ck=64, iters=2, p=0.9, spli
     queries q [B, lq, H, D] against the cache kc, vc.  The keys of every
     chunk slot are clustered first (Ck clusters, from tokens, 3 iterations:
     a stored chunk's clusters are made once).  A denoising call then runs
-    k-means of the own slot's keys and of the queries (on two streams, each
-    started from the previous call's centroids, `iters` iterations), the
+    k-means of the own slot's keys and of the queries (both in one launch
+    sequence, each started from the previous call's centroids, `iters`
+    iterations; the same call with the two k-means on two streams is timed
+    beside it), the
     plan (top-p selection, key lists, query tiles) and the attention over
     the lists.  Returns per-launch times (ms) of each part and of the whole
     call, and the FLOPs over the listed keys."""
@@ -351,7 +353,7 @@ def time_svg2(crattn, w, q, kc, vc, out, lse, Cq=20, Ck=64, iters=2, p=0.9, spli
     def attn_call(i):
         crattn.svg2_attn(q, kc, vc, qperm, slots, lists, llen, out, lse, splits, wsa)
 
-    def whole_call(i):
+    def whole_call_two_streams(i):
         # the query k-means on a second stream, overlapping the key k-means
         side.wait_stream(main)
         query_call(i, side)
@@ -360,17 +362,25 @@ def time_svg2(crattn, w, q, kc, vc, out, lse, Cq=20, Ck=64, iters=2, p=0.9, spli
         plan_call(i)
         attn_call(i)
 
+    def whole_call(i):
+        # both k-means in one launch sequence (svg2_kmeans2)
+        crattn.svg2_kmeans2((ks, Ck, kcent[:, :, own], kperm[:, :, own], koff[:, :, own], wsk),
+                            (qv, Cq, qcent, qperm, qoff, wsq), iters, False)
+        plan_call(i)
+        attn_call(i)
+
     def cold_call(i):
         crattn.svg2_kmeans(ks, Ck, 3, True, kcent[:, :, own], kperm[:, :, own],
                            koff[:, :, own], wsk)
 
-    for f in (key_call, query_call, plan_call, attn_call, whole_call):
+    for f in (key_call, query_call, plan_call, attn_call, whole_call, whole_call_two_streams):
         for i in range(3):
             f(i)
     torch.cuda.synchronize()
     t = {"keys": burst_ms(key_call, 5, 10)[2], "queries": burst_ms(query_call, 5, 10)[2],
          "plan": burst_ms(plan_call, 5, 10)[2], "attn": burst_ms(attn_call, 5, 10)[2],
-         "call": burst_ms(whole_call, 5, 10)[2], "keys_cold": burst_ms(cold_call, 3, 5)[1]}
+         "call": burst_ms(whole_call, 5, 10)[2], "keys_cold": burst_ms(cold_call, 3, 5)[1],
+         "call_two_streams": burst_ms(whole_call_two_streams, 5, 10)[2]}
     # the same call captured once in a HIP graph and replayed (its ~15
     # launches then cost no host-side launch time)
     graph = torch.cuda.CUDAGraph()
@@ -422,6 +432,7 @@ def svg2_extras(crattn, w, dev, dense_attn_ms, dense_flops, Cq=20, Ck=64, iters=
             "kmeans_queries_us": round(t["queries"] * 1e3, 1),
             "plan_us": round(t["plan"] * 1e3, 1), "attn_us": round(t["attn"] * 1e3, 1),
             "call_us": round(t["call"] * 1e3, 1),
+            "call_two_streams_us": round(t["call_two_streams"] * 1e3, 1),
             "call_graph_replay_us": round(t["call_graph"] * 1e3, 1), "listed_flops": sfl,
             "attn_tflops": round(tf, 1),
             "call_speedup_vs_dense_attn": (round(dense_attn_ms / t["call"], 2)

@@ -441,6 +441,39 @@ int svg2_kmeans(const void *x, int64_t stride_b, int64_t stride_h, int64_t strid
                 int64_t cent_stride, int32_t *perm, int64_t perm_stride, int32_t *offsets,
                 int64_t off_stride, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * One k-means problem of svg2_kmeans2: the arguments of svg2_kmeans that
+ * differ between the two problems, with the same meaning and limits.
+ */
+typedef struct svg2_kmeans_problem {
+  const void *x;
+  int64_t stride_b, stride_h, stride_row;
+  int B, H, n, C;
+  float *centroids;
+  int64_t cent_stride;
+  int32_t *perm;
+  int64_t perm_stride;
+  int32_t *offsets;
+  int64_t off_stride;
+  void *workspace;
+  size_t ws_bytes;
+} svg2_kmeans_problem;
+
+/*
+ * svg2_kmeans of two problems at once ("Sparse VideoGen2" §2.A: a denoising
+ * call clusters its queries and the new keys), p[0] and p[1], with the same
+ * D, iters and from_tokens: every kernel of the sequence is launched once
+ * for both, so the two share no stream synchronisation.  Each result equals
+ * that of svg2_kmeans on the problem alone, bit for bit.
+ *
+ *   p   host pointer to two problems (read during the call only).
+ *
+ * Errors: those of svg2_kmeans for either problem (the message names it);
+ * EINVAL if p is NULL or if an output or workspace range of one problem
+ * overlaps any range (x included) of the other.
+ */
+int svg2_kmeans2(const svg2_kmeans_problem *p, int D, int iters, int from_tokens, void *stream);
+
 /* Query tiles of a call with Lq queries in Cq clusters: ceil(Lq / 256) + Cq
  * (an upper bound of sum over clusters of ceil(size / 256)); 0 if invalid. */
 int svg2_n_slots(int64_t Lq, int Cq);

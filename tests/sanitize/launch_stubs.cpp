@@ -16,6 +16,7 @@ hipError_t launch_qkv_rope(const QkvArgs &, hipStream_t) { return ++g_launches, 
 hipError_t launch_hsa_pool(const HsaPoolArgs &, int, hipStream_t) { return ++g_launches, hipSuccess; }
 hipError_t launch_hsa_select(const HsaSelectArgs &, int, hipStream_t) { return ++g_launches, hipSuccess; }
 hipError_t launch_svg2_kmeans(const KmArgs &, int, int, bool, hipStream_t) { return ++g_launches, hipSuccess; }
+hipError_t launch_svg2_kmeans2(const KmArgs &, const KmArgs &, int, int, bool, hipStream_t) { return ++g_launches, hipSuccess; }
 hipError_t launch_svg2_plan(const SvgPlanArgs &, int, hipStream_t) { return ++g_launches, hipSuccess; }
 static char fake_scratch[256];
 void *attn_scratch(hipError_t *err) { *err = hipSuccess; return fake_scratch; }

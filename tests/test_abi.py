@@ -364,3 +364,40 @@ def _svg2_attn(**kw):
 def test_svg2_attn_rejects(kw, code):
     assert _svg2_attn(**kw) == code
     assert crattn.crattn_last_error() != ""
+
+
+def _km_problem(base, **kw):
+    # distinct 16-byte-aligned fake addresses per buffer; nothing is launched
+    # (every case below fails validation first)
+    a = dict(x=base, stride_b=2 * 64 * 64, stride_h=64, stride_row=2 * 64, B=1, H=2, n=64, C=8,
+             centroids=base + (1 << 24), cent_stride=8 * 64, perm=base + (2 << 24), perm_stride=64,
+             offsets=base + (3 << 24), off_stride=9, workspace=base + (4 << 24), ws_bytes=1 << 20)
+    a.update(kw)
+    return crattn._KmProblem(**a)
+
+
+@pytest.mark.parametrize("case", ["null", "problem1", "shared_workspace", "x_in_output",
+                                  "head_dim"])
+def test_svg2_kmeans2_rejects(case):
+    lib = _lib()
+    p0, p1 = _km_problem(1 << 36), _km_problem(2 << 36)
+    D = 64
+    if case == "null":
+        assert lib.svg2_kmeans2(None, D, 2, 1, None) == 1
+        return
+    if case == "problem1":
+        p1.n = 0
+    elif case == "shared_workspace":
+        p1.workspace = p0.workspace + 4096
+    elif case == "x_in_output":
+        p1.x = p0.perm
+    elif case == "head_dim":
+        D = 96
+    arr = (crattn._KmProblem * 2)(p0, p1)
+    assert lib.svg2_kmeans2(arr, D, 2, 1, None) == (2 if case == "head_dim" else 1)
+    msg = crattn.crattn_last_error()
+    assert msg.startswith("svg2_kmeans2")
+    if case == "problem1":
+        assert "problem 1" in msg
+    if case in ("shared_workspace", "x_in_output"):
+        assert "overlap" in msg

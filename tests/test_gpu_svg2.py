@@ -571,3 +571,41 @@ def test_svg2_call_replays_from_a_hip_graph():
         call()
         torch.cuda.synchronize()
         assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("D,from_tokens", [(128, True), (128, False), (64, True)])
+def test_kmeans2_equals_two_single_calls(D, from_tokens):
+    """svg2_kmeans2 launches both problems together (one chunk slot's keys,
+    64 clusters, and the queries, 20 clusters, of different lengths); each
+    result equals svg2_kmeans on that problem alone, bit for bit."""
+    B, H = 1, 3
+    kc = normal((B, H, 3000, D), 11).to(dev())
+    q = normal((B, 777, H, D), 12).to(dev())
+    probs = [(kc[:, :, 1000:2000], 64), (q.permute(0, 2, 1, 3), 20)]
+    init = [normal((B, H, C, D), 13 + i, torch.float32).to(dev())
+            for i, (_, C) in enumerate(probs)]
+    outs = []
+    for fused in (False, True):
+        bufs = []
+        for (x, C), c0 in zip(probs, init):
+            n = x.shape[2]
+            perm = torch.full((B, H, n), -7, dtype=torch.int32, device=dev())
+            off = torch.full((B, H, C + 1), -7, dtype=torch.int32, device=dev())
+            ws = _ws(crattn.svg2_kmeans_workspace_bytes(B, H, n, C))
+            bufs.append((x, C, c0.clone(), perm, off, ws))
+        if fused:
+            crattn.svg2_kmeans2(bufs[0], bufs[1], 2, from_tokens)
+        else:
+            for b in bufs:
+                crattn.svg2_kmeans(b[0], b[1], 2, from_tokens, *b[2:])
+        torch.cuda.synchronize()
+        outs.append([(b[2].cpu(), b[3].cpu(), b[4].cpu()) for b in bufs])
+    for single, pair in zip(outs[0], outs[1]):
+        for u, v in zip(single, pair):
+            assert torch.equal(u, v)
+    # the clusterings are real ones: offsets end at n, perm is a permutation
+    for (x, C), (_, perm, off) in zip(probs, outs[1]):
+        n = x.shape[2]
+        assert int(off[..., -1].min()) == n == int(off[..., -1].max())
+        assert torch.equal(perm.sort(dim=-1).values,
+                           torch.arange(n, dtype=torch.int32).expand(B, H, n))
