@@ -608,8 +608,9 @@ struct ByteRange {
   uintptr_t lo, hi;  // [lo, hi)
 };
 
-// The bytes a problem writes (centroids, perm, offsets, workspace) and,
-// last, the bytes of x it reads, from its (already checked) arguments.
+// The bytes a problem writes (centroids, perm, offsets, the workspace bytes
+// it needs) and, last, the bytes of x it reads, from its (already checked)
+// arguments.
 void km_ranges(const svg2_kmeans_problem &p, int D, ByteRange r[5]) {
   const int64_t heads = (int64_t)p.B * p.H;
   auto span = [](const void *ptr, int64_t last_elem_end, size_t elem) {
@@ -619,7 +620,7 @@ void km_ranges(const svg2_kmeans_problem &p, int D, ByteRange r[5]) {
   r[0] = span(p.centroids, (heads - 1) * p.cent_stride + (int64_t)p.C * D, 4);
   r[1] = span(p.perm, (heads - 1) * p.perm_stride + p.n, 4);
   r[2] = span(p.offsets, (heads - 1) * p.off_stride + p.C + 1, 4);
-  r[3] = span(p.workspace, (int64_t)p.ws_bytes, 1);
+  r[3] = span(p.workspace, (int64_t)svg2_kmeans_workspace_bytes(p.B, p.H, p.n, p.C), 1);
   r[4] = span(p.x, (int64_t)(p.B - 1) * p.stride_b + (int64_t)(p.H - 1) * p.stride_h +
                        (int64_t)(p.n - 1) * p.stride_row + D, 2);
 }

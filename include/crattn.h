@@ -469,8 +469,8 @@ typedef struct svg2_kmeans_problem {
  *   p   host pointer to two problems (read during the call only).
  *
  * Errors: those of svg2_kmeans for either problem (the message names it);
- * EINVAL if p is NULL or if an output or workspace range of one problem
- * overlaps any range (x included) of the other.
+ * EINVAL if p is NULL or if an output, or the workspace bytes it needs, of
+ * one problem overlaps any range (x included) of the other.
  */
 int svg2_kmeans2(const svg2_kmeans_problem *p, int D, int iters, int from_tokens, void *stream);
 
